@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved HBM GB/s and % of MI355X peak per norm kernel (one GPU).
+
+Headline step: LayerNorm forward on x [16, 64, 256, 256] fp32 ~ N(0,1),
+normalized over (64, 256, 256), elementwise weight/bias (LN page "Kimi-K2.6
+l1_p40" problem).  One step = the whole LN path (partial moments, merge,
+normalize) over one batch; `value` = algorithmic bytes / wall time per step,
+with inputs resident in HBM.  Algorithmic bytes of the method = x read twice
+(moments pass + normalize pass) + weight + bias read once + y written once
+= 838,860,800 B.
+
+Also measured (the `kernels` object): GroupNorm+LeakyReLU+x2 [1024, 8192],
+RMSNorm over dim 1 [112, 64, 512, 512], the LN N(100, 0.01) stress input,
+both LN schedules, and fc+GN [1024 x 8192 x 8192] (TFLOP/s).
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by
+torch.cuda.synchronize(); per-launch kernel durations from HIP events
+recorded on the stream the library launches on (torch's current stream).
+Inputs rotate over several buffer sets (>= 2 GiB working set) so the 256 MB
+Infinity Cache cannot hold a step's inputs from the previous step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
+PEAK_FP32_MATRIX_TFLOPS = 157.3  # MI355X dense fp32 MFMA peak
+METRIC = "achieved HBM GB/s and % of MI355X peak per norm kernel (1 GPU)"
+
+LN_SHAPE = (16, 64, 256, 256)
+LN_BYTES = 4 * (2 * 16 * 4194304 + 2 * 4194304 + 16 * 4194304)       # 838,860,800
+LN_NORMALIZE_BYTES = 4 * (16 * 4194304 + 2 * 4194304 + 16 * 4194304)  # 570,425,344
+GN_BYTES = 4 * (2 * 1024 * 8192 + 2 * 8192)                           # 67,174,400
+RMS_BYTES = 4 * 2 * 112 * 64 * 512 * 512                              # 15,032,385,536
+FC_FLOPS = 2 * 1024 * 8192 * 8192                                     # 137,438,953,472
+FC_GN_BYTES = 4 * (1024 * 8192 + 8192 * 8192 + 8192 + 1024 * 8192)    # x, W, b, h write (GEMM part)
+
+CSRC = os.path.join(ROOT, "normalization_ln_forward_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, files):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if the kernel source is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entries = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = entries.get(kernel)
+    if not e or e.get("source_sha") != source_sha(files):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--variant", type=int, default=None, choices=[0, 1],
+                    help="LN schedule for the headline (default: the library's fastest measured, 1)")
+    ap.add_argument("--rotate", type=int, default=4, help="LN buffer sets rotated through (>=1)")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import normalization_ln_forward_amd as nf
+    from normalization_ln_forward_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nf.lib()
+    variant = 1 if args.variant is None else args.variant
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ headline: LN
+    log(f"[bench] LN {LN_SHAPE} variant={variant} rotate={args.rotate}")
+    R = max(1, args.rotate)
+    base = synth.make("ln_16x64x256x256", device=dev)
+    xs = [base["x"]] + [synth.make("ln_16x64x256x256", device=dev, seed=2000 + i)["x"] for i in range(1, R)]
+    ys = [torch.empty_like(base["x"]) for _ in range(R)]
+    w, b = base["weight"], base["bias"]
+    outer, inner = 16, 4194304
+    _, ws = nf.alloc_workspace(nf.ln_forward_workspace_size(outer, inner), dev)
+    nf.ln_forward_workspace_init(ws)
+    stream = torch.cuda.current_stream(dev)
+
+    def ln_step(i, ev=None):
+        x, y = xs[i % R], ys[i % R]
+        if variant == 1:
+            if ev:
+                ev[0].record(stream)
+            nf.ln_forward(x, w, b, variant=1, out=y, workspace=ws)
+            if ev:
+                ev[1].record(stream)
+        else:
+            if ev:
+                ev[0].record(stream)
+            nf.ln_forward_stats(x, workspace=ws)
+            if ev:
+                ev[1].record(stream)
+            nf.ln_forward_apply(x, w, b, ws, out=y)
+            if ev:
+                ev[2].record(stream)
+
+    for i in range(args.warmup):
+        ln_step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ln_step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    value = LN_BYTES / (ms_per_step / 1e3) / 1e9
+    if variant == 1:
+        dur = [e[0].elapsed_time(e[1]) for e in evs]
+        dom_kernel, dom_bytes, dom_files = "ln_single_kernel", LN_BYTES, ["ln.hip", "common.hpp"]
+    else:
+        dur = [e[1].elapsed_time(e[2]) for e in evs]
+        dom_kernel, dom_bytes, dom_files = "ln_normalize_kernel", LN_NORMALIZE_BYTES, ["ln.hip", "common.hpp"]
+    avg_ms = sum(dur) / len(dur)
+    achieved = dom_bytes / (avg_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(dom_kernel, dom_files),
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": round(avg_ms, 5)}
+    log(f"[bench] LN: {ms_per_step:.4f} ms/step wall, {value:.1f} GB/s; {dom_kernel} {avg_ms:.4f} ms, "
+        f"{achieved:.1f} GB/s")
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    kernels = {}
+    if not args.no_kernels:
+        kernels = per_kernel_table(torch, nf, synth, dev, stream, args, log)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(base, args.cpu_seconds, log)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "config": {"workload": "ln_16x64x256x256", "shape": list(LN_SHAPE), "normalized_shape": [64, 256, 256],
+                   "variant": ["split", "single"][variant], "rotate_buffer_sets": R,
+                   "algorithmic_bytes": LN_BYTES, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def time_launches(torch, stream, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    d = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"avg_ms": sum(d) / len(d), "median_ms": d[len(d) // 2], "min_ms": d[0], "wall_ms": 1e3 * wall}
+
+
+def _entry(t, nbytes=None, flops=None):
+    e = {k: round(v, 5) for k, v in t.items()}
+    if nbytes:
+        gbs = nbytes / (t["avg_ms"] / 1e3) / 1e9
+        e.update({"algorithmic_bytes": nbytes, "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+    if flops:
+        tf = flops / (t["avg_ms"] / 1e3) / 1e12
+        e.update({"flops": flops, "TFLOP/s": round(tf, 2), "frac_of_fp32_matrix_peak":
+                  round(tf / PEAK_FP32_MATRIX_TFLOPS, 4)})
+    return e
+
+
+def per_kernel_table(torch, nf, synth, dev, stream, args, log):
+    steps, warm = max(10, args.steps // 2), max(3, args.warmup // 2)
+    out = {}
+
+    # GroupNorm + LeakyReLU + x2: 64 MiB per set, rotate 32 sets (2 GiB)
+    log("[bench] GN [1024, 8192]")
+    g = synth.make("gn_lrelu_x2_1024x8192", device=dev)
+    R = 32
+    xs = [g["x"]] + [synth.make("gn_lrelu_x2_1024x8192", device=dev, seed=3000 + i)["x"] for i in range(1, R)]
+    ys = [torch.empty_like(g["x"]) for _ in range(R)]
+    t = time_launches(torch, stream, lambda i: nf.gn_lrelu_x2_forward(xs[i % R], g["gamma"], g["beta"], 512,
+                                                                      out=ys[i % R]), max(steps, 64), warm)
+    out["gn_lrelu_x2_1024x8192"] = _entry(t, GN_BYTES)
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    # LN, both schedules, N(0,1) and the N(100, 0.01) stress input
+    for name in ("ln_16x64x256x256", "ln_stress_16x64x256x256"):
+        d = synth.make(name, device=dev)
+        y = torch.empty_like(d["x"])
+        x2 = synth.make(name, device=dev, seed=4000)["x"]
+        y2 = torch.empty_like(d["x"])
+        for variant in (0, 1):
+            log(f"[bench] {name} variant={variant}")
+            t = time_launches(torch, stream, lambda i: nf.ln_forward(
+                (d["x"], x2)[i % 2], d["weight"], d["bias"], variant=variant, out=(y, y2)[i % 2]), steps, warm)
+            out[f"{name}/{['split', 'single'][variant]}"] = _entry(t, LN_BYTES)
+        del d, y, x2, y2
+        torch.cuda.empty_cache()
+
+    # RMSNorm over dim 1: 7.5 GB in, 7.5 GB out (far beyond any cache)
+    log("[bench] RMS [112, 64, 512, 512]")
+    r = synth.make("rms_ch_112x64x512x512", device=dev)
+    y = torch.empty_like(r["x"])
+    t = time_launches(torch, stream, lambda i: nf.rmsnorm_ch_forward(r["x"], out=y), max(5, steps // 4), 2)
+    out["rms_ch_112x64x512x512"] = _entry(t, RMS_BYTES)
+    del r, y
+    torch.cuda.empty_cache()
+
+    # fc + GN
+    log("[bench] fc+GN [1024 x 8192 x 8192]")
+    f = synth.make("fc_gn_1024x8192x8192", device=dev)
+    y = torch.empty(1024, 8192, device=dev)
+    t = time_launches(torch, stream, lambda i: nf.fc_gn_forward(f["x"], f["W"], f["b"], f["gamma"], f["beta"], 512,
+                                                               out=y), max(5, steps // 4), 2)
+    out["fc_gn_1024x8192x8192"] = _entry(t, flops=FC_FLOPS)
+    del f, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(base, seconds, log):
+    """The fp64 oracle on the host cores, on the same LN workload, repeated for ~`seconds`."""
+    import oracle
+
+    x = base["x"].cpu().numpy()
+    w = base["weight"].cpu().numpy()
+    b = base["bias"].cpu().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.ln(x, w, b, eps=1e-5)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 100:
+            break
+    per = el / reps
+    log(f"[bench] oracle LN: {per:.3f} s per full workload ({reps} reps, {oracle.num_threads()} threads)")
+    return {"value": round(LN_BYTES / per / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds_per_step": round(per, 4),
+            "sample": f"full ln_16x64x256x256 workload (16 samples x 4,194,304), {reps} repetitions, fp64 two-pass",
+            "host_cpu": platform.processor() or platform.machine(), "host_logical_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

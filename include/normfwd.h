@@ -1,0 +1,153 @@
+/*
+ * normfwd — forward passes of three normalization layers on AMD MI355X
+ * (gfx950), as a C ABI over hand-written HIP kernels.
+ *
+ * Sources (three POPCORNBENCH agent transcripts; a "turn" is one agent
+ * message on a page):
+ *   LN page  "Kimi-K2.6 l1_p40": LayerNorm over normalized_shape (64,256,256)
+ *   GN page  "Kimi-K2.6 l2_p62": fc -> GroupNorm(512) -> LeakyReLU -> x + x
+ *   RMS page "Kimi-K2.6 l1_p36": RMSNorm along dim 1 of an NCHW tensor
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are fp32, contiguous, row-major, in device memory (HBM).  The
+ *     caller owns every buffer; the library never allocates, frees or
+ *     synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued on it; calls return as soon as the work is
+ *     enqueued.
+ *   - Any alignment and any length are accepted.  128-bit vector paths are
+ *     taken when pointers are 16-byte aligned and the contiguous extent is a
+ *     multiple of 4; otherwise a scalar path computes the same result.
+ *   - In place (y == x) is allowed: every element is read before the same
+ *     lane writes it.  Partial overlap of inputs and outputs is undefined.
+ *   - Results are run-to-run bitwise deterministic: no floating-point
+ *     atomics, every reduction has a fixed order.
+ *   - Errors are returned, never thrown: arguments are validated before
+ *     anything is enqueued, so a non-OK return from validation means nothing
+ *     was launched.  normfwd_last_error() then describes the failure
+ *     (thread-local, valid until the next call on the same thread).
+ */
+#ifndef NORMFWD_H
+#define NORMFWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int normfwd_status;
+#define NORMFWD_OK 0
+#define NORMFWD_ERR_INVALID 1     /* bad shape, null required pointer, bad enum value   */
+#define NORMFWD_ERR_UNSUPPORTED 2 /* valid arguments this build does not handle         */
+#define NORMFWD_ERR_WORKSPACE 3   /* workspace null or smaller than the size query says */
+#define NORMFWD_ERR_HIP 4         /* a HIP runtime call or kernel launch failed         */
+
+/* Static string naming a status code ("unknown status" for other values). */
+const char* normfwd_status_string(normfwd_status status);
+
+/* Message describing the last non-OK return on this thread ("" if none). */
+const char* normfwd_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * LayerNorm (LN page, turn 1: per sample, mean and population variance over
+ * all elements of normalized_shape; y = (x - mean) / sqrt(var + eps) * weight
+ * + bias, weight and bias elementwise of normalized_shape.  Turn 2 splits
+ * each sample over many workgroups that write partial moments, reduces them
+ * per sample, then normalizes.  Turn 6 sketches the single-kernel variant in
+ * which the last workgroup to finish a sample reduces it.)
+ *
+ *   x, y      [outer, inner] fp32; inner = prod(normalized_shape)
+ *   weight    [inner] fp32 or NULL (= all ones)
+ *   bias      [inner] fp32 or NULL (= all zeros)
+ *   eps       added to the variance inside the square root
+ *   mean_out  [outer] fp32 or NULL: the sample mean, rounded to fp32
+ *   rstd_out  [outer] fp32 or NULL: 1 / sqrt(var + eps), rounded to fp32
+ *   workspace device buffer of at least ln_forward_workspace_size(outer,
+ *             inner) bytes, 256-byte aligned.  It holds per-chunk partial
+ *             moments, per-sample statistics and (variant 1) a control
+ *             block of counters.  One workspace must not be used by two
+ *             calls that may run concurrently.
+ *   variant   0 = split: partial-moments kernel, per-sample merge kernel,
+ *                 normalize kernel;
+ *             1 = single kernel: the same three phases in one cooperative
+ *                 launch, the last workgroup to finish a sample merges it.
+ *                 Needs a workspace whose control block was zeroed once by
+ *                 ln_forward_workspace_init(); each call leaves it reusable.
+ *
+ * Statistics are exact to about 1e-7 relative even when |mean| >> std: the
+ * partial moments are accumulated around a per-sample shift (the sample's
+ * first element), handed between workgroups in fp64, merged with Chan's
+ * pairwise update in a fixed order, and the mean is applied as an fp32
+ * hi + lo pair.
+ * ---------------------------------------------------------------------- */
+size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
+
+/* Zero the control block of `workspace` (enqueued on `stream`). */
+normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+normfwd_status ln_forward(const float* x, const float* weight, const float* bias, float* y,
+                          int64_t outer, int64_t inner, float eps,
+                          void* workspace, size_t workspace_bytes,
+                          float* mean_out, float* rstd_out, int variant, void* stream);
+
+/* The split variant's two halves, for callers that want the statistics
+ * alone or want to time the phases: ln_forward_stats runs the partial and
+ * merge kernels and leaves per-sample (mean hi, mean lo, rstd) in the
+ * workspace; ln_forward_apply runs the normalize kernel from them.  Calling
+ * stats then apply on one stream equals ln_forward(..., variant 0, ...). */
+normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, float eps,
+                                void* workspace, size_t workspace_bytes,
+                                float* mean_out, float* rstd_out, void* stream);
+normfwd_status ln_forward_apply(const float* x, const float* weight, const float* bias, float* y,
+                                int64_t outer, int64_t inner,
+                                const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * GroupNorm -> LeakyReLU -> x + x (GN page, turn 1: the [N, C] fc output is
+ * split into num_groups groups of M = C / num_groups contiguous channels;
+ * each (row, group) is normalized with its own mean and population variance
+ * (eps inside the square root), then scaled by gamma[c] and shifted by
+ * beta[c]; then LeakyReLU with negative_slope; then the result is added to
+ * itself.)
+ *
+ *   x, y          [N, C] fp32
+ *   gamma, beta   [C] fp32, or NULL (= ones / zeros)
+ *   C % num_groups != 0 -> NORMFWD_ERR_INVALID (the GN page checks the same)
+ * ---------------------------------------------------------------------- */
+normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const float* beta, float* y,
+                                   int64_t N, int64_t C, int64_t num_groups, float eps,
+                                   float negative_slope, void* stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm along dim 1 (RMS page, turns 1-2: rms = sqrt(mean over the
+ * feature dim of x^2 + eps), y = x / rms, no affine).  The tensor is viewed
+ * as [B, C, S] with S the product of the trailing dims, so one position's C
+ * values sit S elements apart.
+ *
+ *   x, y   [B, C, S] fp32 (B * C * S may exceed 2^31)
+ * ---------------------------------------------------------------------- */
+normfwd_status rmsnorm_ch_forward(const float* x, float* y, int64_t B, int64_t C, int64_t S,
+                                  float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fc followed by GroupNorm -> LeakyReLU -> x + x (GN page, turn 1: h = x W^T
+ * + b with x [N, K], W [C, K], b [C]; then the GN epilogue above on h).
+ *
+ *   workspace  device buffer of at least fc_gn_forward_workspace_size(N, K,
+ *              C) bytes (holds h, [N, C] fp32), 256-byte aligned
+ *   b, gamma, beta may be NULL.
+ * ---------------------------------------------------------------------- */
+size_t fc_gn_forward_workspace_size(int64_t N, int64_t K, int64_t C);
+normfwd_status fc_gn_forward(const float* x, const float* W, const float* b,
+                             const float* gamma, const float* beta, float* y,
+                             int64_t N, int64_t K, int64_t C, int64_t num_groups, float eps,
+                             float negative_slope, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMFWD_H */

@@ -1,0 +1,265 @@
+"""ctypes binding of libnormfwd.so (the C ABI in include/normfwd.h).
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are checked
+here, outputs and workspaces are allocated with torch, and every call goes
+straight to the HIP library on the caller's current stream.  Nothing is
+computed in Python, and there is no fallback: if the library is not built the
+functions raise.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (one runtime per process, so torch's
+stream handles and device pointers are valid inside the library).
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnormfwd.so")
+
+NORMFWD_OK = 0
+STATUS_NAMES = {0: "NORMFWD_OK", 1: "NORMFWD_ERR_INVALID", 2: "NORMFWD_ERR_UNSUPPORTED",
+                3: "NORMFWD_ERR_WORKSPACE", 4: "NORMFWD_ERR_HIP"}
+
+# Every symbol include/normfwd.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_ST = ctypes.c_int
+SIGNATURES = {
+    "normfwd_status_string": (ctypes.c_char_p, [_ST]),
+    "normfwd_last_error": (ctypes.c_char_p, []),
+    "ln_forward_workspace_size": (_SZ, [_I64, _I64]),
+    "ln_forward_workspace_init": (_ST, [_P, _SZ, _P]),
+    "ln_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P, _P, ctypes.c_int, _P]),
+    "ln_forward_stats": (_ST, [_P, _I64, _I64, _F, _P, _SZ, _P, _P, _P]),
+    "ln_forward_apply": (_ST, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "gn_lrelu_x2_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _F, _F, _P]),
+    "rmsnorm_ch_forward": (_ST, [_P, _P, _I64, _I64, _I64, _F, _P]),
+    "fc_gn_forward_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "fc_gn_forward": (_ST, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P, _SZ, _P]),
+}
+
+_LIB = None
+
+
+class NormFwdError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m normalization_ln_forward_amd.build` "
+                               "(hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(status):
+    if status != NORMFWD_OK:
+        raise NormFwdError(status, lib().normfwd_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _opt(t, name, numel, device):
+    if t is None:
+        return
+    _need(t, name, device)
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def alloc_workspace(nbytes, device):
+    """A 256-byte aligned uint8 device buffer of at least nbytes (returned as (buffer, view))."""
+    nbytes = max(int(nbytes), 256)
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf, buf[off:off + nbytes]
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+_LN_SINGLE_WS = {}
+
+
+def ln_forward_workspace_size(outer, inner):
+    return int(lib().ln_forward_workspace_size(outer, inner))
+
+
+def ln_forward_workspace_init(workspace):
+    _check(lib().ln_forward_workspace_init(_ptr(workspace), workspace.numel(), _stream(workspace.device)))
+
+
+def _ln_shape(x, normalized_ndim):
+    nd = x.dim() - 1 if normalized_ndim is None else int(normalized_ndim)
+    if not 0 <= nd <= x.dim():
+        raise ValueError("normalized_ndim out of range")
+    inner = 1
+    for s in x.shape[x.dim() - nd:]:
+        inner *= s
+    outer = x.numel() // inner if inner else 0
+    return outer, inner
+
+
+def _ln_workspace(device, nbytes, variant):
+    """A cached workspace per (device, variant); the single-kernel variant's is zeroed once."""
+    key = (device, variant)
+    hit = _LN_SINGLE_WS.get(key)
+    if hit is None or hit[1].numel() < nbytes:
+        buf, view = alloc_workspace(nbytes, device)
+        if variant == 1:
+            ln_forward_workspace_init(view)
+        hit = (buf, view)
+        _LN_SINGLE_WS[key] = hit
+    return hit[1]
+
+
+def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, variant=0, out=None,
+               workspace=None, mean_out=None, rstd_out=None):
+    """LayerNorm over the trailing ``normalized_ndim`` dims (default: all but dim 0).
+
+    ``variant`` 0 = split (3 kernels), 1 = single cooperative kernel.  A
+    caller-provided ``workspace`` for variant 1 must have been passed through
+    ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if None).
+    """
+    _need(x, "x")
+    dev = x.device
+    outer, inner = _ln_shape(x, normalized_ndim)
+    _opt(weight, "weight", inner, dev)
+    _opt(bias, "bias", inner, dev)
+    _opt(mean_out, "mean_out", outer, dev)
+    _opt(rstd_out, "rstd_out", outer, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", dev)
+    if y.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    nbytes = ln_forward_workspace_size(outer, inner)
+    ws = _ln_workspace(dev, nbytes, variant) if workspace is None else workspace
+    _check(lib().ln_forward(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, float(eps), _ptr(ws),
+                            ws.numel() * ws.element_size(), _ptr(mean_out), _ptr(rstd_out), int(variant),
+                            _stream(dev)))
+    return y
+
+
+def ln_forward_stats(x, eps=1e-5, normalized_ndim=None, workspace=None, mean_out=None, rstd_out=None):
+    """Partial-moment and merge kernels only; returns the workspace holding the statistics."""
+    _need(x, "x")
+    dev = x.device
+    outer, inner = _ln_shape(x, normalized_ndim)
+    _opt(mean_out, "mean_out", outer, dev)
+    _opt(rstd_out, "rstd_out", outer, dev)
+    ws = _ln_workspace(dev, ln_forward_workspace_size(outer, inner), 0) if workspace is None else workspace
+    _check(lib().ln_forward_stats(_ptr(x), outer, inner, float(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _ptr(mean_out), _ptr(rstd_out), _stream(dev)))
+    return ws
+
+
+def ln_forward_apply(x, weight, bias, workspace, normalized_ndim=None, out=None):
+    """Normalize kernel only, from statistics left in ``workspace`` by ln_forward_stats."""
+    _need(x, "x")
+    dev = x.device
+    outer, inner = _ln_shape(x, normalized_ndim)
+    _opt(weight, "weight", inner, dev)
+    _opt(bias, "bias", inner, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", dev)
+    _check(lib().ln_forward_apply(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev)))
+    return y
+
+
+# ---------------------------------------------------------------- GroupNorm + LeakyReLU + x2
+
+def gn_lrelu_x2_forward(x, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01, out=None):
+    """GroupNorm(num_groups) on [N, C], then LeakyReLU(negative_slope), then x + x."""
+    _need(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, C]")
+    N, C = x.shape
+    dev = x.device
+    _opt(gamma, "gamma", C, dev)
+    _opt(beta, "beta", C, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", dev)
+    _check(lib().gn_lrelu_x2_forward(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), N, C, int(num_groups),
+                                     float(eps), float(negative_slope), _stream(dev)))
+    return y
+
+
+# ---------------------------------------------------------------- RMSNorm over dim 1
+
+def rmsnorm_ch_forward(x, eps=1e-5, out=None):
+    """y = x / sqrt(mean over dim 1 of x^2 + eps) for x of shape [B, C, *spatial]."""
+    _need(x, "x")
+    if x.dim() < 2:
+        raise ValueError("x must have at least 2 dims")
+    B, C = x.shape[0], x.shape[1]
+    S = x.numel() // (B * C) if B * C else 0
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", x.device)
+    _check(lib().rmsnorm_ch_forward(_ptr(x), _ptr(y), B, C, S, float(eps), _stream(x.device)))
+    return y
+
+
+# ---------------------------------------------------------------- fc + GroupNorm epilogue
+
+_FC_WS = {}
+
+
+def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01, out=None, workspace=None):
+    """h = x W^T + b (fp32 on the matrix cores), then gn_lrelu_x2_forward on h."""
+    _need(x, "x")
+    _need(W, "W", x.device)
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[1]:
+        raise ValueError("x must be [N, K] and W [C, K]")
+    N, K = x.shape
+    C = W.shape[0]
+    dev = x.device
+    _opt(b, "b", C, dev)
+    _opt(gamma, "gamma", C, dev)
+    _opt(beta, "beta", C, dev)
+    y = torch.empty((N, C), dtype=torch.float32, device=dev) if out is None else out
+    _need(y, "out", dev)
+    nbytes = int(lib().fc_gn_forward_workspace_size(N, K, C))
+    if workspace is None:
+        hit = _FC_WS.get(dev)
+        if hit is None or hit[1].numel() < nbytes:
+            hit = alloc_workspace(nbytes, dev)
+            _FC_WS[dev] = hit
+        workspace = hit[1]
+    _check(lib().fc_gn_forward(_ptr(x), _ptr(W), _ptr(b), _ptr(gamma), _ptr(beta), _ptr(y), N, K, C,
+                               int(num_groups), float(eps), float(negative_slope), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev)))
+    return y

@@ -1,0 +1,208 @@
+// C ABI of libnormfwd: argument validation, status reporting and dispatch
+// to the per-operation launchers.  Declarations and contracts are in
+// include/normfwd.h.
+#include "normfwd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <limits>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+normfwd_status fail(normfwd_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+normfwd_status ok()
+{
+    g_last_error[0] = '\0';
+    return NORMFWD_OK;
+}
+
+normfwd_status hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(NORMFWD_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// Largest element count one tensor may have: grid sizes and 32-bit block
+// indices stay in range below this, with headroom.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+normfwd_status check_ln(const float* x, const float* y, int64_t outer, int64_t inner, float eps)
+{
+    if (!x || !y) return fail(NORMFWD_ERR_INVALID, "ln: x and y must not be NULL");
+    if (outer <= 0 || inner <= 0) return fail(NORMFWD_ERR_INVALID, "ln: outer (%lld) and inner (%lld) must be > 0",
+                                               (long long)outer, (long long)inner);
+    if (outer > kMaxElems / inner) return fail(NORMFWD_ERR_UNSUPPORTED, "ln: outer*inner too large");
+    if (outer > ((int64_t)1 << 22)) return fail(NORMFWD_ERR_UNSUPPORTED, "ln: outer > 2^22 samples");
+    if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "ln: eps must be >= 0");
+    return ok();
+}
+
+normfwd_status check_ws(const void* ws, size_t bytes, size_t need, const char* who)
+{
+    if (!ws) return fail(NORMFWD_ERR_WORKSPACE, "%s: workspace is NULL", who);
+    if (!aligned256(ws)) return fail(NORMFWD_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+    if (bytes < need)
+        return fail(NORMFWD_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, bytes, need);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* normfwd_status_string(normfwd_status s)
+{
+    switch (s) {
+        case NORMFWD_OK: return "NORMFWD_OK";
+        case NORMFWD_ERR_INVALID: return "NORMFWD_ERR_INVALID: invalid argument";
+        case NORMFWD_ERR_UNSUPPORTED: return "NORMFWD_ERR_UNSUPPORTED: arguments valid but not supported";
+        case NORMFWD_ERR_WORKSPACE: return "NORMFWD_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case NORMFWD_ERR_HIP: return "NORMFWD_ERR_HIP: HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* normfwd_last_error(void) { return g_last_error; }
+
+size_t ln_forward_workspace_size(int64_t outer, int64_t inner)
+{
+    if (outer <= 0 || inner <= 0) return 0;
+    return normfwd::ln_layout(outer, inner).total;
+}
+
+normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!workspace || workspace_bytes < 256 || !aligned256(workspace))
+        return fail(NORMFWD_ERR_WORKSPACE, "ln_forward_workspace_init: need a 256-byte aligned workspace of >= 256 bytes");
+    // The whole workspace is cleared: control block, counters and flags.
+    (void)hipGetLastError();
+    return hip_status(normfwd::launch_zero_words(workspace, workspace_bytes, (hipStream_t)stream),
+                      "ln_forward_workspace_init launch");
+}
+
+normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, float eps, void* workspace,
+                                size_t workspace_bytes, float* mean_out, float* rstd_out, void* stream)
+{
+    normfwd_status s = check_ln(x, x, outer, inner, eps);
+    if (s != NORMFWD_OK) return s;
+    const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
+    s = check_ws(workspace, workspace_bytes, lay.total, "ln_forward_stats");
+    if (s != NORMFWD_OK) return s;
+    (void)hipGetLastError();
+    return hip_status(normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out,
+                                               (hipStream_t)stream),
+                      "ln_forward_stats launch");
+}
+
+normfwd_status ln_forward_apply(const float* x, const float* weight, const float* bias, float* y, int64_t outer,
+                                int64_t inner, const void* workspace, size_t workspace_bytes, void* stream)
+{
+    normfwd_status s = check_ln(x, y, outer, inner, 0.0f);
+    if (s != NORMFWD_OK) return s;
+    const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
+    s = check_ws(workspace, workspace_bytes, lay.total, "ln_forward_apply");
+    if (s != NORMFWD_OK) return s;
+    (void)hipGetLastError();
+    return hip_status(normfwd::launch_ln_apply(x, weight, bias, y, outer, inner, workspace, lay, (hipStream_t)stream),
+                      "ln_forward_apply launch");
+}
+
+normfwd_status ln_forward(const float* x, const float* weight, const float* bias, float* y, int64_t outer,
+                          int64_t inner, float eps, void* workspace, size_t workspace_bytes, float* mean_out,
+                          float* rstd_out, int variant, void* stream)
+{
+    normfwd_status s = check_ln(x, y, outer, inner, eps);
+    if (s != NORMFWD_OK) return s;
+    if (variant != 0 && variant != 1) return fail(NORMFWD_ERR_INVALID, "ln_forward: variant must be 0 or 1");
+    const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
+    s = check_ws(workspace, workspace_bytes, lay.total, "ln_forward");
+    if (s != NORMFWD_OK) return s;
+    (void)hipGetLastError();
+    hipStream_t st = (hipStream_t)stream;
+    if (variant == 1)
+        return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
+                                                    rstd_out, st),
+                          "ln_forward (single kernel) launch");
+    hipError_t e = normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out, st);
+    if (e != hipSuccess) return hip_status(e, "ln_forward stats launch");
+    return hip_status(normfwd::launch_ln_apply(x, weight, bias, y, outer, inner, workspace, lay, st),
+                      "ln_forward normalize launch");
+}
+
+normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
+                                   int64_t C, int64_t num_groups, float eps, float negative_slope, void* stream)
+{
+    if (!x || !y) return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: x and y must not be NULL");
+    if (N <= 0 || C <= 0 || num_groups <= 0)
+        return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: N, C and num_groups must be > 0");
+    if (C % num_groups != 0)
+        return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: C (%lld) must be a multiple of num_groups (%lld)",
+                    (long long)C, (long long)num_groups);
+    if (N > kMaxElems / C) return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: N*C too large");
+    if (N * num_groups > ((int64_t)1 << 38))
+        return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: too many groups");
+    if (C / num_groups > std::numeric_limits<int>::max())
+        return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: group too large");
+    if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: eps must be >= 0");
+    (void)hipGetLastError();
+    return hip_status(normfwd::launch_gn_lrelu_x2(x, gamma, beta, y, N, C, num_groups, eps, negative_slope,
+                                                  (hipStream_t)stream),
+                      "gn_lrelu_x2_forward launch");
+}
+
+normfwd_status rmsnorm_ch_forward(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps, void* stream)
+{
+    if (!x || !y) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward: x and y must not be NULL");
+    if (B <= 0 || C <= 0 || S <= 0) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward: B, C and S must be > 0");
+    if (C > std::numeric_limits<int>::max() || S > ((int64_t)1 << 26) || B > kMaxElems / (C * S))
+        return fail(NORMFWD_ERR_UNSUPPORTED, "rmsnorm_ch_forward: shape too large (C < 2^31, S <= 2^26)");
+    if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward: eps must be >= 0");
+    (void)hipGetLastError();
+    return hip_status(normfwd::launch_rms_ch(x, y, B, C, S, eps, (hipStream_t)stream), "rmsnorm_ch_forward launch");
+}
+
+size_t fc_gn_forward_workspace_size(int64_t N, int64_t K, int64_t C)
+{
+    (void)K;
+    if (N <= 0 || C <= 0) return 0;
+    return ((size_t)N * (size_t)C * sizeof(float) + 255) & ~(size_t)255;
+}
+
+normfwd_status fc_gn_forward(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
+                             float* y, int64_t N, int64_t K, int64_t C, int64_t num_groups, float eps,
+                             float negative_slope, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!x || !W || !y) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: x, W and y must not be NULL");
+    if (N <= 0 || K <= 0 || C <= 0 || num_groups <= 0)
+        return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: N, K, C and num_groups must be > 0");
+    if (C % num_groups != 0)
+        return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: C (%lld) must be a multiple of num_groups (%lld)",
+                    (long long)C, (long long)num_groups);
+    if (N > kMaxElems / C || C > kMaxElems / K || N > kMaxElems / K || N > (1 << 23) || C > (1 << 24))
+        return fail(NORMFWD_ERR_UNSUPPORTED, "fc_gn_forward: shape too large");
+    if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: eps must be >= 0");
+    normfwd_status s = check_ws(workspace, workspace_bytes, fc_gn_forward_workspace_size(N, K, C), "fc_gn_forward");
+    if (s != NORMFWD_OK) return s;
+    (void)hipGetLastError();
+    return hip_status(normfwd::launch_fc_gn(x, W, b, gamma, beta, y, N, K, C, num_groups, eps, negative_slope,
+                                            workspace, (hipStream_t)stream),
+                      "fc_gn_forward launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Host-side launchers behind the C ABI (one translation unit per operation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace normfwd {
+
+hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
+                         hipStream_t st);
+
+hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
+                              int64_t C, int64_t G, float eps, float slope, hipStream_t st);
+
+// LayerNorm workspace: byte offsets of each region (all 256-byte aligned).
+struct LnLayout {
+    int64_t P;        // chunks per sample, split variant
+    int64_t chunk;    // elements per chunk, split variant (multiple of 4)
+    int64_t P_cap;    // partial-moment slots per sample (>= chunks of either variant)
+    size_t off_ctrl;  // control block: generation, completion counter, error word
+    size_t off_counter;
+    size_t off_flag;
+    size_t off_stats;
+    size_t off_part;
+    size_t total;
+};
+LnLayout ln_layout(int64_t outer, int64_t inner);
+
+hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float eps, void* ws,
+                           const LnLayout& lay, float* mean_out, float* rstd_out, hipStream_t st);
+hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float* y, int64_t outer,
+                           int64_t inner, const void* ws, const LnLayout& lay, hipStream_t st);
+hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
+                            int64_t inner, float eps, void* ws, const LnLayout& lay, float* mean_out,
+                            float* rstd_out, hipStream_t st);
+
+// Fill bytes/4 32-bit words with zero (a kernel, not a memset, so the call
+// can sit inside a captured HIP graph).
+hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t st);
+
+hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
+                        float* y, int64_t N, int64_t K, int64_t C, int64_t G, float eps, float slope, void* ws,
+                        hipStream_t st);
+
+}  // namespace normfwd

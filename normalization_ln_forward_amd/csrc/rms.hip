@@ -1,0 +1,194 @@
+// RMSNorm along the channel dim of a [B, C, S] tensor
+// (RMS page "Kimi-K2.6 l1_p36", turns 1-2: y = x / sqrt(mean_c x^2 + eps)).
+//
+// Layout: one position (b, s) has its C values S elements apart, so a lane
+// that owns a position walks the channels with stride S while the 64 lanes
+// of a wave own consecutive positions and read each channel row together
+// (RMS page, turn 2, the lane-per-position idea; turn 4 widens it to four
+// positions per lane with 128-bit loads).
+//
+// gfx950 design: a workgroup owns a tile of 64*VEC consecutive positions of
+// one sample.  Its W waves split the C channels, CPW each, and hold their
+// CPW values of the tile in VGPRs, so x is read from HBM exactly once:
+//   1. each wave issues its CPW 128-bit loads (64 lanes x 16 B = one 1 KiB
+//      row segment per channel, fully coalesced), then sums squares;
+//   2. per-lane partial sums cross waves through LDS (W x 64 x 16 B), each
+//      wave adds them in wave order (fixed order: deterministic);
+//   3. each wave scales its held values by 1/sqrt(ms + eps) and writes them
+//      with nontemporal 128-bit stores.
+// Channel counts beyond what fits in registers use a streaming kernel that
+// reads x twice (the second read is served by L2 / MALL when it hits).
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <algorithm>
+
+#ifndef NORMFWD_RMS_CPW
+#define NORMFWD_RMS_CPW 16
+#endif
+
+namespace normfwd {
+
+template <int VEC>
+struct VecOf;
+template <>
+struct VecOf<4> { using T = f4; };
+template <>
+struct VecOf<1> { using T = float; };
+
+template <int CPW, int VEC>
+__global__ void __launch_bounds__(1024)
+rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+{
+    using V = typename VecOf<VEC>::T;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    V* part = reinterpret_cast<V*>(smem_raw);  // [nwaves][64]
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const int64_t b = blockIdx.x / tiles;
+    const int64_t tile = blockIdx.x - b * tiles;
+    const int64_t s = (tile * kWave + lane) * VEC;
+    const bool active = s < S;  // VEC == 4 implies S % 4 == 0: a lane's 4 positions are all in range
+    const int c0 = wave * CPW;
+    const int64_t base = (b * C + c0) * S + s;
+
+    V v[CPW];
+    V acc = V(0.0f);
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+        if (active && c0 + k < C)
+            v[k] = ld_nt(reinterpret_cast<const V*>(x + base + (int64_t)k * S));
+        else
+            v[k] = V(0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) acc += v[k] * v[k];
+
+    part[wave * kWave + lane] = acc;
+    __syncthreads();
+    V tot = part[lane];
+    for (int w = 1; w < nwaves; ++w) tot += part[w * kWave + lane];
+
+    V inv;
+    if constexpr (VEC == 4) {
+        inv.x = 1.0f / sqrtf(tot.x / (float)C + eps);
+        inv.y = 1.0f / sqrtf(tot.y / (float)C + eps);
+        inv.z = 1.0f / sqrtf(tot.z / (float)C + eps);
+        inv.w = 1.0f / sqrtf(tot.w / (float)C + eps);
+    } else {
+        inv = 1.0f / sqrtf(tot / (float)C + eps);
+    }
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+        if (active && c0 + k < C) st_nt(v[k] * inv, reinterpret_cast<V*>(y + base + (int64_t)k * S));
+    }
+}
+
+// Streaming variant for large C: 4 waves split the channels; pass 1 sums
+// squares, pass 2 re-reads x and writes y.
+template <int VEC>
+__global__ void __launch_bounds__(256)
+rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+{
+    using V = typename VecOf<VEC>::T;
+    __shared__ V part[4][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t b = blockIdx.x / tiles;
+    const int64_t tile = blockIdx.x - b * tiles;
+    const int64_t s = (tile * kWave + lane) * VEC;
+    const bool active = s < S;
+    const int per = (int)ceil_div(C, 4);
+    const int c_begin = wave * per;
+    const int c_end = min(C, c_begin + per);
+
+    V acc = V(0.0f);
+    if (active) {
+        for (int c = c_begin; c < c_end; ++c) {
+            V v = *reinterpret_cast<const V*>(x + (b * C + c) * S + s);
+            acc += v * v;
+        }
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    V tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    V inv;
+    if constexpr (VEC == 4) {
+        inv.x = 1.0f / sqrtf(tot.x / (float)C + eps);
+        inv.y = 1.0f / sqrtf(tot.y / (float)C + eps);
+        inv.z = 1.0f / sqrtf(tot.z / (float)C + eps);
+        inv.w = 1.0f / sqrtf(tot.w / (float)C + eps);
+    } else {
+        inv = 1.0f / sqrtf(tot / (float)C + eps);
+    }
+    if (active) {
+        for (int c = c_begin; c < c_end; ++c) {
+            const int64_t off = (b * C + c) * S + s;
+            V v = *reinterpret_cast<const V*>(x + off);
+            st_nt(v * inv, reinterpret_cast<V*>(y + off));
+        }
+    }
+}
+
+// Blocks per launch stay below the 2^32 work-item limit of one grid dimension;
+// larger tensors are launched in batches of whole samples.
+constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
+
+template <int CPW, int VEC>
+static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
+                              hipStream_t st)
+{
+    const int nwaves = (int)ceil_div(C, CPW);
+    const int64_t tiles = ceil_div(S, (int64_t)kWave * VEC);
+    const size_t lds = (size_t)nwaves * kWave * sizeof(typename VecOf<VEC>::T);
+    const int64_t per_launch = std::max<int64_t>(1, kMaxGridItems / (tiles * nwaves * kWave));
+    for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
+        const int64_t nb = std::min(per_launch, B - b0);
+        const int64_t off = b0 * C * S;
+        hipLaunchKernelGGL((rms_ch_hold_kernel<CPW, VEC>), dim3((unsigned)(nb * tiles)), dim3(nwaves * kWave),
+                           lds, st, x + off, y + off, (int)C, S, tiles, eps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int VEC>
+static hipError_t launch_stream(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
+                                hipStream_t st)
+{
+    const int64_t tiles = ceil_div(S, (int64_t)kWave * VEC);
+    const int64_t per_launch = std::max<int64_t>(1, kMaxGridItems / (tiles * 256));
+    for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
+        const int64_t nb = std::min(per_launch, B - b0);
+        const int64_t off = b0 * C * S;
+        hipLaunchKernelGGL((rms_ch_stream_kernel<VEC>), dim3((unsigned)(nb * tiles)), dim3(256), 0, st,
+                           x + off, y + off, (int)C, S, tiles, eps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int VEC>
+static hipError_t launch_vec(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
+                             hipStream_t st)
+{
+    // Register-held kernel while C fits in at most 16 waves of CPW channels.
+    constexpr int cpw = NORMFWD_RMS_CPW;
+    if (C <= 16 * cpw) return launch_hold<cpw, VEC>(x, y, B, C, S, eps, st);
+    if (C <= 16 * 32) return launch_hold<32, VEC>(x, y, B, C, S, eps, st);
+    return launch_stream<VEC>(x, y, B, C, S, eps, st);
+}
+
+hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
+                         hipStream_t st)
+{
+    const bool vec4 = (S % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+    return vec4 ? launch_vec<4>(x, y, B, C, S, eps, st) : launch_vec<1>(x, y, B, C, S, eps, st);
+}
+
+}  // namespace normfwd

@@ -1,0 +1,123 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol, and
+rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+from normalization_ln_forward_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "normfwd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libnormfwd.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.normfwd_status_string(code).decode().startswith(name)
+    assert lib.normfwd_status_string(99).decode() == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+FAKE_WS = ctypes.c_void_p(0x200000)  # 256-byte aligned
+
+
+def _err(code):
+    return code, _lib.lib().normfwd_last_error().decode()
+
+
+def test_ln_validation():
+    lib = _lib.lib()
+    st, msg = _err(lib.ln_forward(None, None, None, FAKE, 2, 8, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
+    assert st == 1 and "NULL" in msg
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 0, 8, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
+    assert st == 1
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 2, -1, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
+    assert st == 1
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 2, 8, 1e-5, FAKE_WS, 1 << 20, None, None, 7, None))
+    assert st == 1
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 2, 8, -1.0, FAKE_WS, 1 << 20, None, None, 0, None))
+    assert st == 1
+    need = lib.ln_forward_workspace_size(16, 4194304)
+    assert need > 16 * 256 * 32
+    st, msg = _err(lib.ln_forward(FAKE, None, None, FAKE, 16, 4194304, 1e-5, FAKE_WS, need - 1, None, None, 0,
+                                  None))
+    assert st == 3 and "needs" in msg
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 16, 4194304, 1e-5, None, need, None, None, 0, None))
+    assert st == 3
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 16, 4194304, 1e-5, ctypes.c_void_p(0x200010), need,
+                                None, None, 0, None))
+    assert st == 3
+    st, _ = _err(lib.ln_forward_stats(FAKE, 16, 4194304, 1e-5, FAKE_WS, 100, None, None, None))
+    assert st == 3
+    st, _ = _err(lib.ln_forward_apply(FAKE, None, None, None, 16, 4194304, FAKE_WS, need, None))
+    assert st == 1
+    assert lib.ln_forward_workspace_size(0, 5) == 0
+    st, _ = _err(lib.ln_forward_workspace_init(None, 1024, None))
+    assert st == 3
+
+
+def test_ln_workspace_size_monotone():
+    lib = _lib.lib()
+    prev = 0
+    for outer in (1, 2, 16, 100):
+        s = lib.ln_forward_workspace_size(outer, 4194304)
+        assert s > prev and s % 256 == 0
+        prev = s
+
+
+def test_gn_validation():
+    lib = _lib.lib()
+    st, msg = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 10, 3, 1e-5, 0.01, None))
+    assert st == 1 and "multiple" in msg
+    st, _ = _err(lib.gn_lrelu_x2_forward(None, None, None, FAKE, 4, 12, 3, 1e-5, 0.01, None))
+    assert st == 1
+    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 0, 12, 3, 1e-5, 0.01, None))
+    assert st == 1
+    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 12, 0, 1e-5, 0.01, None))
+    assert st == 1
+
+
+def test_rms_validation():
+    lib = _lib.lib()
+    st, _ = _err(lib.rmsnorm_ch_forward(None, FAKE, 2, 3, 4, 1e-5, None))
+    assert st == 1
+    st, _ = _err(lib.rmsnorm_ch_forward(FAKE, FAKE, 2, 0, 4, 1e-5, None))
+    assert st == 1
+    st, _ = _err(lib.rmsnorm_ch_forward(FAKE, FAKE, 2, 3, 1 << 30, 1e-5, None))
+    assert st == 2
+
+
+def test_fc_validation():
+    lib = _lib.lib()
+    need = lib.fc_gn_forward_workspace_size(1024, 8192, 8192)
+    assert need == 1024 * 8192 * 4
+    st, _ = _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, 1024, 8192, 8192, 500, 1e-5, 0.01, FAKE_WS,
+                                   need, None))
+    assert st == 1
+    st, _ = _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, 1024, 8192, 8192, 512, 1e-5, 0.01, FAKE_WS,
+                                   need - 4, None))
+    assert st == 3
+    st, _ = _err(lib.fc_gn_forward(FAKE, None, None, None, None, FAKE, 1024, 8192, 8192, 512, 1e-5, 0.01, FAKE_WS,
+                                   need, None))
+    assert st == 1

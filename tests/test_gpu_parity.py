@@ -1,0 +1,275 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Pass rule, elementwise: |g - o| <= atol + rtol*|o| with g finite, where o is
+the oracle's unrounded fp64 value.  atol = rtol = 1e-4 for the three norms,
+rtol = 2e-3 for the fc path (fp32 accumulation over K = 8192 products).
+Inputs come from the shared seeded generators (normalization_ln_forward_amd.synth)
+with the workloads' distributions; small cases span several tiles and ragged
+tails, full-size cases use the workloads' own shapes.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from normalization_ln_forward_amd import _lib, synth
+import normalization_ln_forward_amd as nf
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-4
+RTOL = 1e-4
+RTOL_FC = 2e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()  # fail loudly if the library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def _assert_close(got, ref, atol=ATOL, rtol=RTOL, what=""):
+    rep = oracle.allclose_report(got, ref, atol, rtol)
+    assert rep["ok"], f"{what}: {rep}"
+    return rep
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# ---------------------------------------------------------------- GroupNorm + LeakyReLU + x2
+
+GN_CASES = [
+    # (N, C, G, affine, misalign)  -> path
+    (5, 8192, 512, True, False),     # fast path, M=16, several tiles per row
+    (3, 1000, 125, True, False),     # fast, M=8, ragged last tile (C/4 = 250)
+    (7, 48, 3, True, False),         # fast, M=16, tile shorter than a wave
+    (4, 256, 64, True, False),       # fast, M=4 (one lane per group)
+    (2, 1024, 4, True, False),       # fast, M=256 (64 lanes per group)
+    (3, 8192, 16, True, False),      # generic wave kernel, M=512
+    (6, 35, 7, True, False),         # generic lane kernel, M=5
+    (2, 300, 3, True, False),        # generic wave kernel, M=100
+    (4, 24, 24, True, False),        # M=1: output is 2*lrelu(beta)
+    (5, 8192, 512, False, False),    # no affine
+    (5, 4096, 256, True, True),      # misaligned base pointer -> generic path
+]
+
+
+@pytest.mark.parametrize("N,C,G,affine,misalign", GN_CASES)
+def test_gn_parity(N, C, G, affine, misalign):
+    _say(f"gn N={N} C={C} G={G} affine={affine} misalign={misalign}")
+    d = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(N, C), seed=7 + N + C)
+    x = d["x"]
+    if misalign:
+        buf = torch.empty(N * C + 1, device="cuda")
+        buf[1:].copy_(x.reshape(-1))
+        x = buf[1:].view(N, C)
+    gamma = d["gamma"] if affine else None
+    beta = d["beta"] if affine else None
+    y = nf.gn_lrelu_x2_forward(x, gamma, beta, G, eps=1e-5, negative_slope=0.01)
+    ref = oracle.gn_lrelu_x2(_np(x), None if gamma is None else _np(gamma), None if beta is None else _np(beta),
+                             G, eps=1e-5, negative_slope=0.01)
+    _assert_close(_np(y), ref, what="gn")
+
+
+def test_gn_full_size_and_determinism():
+    _say("gn full 1024x8192 G=512")
+    d = synth.make("gn_lrelu_x2_1024x8192", device="cuda")
+    y1 = nf.gn_lrelu_x2_forward(d["x"], d["gamma"], d["beta"], 512)
+    y2 = nf.gn_lrelu_x2_forward(d["x"], d["gamma"], d["beta"], 512)
+    ref = oracle.gn_lrelu_x2(_np(d["x"]), _np(d["gamma"]), _np(d["beta"]), 512)
+    rep = _assert_close(_np(y1), ref, what="gn full")
+    _say(f"  max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}")
+    assert torch.equal(y1, y2)
+
+
+def test_gn_in_place():
+    _say("gn in place")
+    d = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(64, 8192), seed=11)
+    ref = oracle.gn_lrelu_x2(_np(d["x"]), _np(d["gamma"]), _np(d["beta"]), 512)
+    x = d["x"].clone()
+    nf.gn_lrelu_x2_forward(x, d["gamma"], d["beta"], 512, out=x)
+    _assert_close(_np(x), ref, what="gn in place")
+
+
+# ---------------------------------------------------------------- RMSNorm over dim 1
+
+RMS_CASES = [
+    # shape, misalign
+    ((3, 64, 1000), False),          # 128-bit path, ragged tile
+    ((3, 64, 1001), False),          # scalar path (S % 4 != 0)
+    ((2, 1, 512), False),            # C = 1
+    ((2, 3, 256), False),            # C < channels per wave
+    ((2, 100, 260), False),          # 7 waves, last one partial
+    ((2, 300, 64), False),           # 32 channels per wave
+    ((2, 600, 64), False),           # streaming kernel (C > 512)
+    ((4, 64, 32, 32), False),        # 4-D input
+    ((2, 64, 1024), True),           # misaligned -> scalar path
+]
+
+
+@pytest.mark.parametrize("shape,misalign", RMS_CASES)
+def test_rms_parity(shape, misalign):
+    _say(f"rms shape={shape} misalign={misalign}")
+    d = synth.make("rms_ch_112x64x512x512", device="cuda", shape=shape, seed=sum(shape))
+    x = d["x"]
+    if misalign:
+        buf = torch.empty(x.numel() + 1, device="cuda")
+        buf[1:].copy_(x.reshape(-1))
+        x = buf[1:].view(shape)
+    y = nf.rmsnorm_ch_forward(x, eps=1e-5)
+    ref = oracle.rms_ch(_np(x), eps=1e-5)
+    _assert_close(_np(y), ref, what="rms")
+
+
+def test_rms_in_place():
+    _say("rms in place")
+    d = synth.make("rms_ch_112x64x512x512", device="cuda", shape=(2, 64, 4096), seed=5)
+    ref = oracle.rms_ch(_np(d["x"]))
+    x = d["x"].clone()
+    nf.rmsnorm_ch_forward(x, out=x)
+    _assert_close(_np(x), ref, what="rms in place")
+
+
+def test_rms_full_size_sampled():
+    """The full [112, 64, 512, 512] workload in the benchmark's launch; whole samples checked."""
+    _say("rms full 112x64x512x512 (sampled samples)")
+    d = synth.make("rms_ch_112x64x512x512", device="cuda")
+    x = d["x"]
+    y = nf.rmsnorm_ch_forward(x, eps=1e-5)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    for b in sorted({0, 111, *rng.choice(112, 4, replace=False).tolist()}):
+        ref = oracle.rms_ch(_np(x[b:b + 1]))
+        rep = _assert_close(_np(y[b:b + 1]), ref, what=f"rms full sample {b}")
+        _say(f"  sample {b}: max_abs={rep['max_abs']:.3e}")
+    y2 = nf.rmsnorm_ch_forward(x, eps=1e-5)
+    assert torch.equal(y, y2)
+    del x, y, y2, d
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+LN_CASES = [
+    # (outer, inner, affine, variant)
+    (3, 5000, True, 0),
+    (3, 5000, True, 1),
+    (2, 40000, True, 0),             # 3 chunks, ragged last
+    (2, 40000, True, 1),
+    (4, 40001, True, 0),             # scalar path (inner % 4 != 0)
+    (4, 40001, True, 1),
+    (5, 1, True, 0),                 # one element per sample: y = bias
+    (5, 1, True, 1),
+    (3, 300000, False, 0),           # no affine
+    (3, 300000, False, 1),
+    (1, 1 << 20, True, 1),           # one sample, many workgroups
+]
+
+
+@pytest.mark.parametrize("outer,inner,affine,variant", LN_CASES)
+def test_ln_parity(outer, inner, affine, variant):
+    _say(f"ln outer={outer} inner={inner} affine={affine} variant={variant}")
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=(outer, inner), seed=outer * 7 + inner,
+                   normalized_ndim=1)
+    w = d["weight"] if affine else None
+    b = d["bias"] if affine else None
+    mean = torch.empty(outer, device="cuda")
+    rstd = torch.empty(outer, device="cuda")
+    y = nf.ln_forward(d["x"], w, b, eps=1e-5, variant=variant, mean_out=mean, rstd_out=rstd)
+    ref, om, ov = oracle.ln(_np(d["x"]), None if w is None else _np(w), None if b is None else _np(b), eps=1e-5,
+                            return_stats=True)
+    _assert_close(_np(y), ref, what="ln")
+    np.testing.assert_allclose(_np(mean), om, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(_np(rstd), 1.0 / np.sqrt(ov + np.float32(1e-5)), rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["ln_16x64x256x256", "ln_stress_16x64x256x256"])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_ln_full_size(name, variant):
+    """Full [16, 64, 256, 256] workloads, N(0,1) and the N(100, 0.01) cancellation stress."""
+    _say(f"ln full {name} variant={variant}")
+    d = synth.make(name, device="cuda")
+    y = nf.ln_forward(d["x"], d["weight"], d["bias"], eps=1e-5, variant=variant)
+    ref = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]), eps=1e-5)
+    rep = _assert_close(_np(y), ref, what=name)
+    _say(f"  max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}")
+    y2 = nf.ln_forward(d["x"], d["weight"], d["bias"], eps=1e-5, variant=variant)
+    assert torch.equal(y, y2), "not bitwise deterministic"
+
+
+def test_ln_single_kernel_repeated_and_split_halves():
+    """Many back-to-back single-kernel launches on one workspace stay bitwise equal and
+    leave the control block clean; stats + apply equals the split variant."""
+    _say("ln single repeated")
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=(4, 1 << 19), normalized_ndim=1, seed=3)
+    outer, inner = 4, 1 << 19
+    nbytes = nf.ln_forward_workspace_size(outer, inner)
+    _, ws = nf.alloc_workspace(nbytes, "cuda")
+    nf.ln_forward_workspace_init(ws)
+    first = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws)
+    for _ in range(50):
+        again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws)
+        assert torch.equal(first, again)
+    torch.cuda.synchronize()
+    ctrl = ws[:16].view(torch.int32).cpu().tolist()  # gen, done, error, pad
+    assert ctrl[1] == 0 and ctrl[2] == 0, ctrl
+    assert ctrl[0] == 51, ctrl
+    ws0 = nf.ln_forward_stats(d["x"])
+    halves = nf.ln_forward_apply(d["x"], d["weight"], d["bias"], ws0)
+    split = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=0)
+    assert torch.equal(halves, split)
+    ref = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]))
+    _assert_close(_np(first), ref, what="ln single")
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_ln_in_place(variant):
+    _say(f"ln in place variant={variant}")
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=(3, 100000), normalized_ndim=1, seed=9)
+    ref = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]))
+    x = d["x"].clone()
+    nf.ln_forward(x, d["weight"], d["bias"], variant=variant, out=x)
+    _assert_close(_np(x), ref, what="ln in place")
+
+
+# ---------------------------------------------------------------- fc -> GroupNorm epilogue
+
+FC_CASES = [
+    # (N, K, C, G)
+    (100, 96, 384, 24),     # ragged row tile (100 < 128), 3 column tiles
+    (130, 70, 256, 16),     # K % 4 != 0 -> scalar tile loader, 2 row tiles
+    (64, 512, 160, 10),     # ragged column tile, M = 16
+]
+
+
+@pytest.mark.parametrize("N,K,C,G", FC_CASES)
+def test_fc_gn_parity(N, K, C, G):
+    _say(f"fc N={N} K={K} C={C} G={G}")
+    d = synth.make("fc_gn_1024x8192x8192", device="cuda", shape=(N, K), hidden=C, seed=N + K + C)
+    y = nf.fc_gn_forward(d["x"], d["W"], d["b"], d["gamma"], d["beta"], G)
+    ref = oracle.fc_gn_lrelu_x2(_np(d["x"]), _np(d["W"]), _np(d["b"]), _np(d["gamma"]), _np(d["beta"]), G)
+    _assert_close(_np(y), ref, rtol=RTOL_FC, what="fc_gn")
+
+
+def test_fc_gn_full_size_sampled_rows():
+    """Full 1024 x 8192 x 8192 problem; the oracle recomputes a sample of rows."""
+    _say("fc full 1024x8192x8192 (sampled rows)")
+    d = synth.make("fc_gn_1024x8192x8192", device="cuda")
+    y = nf.fc_gn_forward(d["x"], d["W"], d["b"], d["gamma"], d["beta"], 512)
+    rows = [0, 1, 127, 128, 511, 1023]
+    ref = oracle.fc_gn_lrelu_x2(_np(d["x"][rows]), _np(d["W"]), _np(d["b"]), _np(d["gamma"]), _np(d["beta"]), 512)
+    rep = _assert_close(_np(y[rows]), ref, rtol=RTOL_FC, what="fc full")
+    _say(f"  max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}")
