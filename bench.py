@@ -14,13 +14,15 @@ RMSNorm over dim 1 [112, 64, 512, 512], the LN N(100, 0.01) stress input,
 both LN schedules, and fc+GN [1024 x 8192 x 8192] (TFLOP/s).
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
-torch.cuda.synchronize(); per-launch kernel durations from HIP events
-recorded on the stream the library launches on (torch's current stream).
+torch.cuda.synchronize(); average launch durations from a pair of HIP events
+recorded around the K launches on the stream the library launches on
+(torch's current stream).  Calls are validated and marshalled once before the
+timed region (normalization_ln_forward_amd.prepare), so the host enqueues
+faster than the GPU drains and the GPU never waits for Python.
 Inputs rotate over several buffer sets (>= 2 GiB working set) so the 256 MB
 Infinity Cache cannot hold a step's inputs from the previous step.
 """
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -42,27 +44,21 @@ RMS_BYTES = 4 * 2 * 112 * 64 * 512 * 512                              # 15,032,3
 FC_FLOPS = 2 * 1024 * 8192 * 8192                                     # 137,438,953,472
 FC_GN_BYTES = 4 * (1024 * 8192 + 8192 * 8192 + 8192 + 1024 * 8192)    # x, W, b, h write (GEMM part)
 
-CSRC = os.path.join(ROOT, "normalization_ln_forward_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workloads.json")
 
 
-def source_sha(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary (FETCH_SIZE + WRITE_SIZE, scaled by
+    a plain copy of known size), or None if the summary is missing or the kernel's source changed since."""
+    from normalization_ln_forward_amd import profiling
 
-
-def traffic_for(kernel, files):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if the kernel source is unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             entries = json.load(f)
     except (OSError, ValueError):
         return None
     e = entries.get(kernel)
-    if not e or e.get("source_sha") != source_sha(files):
+    if not e or e.get("source_sha") != profiling.source_sha(profiling.KERNEL_SOURCES[kernel]):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -72,12 +68,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--variant", type=int, default=None, choices=[0, 1],
-                    help="LN schedule for the headline (default: the library's fastest measured, 1)")
+    ap.add_argument("--variant", type=int, default=0, choices=[0, 1],
+                    help="LN schedule for the headline: 0 = split (default, fastest measured), 1 = single kernel")
     ap.add_argument("--rotate", type=int, default=4, help="LN buffer sets rotated through (>=1)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB a few times (reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     return ap.parse_args()
 
 
@@ -98,7 +97,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     nf.lib()
-    variant = 1 if args.variant is None else args.variant
+    variant = args.variant
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -114,52 +113,59 @@ def main():
     _, ws = nf.alloc_workspace(nf.ln_forward_workspace_size(outer, inner), dev)
     nf.ln_forward_workspace_init(ws)
     stream = torch.cuda.current_stream(dev)
-
-    def ln_step(i, ev=None):
-        x, y = xs[i % R], ys[i % R]
-        if variant == 1:
-            if ev:
-                ev[0].record(stream)
-            nf.ln_forward(x, w, b, variant=1, out=y, workspace=ws)
-            if ev:
-                ev[1].record(stream)
-        else:
-            if ev:
-                ev[0].record(stream)
-            nf.ln_forward_stats(x, workspace=ws)
-            if ev:
-                ev[1].record(stream)
-            nf.ln_forward_apply(x, w, b, ws, out=y)
-            if ev:
-                ev[2].record(stream)
-
-    for i in range(args.warmup):
-        ln_step(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ln_step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / args.steps
-    value = LN_BYTES / (ms_per_step / 1e3) / 1e9
+    # argument checking and marshalling happen once per buffer set, outside the timed region
     if variant == 1:
-        dur = [e[0].elapsed_time(e[1]) for e in evs]
-        dom_kernel, dom_bytes, dom_files = "ln_single_kernel", LN_BYTES, ["ln.hip", "common.hpp"]
+        steps = [nf.prepare(nf.ln_forward, xs[r], w, b, variant=1, out=ys[r], workspace=ws) for r in range(R)]
+        t = time_launches(torch, stream, lambda i: steps[i % R](), args.steps, args.warmup)
+        ms_per_step = t["wall_ms"]
+        # the single-read kernel moves x once: its own algorithmic bytes are the normalize pass's
+        dom_kernel, dom_bytes, avg_ms = "ln_single_hold_kernel", LN_NORMALIZE_BYTES, t["avg_ms"]
     else:
-        dur = [e[1].elapsed_time(e[2]) for e in evs]
-        dom_kernel, dom_bytes, dom_files = "ln_normalize_kernel", LN_NORMALIZE_BYTES, ["ln.hip", "common.hpp"]
-    avg_ms = sum(dur) / len(dur)
+        # the step is the two halves of the split schedule; events between them time the
+        # normalize kernel inside the step itself
+        stats = [nf.prepare(nf.ln_forward_stats, xs[r], workspace=ws) for r in range(R)]
+        applies = [nf.prepare(nf.ln_forward_apply, xs[r], w, b, ws, out=ys[r]) for r in range(R)]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+
+        def step(i):
+            stats[i % R]()
+            evs[i][0].record(stream)
+            applies[i % R]()
+            evs[i][1].record(stream)
+
+        def plain_step(i):
+            stats[i % R]()
+            applies[i % R]()
+
+        # the timed steps carry no events between kernels (an event between two kernels can keep
+        # them from overlapping); a second, identical loop with events times the normalize kernel
+        t = time_launches(torch, stream, plain_step, args.steps, args.warmup)
+        ms_per_step = t["wall_ms"]
+        time_launches(torch, stream, step, args.steps, 0)
+        dom_kernel, dom_bytes = "ln_normalize_rows_kernel", LN_NORMALIZE_BYTES
+        avg_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / len(evs)
+    value = LN_BYTES / (ms_per_step / 1e3) / 1e9
     achieved = dom_bytes / (avg_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(dom_kernel, dom_files),
+                "traffic": traffic_for(dom_kernel),
                 "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": round(avg_ms, 5)}
     log(f"[bench] LN: {ms_per_step:.4f} ms/step wall, {value:.1f} GB/s; {dom_kernel} {avg_ms:.4f} ms, "
         f"{achieved:.1f} GB/s")
     del xs, ys
     torch.cuda.empty_cache()
+
+    if args.copy_ref > 0:
+        n = args.copy_ref * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy reference: 3 x {args.copy_ref} MiB")
+        del src, dst
+        torch.cuda.empty_cache()
 
     kernels = {}
     if not args.no_kernels:
@@ -186,19 +192,21 @@ def main():
 
 
 def time_launches(torch, stream, fn, steps, warmup):
+    """Run fn(i) for i < warmup untimed, then `steps` times between two HIP
+    events on `stream`, bracketed by synchronize() for the wall clock.
+    Returns the average per launch from the events and from the wall clock."""
     for i in range(warmup):
         fn(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        evs[i][0].record(stream)
         fn(i)
-        evs[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    d = sorted(a.elapsed_time(b) for a, b in evs)
-    return {"avg_ms": sum(d) / len(d), "median_ms": d[len(d) // 2], "min_ms": d[0], "wall_ms": 1e3 * wall}
+    return {"avg_ms": e0.elapsed_time(e1) / steps, "wall_ms": 1e3 * wall}
 
 
 def _entry(t, nbytes=None, flops=None):
@@ -223,8 +231,8 @@ def per_kernel_table(torch, nf, synth, dev, stream, args, log):
     R = 32
     xs = [g["x"]] + [synth.make("gn_lrelu_x2_1024x8192", device=dev, seed=3000 + i)["x"] for i in range(1, R)]
     ys = [torch.empty_like(g["x"]) for _ in range(R)]
-    t = time_launches(torch, stream, lambda i: nf.gn_lrelu_x2_forward(xs[i % R], g["gamma"], g["beta"], 512,
-                                                                      out=ys[i % R]), max(steps, 64), warm)
+    calls = [nf.prepare(nf.gn_lrelu_x2_forward, xs[r], g["gamma"], g["beta"], 512, out=ys[r]) for r in range(R)]
+    t = time_launches(torch, stream, lambda i: calls[i % R](), max(steps, 64), warm)
     out["gn_lrelu_x2_1024x8192"] = _entry(t, GN_BYTES)
     del xs, ys
     torch.cuda.empty_cache()
@@ -237,8 +245,9 @@ def per_kernel_table(torch, nf, synth, dev, stream, args, log):
         y2 = torch.empty_like(d["x"])
         for variant in (0, 1):
             log(f"[bench] {name} variant={variant}")
-            t = time_launches(torch, stream, lambda i: nf.ln_forward(
-                (d["x"], x2)[i % 2], d["weight"], d["bias"], variant=variant, out=(y, y2)[i % 2]), steps, warm)
+            calls = [nf.prepare(nf.ln_forward, xx, d["weight"], d["bias"], variant=variant, out=yy)
+                     for xx, yy in ((d["x"], y), (x2, y2))]
+            t = time_launches(torch, stream, lambda i: calls[i % 2](), steps, warm)
             out[f"{name}/{['split', 'single'][variant]}"] = _entry(t, LN_BYTES)
         del d, y, x2, y2
         torch.cuda.empty_cache()
@@ -247,7 +256,8 @@ def per_kernel_table(torch, nf, synth, dev, stream, args, log):
     log("[bench] RMS [112, 64, 512, 512]")
     r = synth.make("rms_ch_112x64x512x512", device=dev)
     y = torch.empty_like(r["x"])
-    t = time_launches(torch, stream, lambda i: nf.rmsnorm_ch_forward(r["x"], out=y), max(5, steps // 4), 2)
+    call = nf.prepare(nf.rmsnorm_ch_forward, r["x"], out=y)
+    t = time_launches(torch, stream, lambda i: call(), max(5, steps // 4), 2)
     out["rms_ch_112x64x512x512"] = _entry(t, RMS_BYTES)
     del r, y
     torch.cuda.empty_cache()
@@ -256,8 +266,8 @@ def per_kernel_table(torch, nf, synth, dev, stream, args, log):
     log("[bench] fc+GN [1024 x 8192 x 8192]")
     f = synth.make("fc_gn_1024x8192x8192", device=dev)
     y = torch.empty(1024, 8192, device=dev)
-    t = time_launches(torch, stream, lambda i: nf.fc_gn_forward(f["x"], f["W"], f["b"], f["gamma"], f["beta"], 512,
-                                                               out=y), max(5, steps // 4), 2)
+    call = nf.prepare(nf.fc_gn_forward, f["x"], f["W"], f["b"], f["gamma"], f["beta"], 512, out=y)
+    t = time_launches(torch, stream, lambda i: call(), max(5, steps // 4), 2)
     out["fc_gn_1024x8192x8192"] = _entry(t, flops=FC_FLOPS)
     del f, y
     torch.cuda.empty_cache()

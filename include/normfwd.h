@@ -55,8 +55,8 @@ const char* normfwd_last_error(void);
  * all elements of normalized_shape; y = (x - mean) / sqrt(var + eps) * weight
  * + bias, weight and bias elementwise of normalized_shape.  Turn 2 splits
  * each sample over many workgroups that write partial moments, reduces them
- * per sample, then normalizes.  Turn 6 sketches the single-kernel variant in
- * which the last workgroup to finish a sample reduces it.)
+ * per sample, then normalizes.  Turn 6 lets the last workgroup to finish a
+ * sample do that reduction, which the single-kernel variant does.)
  *
  *   x, y      [outer, inner] fp32; inner = prod(normalized_shape)
  *   weight    [inner] fp32 or NULL (= all ones)
@@ -65,16 +65,21 @@ const char* normfwd_last_error(void);
  *   mean_out  [outer] fp32 or NULL: the sample mean, rounded to fp32
  *   rstd_out  [outer] fp32 or NULL: 1 / sqrt(var + eps), rounded to fp32
  *   workspace device buffer of at least ln_forward_workspace_size(outer,
- *             inner) bytes, 256-byte aligned.  It holds per-chunk partial
- *             moments, per-sample statistics and (variant 1) a control
- *             block of counters.  One workspace must not be used by two
+ *             inner) bytes, 256-byte aligned, zeroed once by
+ *             ln_forward_workspace_init() before its first use (each call
+ *             leaves it ready for the next).  It holds per-workgroup partial
+ *             moments, per-sample statistics and the arrival counters the
+ *             kernels synchronize on.  One workspace must not be used by two
  *             calls that may run concurrently.
- *   variant   0 = split: partial-moments kernel, per-sample merge kernel,
- *                 normalize kernel;
- *             1 = single kernel: the same three phases in one cooperative
- *                 launch, the last workgroup to finish a sample merges it.
- *                 Needs a workspace whose control block was zeroed once by
- *                 ln_forward_workspace_init(); each call leaves it reusable.
+ *   variant   0 = split: a partial-moments kernel, a per-sample merge kernel
+ *                 and a normalize kernel;
+ *             1 = single kernel: one cooperative launch in which every
+ *                 workgroup keeps its share of each sample in registers
+ *                 between the moments pass and the normalize pass (x is
+ *                 read from HBM once) and waits for the sample's merged
+ *                 statistics; shapes it cannot hold (inner % 4 != 0,
+ *                 unaligned pointers, more rows than co-resident
+ *                 workgroups can keep) run the split schedule instead.
  *
  * Statistics are exact to about 1e-7 relative even when |mean| >> std: the
  * partial moments are accumulated around a per-sample shift (the sample's
@@ -84,7 +89,8 @@ const char* normfwd_last_error(void);
  * ---------------------------------------------------------------------- */
 size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
 
-/* Zero the control block of `workspace` (enqueued on `stream`). */
+/* Zero `workspace` (enqueued on `stream`, as a kernel: safe inside a
+ * captured HIP graph).  Required once before a workspace's first use. */
 normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 normfwd_status ln_forward(const float* x, const float* weight, const float* bias, float* y,
@@ -93,10 +99,10 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
                           float* mean_out, float* rstd_out, int variant, void* stream);
 
 /* The split variant's two halves, for callers that want the statistics
- * alone or want to time the phases: ln_forward_stats runs the partial and
- * merge kernels and leaves per-sample (mean hi, mean lo, rstd) in the
- * workspace; ln_forward_apply runs the normalize kernel from them.  Calling
- * stats then apply on one stream equals ln_forward(..., variant 0, ...). */
+ * alone or want to time the phases: ln_forward_stats runs the moments and
+ * merge kernels and leaves per-sample (mean hi, mean lo, rstd) in the workspace;
+ * ln_forward_apply runs the normalize kernel from them.  Calling stats then
+ * apply on one stream equals ln_forward(..., variant 0, ...). */
 normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, float eps,
                                 void* workspace, size_t workspace_bytes,
                                 float* mean_out, float* rstd_out, void* stream);

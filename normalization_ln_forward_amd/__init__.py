@@ -17,5 +17,6 @@ from ._lib import (  # noqa: F401
     ln_forward_stats,
     ln_forward_workspace_init,
     ln_forward_workspace_size,
+    prepare,
     rmsnorm_ch_forward,
 )

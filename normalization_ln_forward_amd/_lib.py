@@ -72,6 +72,42 @@ def _check(status):
         raise NormFwdError(status, lib().normfwd_last_error().decode())
 
 
+_capture = None
+
+
+def _invoke(name, *args):
+    """Call C entry point `name`, or record the marshalled call while prepare() runs."""
+    if _capture is not None:
+        _capture.append((name, args))
+        return
+    _check(getattr(lib(), name)(*args))
+
+
+def prepare(fn, *args, **kwargs):
+    """Validate and marshal one call of a binding function once; return a
+    zero-argument callable that re-issues the same C call(s) (same tensors,
+    same stream) with no Python-side checks.  For tight launch loops, where
+    per-call argument checking would otherwise cost more host time than the
+    kernels take on the GPU."""
+    global _capture
+    _capture = []
+    try:
+        out = fn(*args, **kwargs)
+    finally:
+        calls, _capture = _capture, None
+    handle = lib()
+    bound = [(getattr(handle, name), a) for name, a in calls]
+
+    def run():
+        for f, a in bound:
+            st = f(*a)
+            if st != NORMFWD_OK:
+                _check(st)
+        return out
+
+    return run
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -111,7 +147,7 @@ def alloc_workspace(nbytes, device):
 
 # ---------------------------------------------------------------- LayerNorm
 
-_LN_SINGLE_WS = {}
+_LN_WS = {}
 
 
 def ln_forward_workspace_size(outer, inner):
@@ -133,16 +169,14 @@ def _ln_shape(x, normalized_ndim):
     return outer, inner
 
 
-def _ln_workspace(device, nbytes, variant):
-    """A cached workspace per (device, variant); the single-kernel variant's is zeroed once."""
-    key = (device, variant)
-    hit = _LN_SINGLE_WS.get(key)
+def _ln_workspace(device, nbytes):
+    """A cached workspace per device, zeroed once by ln_forward_workspace_init."""
+    hit = _LN_WS.get(device)
     if hit is None or hit[1].numel() < nbytes:
         buf, view = alloc_workspace(nbytes, device)
-        if variant == 1:
-            ln_forward_workspace_init(view)
+        ln_forward_workspace_init(view)
         hit = (buf, view)
-        _LN_SINGLE_WS[key] = hit
+        _LN_WS[device] = hit
     return hit[1]
 
 
@@ -150,9 +184,10 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
                workspace=None, mean_out=None, rstd_out=None):
     """LayerNorm over the trailing ``normalized_ndim`` dims (default: all but dim 0).
 
-    ``variant`` 0 = split (3 kernels), 1 = single cooperative kernel.  A
-    caller-provided ``workspace`` for variant 1 must have been passed through
-    ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if None).
+    ``variant`` 0 = split (moments kernel + normalize kernel), 1 = single
+    cooperative kernel.  A caller-provided ``workspace`` must have been passed
+    through ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if
+    None).
     """
     _need(x, "x")
     dev = x.device
@@ -166,10 +201,10 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
     if y.shape != x.shape:
         raise ValueError("out must have x's shape")
     nbytes = ln_forward_workspace_size(outer, inner)
-    ws = _ln_workspace(dev, nbytes, variant) if workspace is None else workspace
-    _check(lib().ln_forward(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, float(eps), _ptr(ws),
+    ws = _ln_workspace(dev, nbytes) if workspace is None else workspace
+    _invoke("ln_forward", _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, float(eps), _ptr(ws),
                             ws.numel() * ws.element_size(), _ptr(mean_out), _ptr(rstd_out), int(variant),
-                            _stream(dev)))
+                            _stream(dev))
     return y
 
 
@@ -180,9 +215,9 @@ def ln_forward_stats(x, eps=1e-5, normalized_ndim=None, workspace=None, mean_out
     outer, inner = _ln_shape(x, normalized_ndim)
     _opt(mean_out, "mean_out", outer, dev)
     _opt(rstd_out, "rstd_out", outer, dev)
-    ws = _ln_workspace(dev, ln_forward_workspace_size(outer, inner), 0) if workspace is None else workspace
-    _check(lib().ln_forward_stats(_ptr(x), outer, inner, float(eps), _ptr(ws), ws.numel() * ws.element_size(),
-                                  _ptr(mean_out), _ptr(rstd_out), _stream(dev)))
+    ws = _ln_workspace(dev, ln_forward_workspace_size(outer, inner)) if workspace is None else workspace
+    _invoke("ln_forward_stats", _ptr(x), outer, inner, float(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _ptr(mean_out), _ptr(rstd_out), _stream(dev))
     return ws
 
 
@@ -195,8 +230,8 @@ def ln_forward_apply(x, weight, bias, workspace, normalized_ndim=None, out=None)
     _opt(bias, "bias", inner, dev)
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", dev)
-    _check(lib().ln_forward_apply(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(dev)))
+    _invoke("ln_forward_apply", _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev))
     return y
 
 
@@ -213,8 +248,8 @@ def gn_lrelu_x2_forward(x, gamma, beta, num_groups, eps=1e-5, negative_slope=0.0
     _opt(beta, "beta", C, dev)
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", dev)
-    _check(lib().gn_lrelu_x2_forward(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), N, C, int(num_groups),
-                                     float(eps), float(negative_slope), _stream(dev)))
+    _invoke("gn_lrelu_x2_forward", _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), N, C, int(num_groups),
+                                     float(eps), float(negative_slope), _stream(dev))
     return y
 
 
@@ -229,7 +264,7 @@ def rmsnorm_ch_forward(x, eps=1e-5, out=None):
     S = x.numel() // (B * C) if B * C else 0
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", x.device)
-    _check(lib().rmsnorm_ch_forward(_ptr(x), _ptr(y), B, C, S, float(eps), _stream(x.device)))
+    _invoke("rmsnorm_ch_forward", _ptr(x), _ptr(y), B, C, S, float(eps), _stream(x.device))
     return y
 
 
@@ -259,7 +294,7 @@ def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.0
             hit = alloc_workspace(nbytes, dev)
             _FC_WS[dev] = hit
         workspace = hit[1]
-    _check(lib().fc_gn_forward(_ptr(x), _ptr(W), _ptr(b), _ptr(gamma), _ptr(beta), _ptr(y), N, K, C,
+    _invoke("fc_gn_forward", _ptr(x), _ptr(W), _ptr(b), _ptr(gamma), _ptr(beta), _ptr(y), N, K, C,
                                int(num_groups), float(eps), float(negative_slope), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(dev)))
+                               workspace.numel() * workspace.element_size(), _stream(dev))
     return y

@@ -28,6 +28,13 @@
 #ifndef NORMFWD_GN_ITEMS
 #define NORMFWD_GN_ITEMS 8
 #endif
+// Streaming (nontemporal) hints on the x loads and y stores.
+#ifndef NORMFWD_GN_NT_LOAD
+#define NORMFWD_GN_NT_LOAD 1
+#endif
+#ifndef NORMFWD_GN_NT_STORE
+#define NORMFWD_GN_NT_STORE 1
+#endif
 
 namespace normfwd {
 
@@ -57,7 +64,7 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const int64_t c4 = c4_0 + i * kWave;
-        v[i] = c4 < C4 ? ld_nt(xr + c4) : f4(0.0f);
+        v[i] = c4 < C4 ? (NORMFWD_GN_NT_LOAD ? ld_nt(xr + c4) : xr[c4]) : f4(0.0f);
     }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
@@ -75,7 +82,10 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
             o.y = lrelu_x2(z.y, slope);
             o.z = lrelu_x2(z.z, slope);
             o.w = lrelu_x2(z.w, slope);
-            st_nt(o, yr + c4);
+            if (NORMFWD_GN_NT_STORE)
+                st_nt(o, yr + c4);
+            else
+                yr[c4] = o;
         }
     }
 }
@@ -157,7 +167,7 @@ static hipError_t launch_fast_items(const float* x, const float* gamma, const fl
 {
     // A wave's tile never needs to be longer than the row.
     constexpr int items = NORMFWD_GN_ITEMS;
-    if (C / 4 <= 1 * kWave) return launch_fast<L, 1>(x, gamma, beta, y, N, C, M, eps, slope, st);
+    if (C / 4 <= 1 * kWave || items <= 1) return launch_fast<L, 1>(x, gamma, beta, y, N, C, M, eps, slope, st);
     if (C / 4 <= 2 * kWave || items <= 2) return launch_fast<L, 2>(x, gamma, beta, y, N, C, M, eps, slope, st);
     if (C / 4 <= 4 * kWave || items <= 4) return launch_fast<L, 4>(x, gamma, beta, y, N, C, M, eps, slope, st);
     if (C / 4 <= 8 * kWave || items <= 8) return launch_fast<L, 8>(x, gamma, beta, y, N, C, M, eps, slope, st);

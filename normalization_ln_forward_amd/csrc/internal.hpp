@@ -15,11 +15,10 @@ hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* b
 
 // LayerNorm workspace: byte offsets of each region (all 256-byte aligned).
 struct LnLayout {
-    int64_t P;        // chunks per sample, split variant
-    int64_t chunk;    // elements per chunk, split variant (multiple of 4)
+    int64_t P;        // partial-moment workgroups per sample, split variant
     int64_t P_cap;    // partial-moment slots per sample (>= chunks of either variant)
     size_t off_ctrl;  // control block: generation, completion counter, error word
-    size_t off_counter;
+    size_t off_counter;  // single kernel: ring of arrival counters
     size_t off_flag;
     size_t off_stats;
     size_t off_part;

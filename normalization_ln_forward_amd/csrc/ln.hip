@@ -22,7 +22,8 @@
 //     (x - hi) - lo keeps ~48 bits of the mean.
 //
 // Two schedules of the same arithmetic:
-//   split  (variant 0): ln_partial_kernel -> ln_merge_kernel -> ln_normalize_kernel.
+//   split  (variant 0): ln_partial_kernel -> ln_merge_kernel ->
+//          ln_normalize_rows_kernel (or ln_normalize_kernel).
 //   single (variant 1): one cooperative launch, one workgroup per chunk
 //          index p; the last workgroup to deliver a sample's partial merges
 //          it and publishes the statistics with an agent-scope release (LN
@@ -52,22 +53,60 @@ struct LnCtrl {
 static_assert(sizeof(LnCtrl) == 256, "control block is 256 bytes");
 
 constexpr int kLnThreads = 256;
-constexpr int kLnUnroll = 4;
+// The single kernel's arrival counters: a ring of kRing, each on its own
+// 128-byte line (atomics that meet on one line serialize).
+constexpr int kCounterStride = 32;  // uint32 words
+constexpr int kRing = 4;
 constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Split schedule tuning: elements per partial-moment workgroup, rows in
+// flight per thread in the moments pass, XCD-aware row order in the
+// normalize pass.
+#ifndef NORMFWD_LN_SPLIT_CHUNK
+#define NORMFWD_LN_SPLIT_CHUNK 16384
+#endif
+#ifndef NORMFWD_LN_PARTIAL_UNROLL
+#define NORMFWD_LN_PARTIAL_UNROLL 4
+#endif
+#ifndef NORMFWD_LN_PARTIAL_NT
+#define NORMFWD_LN_PARTIAL_NT 0
+#endif
+#ifndef NORMFWD_LN_NORM_ROWS
+#define NORMFWD_LN_NORM_ROWS 1
+#endif
+#ifndef NORMFWD_LN_NORM_NT_STORE
+#define NORMFWD_LN_NORM_NT_STORE 1
+#endif
+// Normalize pass: 1 = sample loop (ln_normalize_rows_kernel), 0 = one row
+// per workgroup in XCD order (ln_normalize_kernel); samples in flight per
+// thread in the sample loop.
+#ifndef NORMFWD_LN_NORM_MODE
+#define NORMFWD_LN_NORM_MODE 1
+#endif
+#ifndef NORMFWD_LN_NORM_SAMPLE_UNROLL
+#define NORMFWD_LN_NORM_SAMPLE_UNROLL 2
+#endif
+#ifndef NORMFWD_LN_XCD_MAP
+#define NORMFWD_LN_XCD_MAP 1
+#endif
+
+
+// uint32 words of the single kernel's arrival-counter ring (4 slots x 128
+// bytes).
+constexpr size_t kLnCounterWords = 4 * 32;
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 LnLayout ln_layout(int64_t outer, int64_t inner)
 {
     LnLayout L{};
-    L.P = std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(inner, 16384)));
-    L.chunk = ceil_div(ceil_div(inner, L.P), 4) * 4;
+    L.P = std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(inner, NORMFWD_LN_SPLIT_CHUNK)));
     L.P_cap = std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(inner, 1024)));
     size_t off = 0;
     L.off_ctrl = off;
     off += sizeof(LnCtrl);
     L.off_counter = off;
-    off += align256(4 * (size_t)outer);
+    off += align256(4 * (size_t)kLnCounterWords);
     L.off_flag = off;
     off += align256(4 * (size_t)outer);
     L.off_stats = off;
@@ -96,37 +135,11 @@ __device__ __forceinline__ void chan_merge(double& n, double& m, double& m2, dou
     n = nn;
 }
 
-// Sum and sum of squares of (x - K) over xs[0, n), reduced over the
-// workgroup; the result is valid in thread 0.  red: LDS of 2*(NT/64) doubles.
-template <int VEC>
-__device__ __forceinline__ void chunk_moments(const float* xs, int64_t n, float K, double* red, double& s1,
-                                              double& s2)
+// Workgroup-wide sums of the lane accumulators a1 (sum of d) and a2 (sum of
+// d^2), widened to fp64, in a fixed order; the result is valid in thread 0.
+// red: LDS of 2*(NT/64) doubles.
+__device__ __forceinline__ void block_moments(f4 a1, f4 a2, double* red, double& s1, double& s2)
 {
-    f4 a1 = f4(0.0f), a2 = f4(0.0f);
-    if constexpr (VEC == 4) {
-        const f4* x4 = reinterpret_cast<const f4*>(xs);
-        const int64_t nv = n / 4;
-        for (int64_t i = threadIdx.x; i < nv; i += kLnThreads * kLnUnroll) {
-            f4 v[kLnUnroll];
-#pragma unroll
-            for (int u = 0; u < kLnUnroll; ++u) {
-                const int64_t j = i + (int64_t)u * kLnThreads;
-                v[u] = j < nv ? x4[j] : f4(K);
-            }
-#pragma unroll
-            for (int u = 0; u < kLnUnroll; ++u) {
-                const f4 d = v[u] - K;
-                a1 += d;
-                a2 += d * d;
-            }
-        }
-    } else {
-        for (int64_t i = threadIdx.x; i < n; i += kLnThreads) {
-            const float d = xs[i] - K;
-            a1.x += d;
-            a2.x += d * d;
-        }
-    }
     double t1 = ((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w);
     double t2 = ((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w);
     t1 = wave_sum(t1);
@@ -160,16 +173,64 @@ __device__ __forceinline__ Partial make_partial(int64_t n, float K, double s1, d
     return p;
 }
 
-// Merge parts[0, P) in a fixed order (thread t folds t, t+NT, ... then a
-// fixed tree over threads); writes (mean hi, mean lo, rstd) for the sample.
-// lds: 3*NT doubles.
-__device__ void merge_and_publish(const Partial* parts, int64_t P, float eps, double* lds, f4* stats_b,
-                                  float* mean_out_b, float* rstd_out_b)
+// Cross-workgroup protocol.  The 8 XCDs have their own L2s, which are not
+// coherent with each other for ordinary accesses; agent-scope release and
+// acquire fences make them coherent by writing back / invalidating the
+// whole L2 (buffer_wbl2 / buffer_inv), which measured ~100 us over one
+// LayerNorm launch.  The protocol below avoids them: every location that
+// crosses workgroups (partial moments, statistics, counters, flags) is only
+// ever accessed with agent-scope atomic loads and stores, which the gfx950
+// code generator issues as device-coherent accesses (sc1) served at the
+// device's coherence point, and a writer waits for its data stores to
+// complete (s_waitcnt vmcnt(0)) before it stores the counter or flag that
+// announces them.  A reader issues its data loads only after it has seen
+// that counter or flag value, so it reads the announced data.
+//
+// Arrival counters live in a ring of kRing slots (sample t uses slot t %
+// kRing), each on its own 128-byte line.  Reuse is safe: the merger of
+// sample t resets the slot before it announces flag[t], and no workgroup
+// arrives at sample t + 2 before it has seen flag[t].
+
+// Wait until this thread's earlier vector-memory accesses have completed.
+__device__ __forceinline__ void vmem_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <typename T>
+__device__ __forceinline__ void dev_store(T* p, T v)
 {
-    double n = 0.0, m = 0.0, m2 = 0.0;
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T dev_load(const T* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish this workgroup's partial and count its arrival on `counter`
+// (thread 0 only); true for the last of the P arrivals.
+__device__ __forceinline__ bool deliver_partial(Partial* part, const Partial& v, uint32_t* counter, int64_t P)
+{
+    dev_store(&part->n, v.n);
+    dev_store(&part->mean, v.mean);
+    dev_store(&part->m2, v.m2);
+    vmem_drain();
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1);
+}
+
+// Merge parts[0, P) in a fixed order: thread t folds partials t, t + 256,
+// ..., then a fixed tree over the threads.  The result is valid in thread 0.
+// Coherent: read the partials with device-coherent loads (they were written
+// by other workgroups of the same launch).  lds: 3 * 256 doubles.
+template <bool Coherent>
+__device__ void merge_partials(const Partial* parts, int64_t P, double* lds, double& n, double& m, double& m2)
+{
+    n = 0.0;
+    m = 0.0;
+    m2 = 0.0;
     for (int64_t j = threadIdx.x; j < P; j += kLnThreads) {
-        const Partial q = parts[j];
-        chan_merge(n, m, m2, q.n, q.mean, q.m2);
+        if constexpr (Coherent)
+            chan_merge(n, m, m2, dev_load(&parts[j].n), dev_load(&parts[j].mean), dev_load(&parts[j].m2));
+        else
+            chan_merge(n, m, m2, parts[j].n, parts[j].mean, parts[j].m2);
     }
     double* ln_ = lds;
     double* lm = lds + kLnThreads;
@@ -188,97 +249,124 @@ __device__ void merge_and_publish(const Partial* parts, int64_t P, float eps, do
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        const double var = n > 0.0 ? m2 / n : 0.0;
-        const double rstd = 1.0 / sqrt(var + (double)eps);
-        const float hi = (float)m;
-        const float lo = (float)(m - (double)hi);
-        *stats_b = f4{hi, lo, (float)rstd, 0.0f};
-        if (mean_out_b) *mean_out_b = hi;
-        if (rstd_out_b) *rstd_out_b = (float)rstd;
-    }
 }
 
-// y = (((x - hi) - lo) * rstd) * w + b over xs/ys[0, n); w/b already
-// offset to the same position in the sample.
-template <int VEC>
-__device__ __forceinline__ void normalize_range(const float* xs, const float* ws, const float* bs, float* ys,
-                                                int64_t n, f4 st)
+// (mean hi, mean lo, rstd) of a merged sample.
+__device__ __forceinline__ f4 finish_stats(double n, double m, double m2, float eps)
 {
-    const float hi = st.x, lo = st.y, rs = st.z;
-    if constexpr (VEC == 4) {
-        const f4* x4 = reinterpret_cast<const f4*>(xs);
-        const f4* w4 = reinterpret_cast<const f4*>(ws);
-        const f4* b4 = reinterpret_cast<const f4*>(bs);
-        f4* y4 = reinterpret_cast<f4*>(ys);
-        const int64_t nv = n / 4;
-        for (int64_t i = threadIdx.x; i < nv; i += kLnThreads * kLnUnroll) {
-            f4 v[kLnUnroll], wv[kLnUnroll], bv[kLnUnroll];
-#pragma unroll
-            for (int u = 0; u < kLnUnroll; ++u) {
-                const int64_t j = i + (int64_t)u * kLnThreads;
-                if (j < nv) {
-                    v[u] = ld_nt(x4 + j);
-                    wv[u] = ws ? w4[j] : f4(1.0f);
-                    bv[u] = bs ? b4[j] : f4(0.0f);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kLnUnroll; ++u) {
-                const int64_t j = i + (int64_t)u * kLnThreads;
-                if (j < nv) {
-                    const f4 t = ((v[u] - hi) - lo) * rs;
-                    st_nt(t * wv[u] + bv[u], y4 + j);
-                }
-            }
-        }
-    } else {
-        for (int64_t i = threadIdx.x; i < n; i += kLnThreads) {
-            const float t = ((xs[i] - hi) - lo) * rs;
-            const float wv = ws ? ws[i] : 1.0f;
-            const float bv = bs ? bs[i] : 0.0f;
-            ys[i] = t * wv + bv;
-        }
-    }
+    const double var = n > 0.0 ? m2 / n : 0.0;
+    const double rstd = 1.0 / sqrt(var + (double)eps);
+    const float hi = (float)m;
+    const float lo = (float)(m - (double)hi);
+    return f4{hi, lo, (float)rstd, 0.0f};
 }
 
 // ---------------------------------------------------------------- split variant
 
 template <int VEC>
-__global__ void __launch_bounds__(kLnThreads)
-ln_partial_kernel(const float* x, int64_t inner, int64_t chunk, int64_t P, int64_t P_cap, Partial* parts)
+struct LnVec;
+template <>
+struct LnVec<4> {
+    using T = f4;
+};
+template <>
+struct LnVec<1> {
+    using T = float;
+};
+
+// Measured on MI355X: HBM streams fastest when the loads in flight at any
+// moment cover one dense address range (few KiB per workgroup, neighbouring
+// workgroups on neighbouring addresses); a workgroup that walks its own
+// 64 KiB run leaves the in-flight set scattered 64 KiB apart and loses ~20%.
+// So a sample is cut into rows of 256 units (a unit is one float4, or one
+// float on the scalar path), and the P workgroups of a sample take the rows
+// round-robin: workgroup p owns rows p, p + P, p + 2P, ...  At any moment
+// the P workgroups read P adjacent rows.  Any partition of the sample works
+// for the moment merge; this one only changes which elements a partial holds.
+__device__ __forceinline__ int64_t rows_owned_units(int64_t nu, int64_t p, int64_t P)
 {
+    const int64_t nrows = ceil_div(nu, (int64_t)kLnThreads);
+    if (p >= nrows) return 0;
+    const int64_t c = (nrows - 1 - p) / P + 1;
+    const int64_t last = nrows - 1;
+    const int64_t last_units = nu - last * kLnThreads;
+    const bool owns_last = (last - p) % P == 0;
+    return owns_last ? (c - 1) * kLnThreads + last_units : c * kLnThreads;
+}
+
+// Moments of workgroup p's rows of sample b, stored as the sample's p-th
+// partial (n, mean, M2).
+template <int VEC>
+__global__ void __launch_bounds__(kLnThreads)
+ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Partial* parts)
+{
+    using V = typename LnVec<VEC>::T;
+    constexpr int U = NORMFWD_LN_PARTIAL_UNROLL;
     __shared__ double red[2 * kLnThreads / kWave];
     const int64_t b = blockIdx.x / P;
     const int64_t p = blockIdx.x - b * P;
-    const int64_t start = p * chunk;
-    const int64_t n = std::max<int64_t>(0, std::min<int64_t>(inner, start + chunk) - start);
     const float* xb = x + b * inner;
+    const V* xv = reinterpret_cast<const V*>(xb);
+    const int64_t nu = inner / VEC;
+    const int64_t nrows = ceil_div(nu, (int64_t)kLnThreads);
     const float K = xb[0];
+    V a1 = V(0.0f), a2 = V(0.0f);
+    for (int64_t r = p; r < nrows; r += P * U) {
+        V v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = (r + (int64_t)u * P) * kLnThreads + threadIdx.x;
+            v[u] = j < nu ? (NORMFWD_LN_PARTIAL_NT ? ld_nt(xv + j) : xv[j]) : V(K);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const V d = v[u] - K;
+            a1 += d;
+            a2 += d * d;
+        }
+    }
+    f4 a1f, a2f;
+    if constexpr (VEC == 4) {
+        a1f = a1;
+        a2f = a2;
+    } else {
+        a1f = f4{a1, 0.0f, 0.0f, 0.0f};
+        a2f = f4{a2, 0.0f, 0.0f, 0.0f};
+    }
     double s1 = 0.0, s2 = 0.0;
-    chunk_moments<VEC>(xb + start, n, K, red, s1, s2);
-    if (threadIdx.x == 0) parts[b * P_cap + p] = make_partial(n, K, s1, s2);
+    block_moments(a1f, a2f, red, s1, s2);
+    if (threadIdx.x == 0) parts[b * P_cap + p] = make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2);
 }
 
+// One workgroup per sample: merge its P partials in partial order into
+// (mean hi, mean lo, rstd).
 __global__ void __launch_bounds__(kLnThreads)
 ln_merge_kernel(const Partial* parts, int64_t P, int64_t P_cap, float eps, f4* stats, float* mean_out,
                 float* rstd_out)
 {
     __shared__ double lds[3 * kLnThreads];
     const int64_t b = blockIdx.x;
-    merge_and_publish(parts + b * P_cap, P, eps, lds, stats + b, mean_out ? mean_out + b : nullptr,
-                      rstd_out ? rstd_out + b : nullptr);
+    double n, m, m2;
+    merge_partials<false>(parts + b * P_cap, P, lds, n, m, m2);
+    if (threadIdx.x == 0) {
+        const f4 st = finish_stats(n, m, m2, eps);
+        stats[b] = st;
+        if (mean_out) mean_out[b] = st.x;
+        if (rstd_out) rstd_out[b] = st.z;
+    }
 }
 
-// Blocks are mapped so that the blocks one XCD runs back to back share the
-// same chunk q of weight/bias across samples (workgroups go to the 8 XCDs
-// round-robin by index): the XCD fetches that chunk of w/b into its L2 once
-// and reuses it for every sample.
+// One row of 256 units per workgroup.  With xcd_map the workgroups one XCD
+// runs back to back (workgroups go to the 8 XCDs round-robin by index) take
+// the same row of every sample in turn, so that XCD's L2 fetches the row of
+// weight/bias once and serves it to all samples.
 template <int VEC>
 __global__ void __launch_bounds__(kLnThreads)
 ln_normalize_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
-                    int64_t Q, int64_t cq, int xcd_map, const f4* stats)
+                    int64_t bps, int xcd_map, const f4* stats)
 {
+    using V = typename LnVec<VEC>::T;
+    constexpr int R = NORMFWD_LN_NORM_ROWS;
     int64_t b, q;
     const int64_t i = blockIdx.x;
     if (xcd_map) {
@@ -286,86 +374,228 @@ ln_normalize_kernel(const float* x, const float* w, const float* bias, float* y,
         b = r % outer;
         q = (r / outer) * 8 + xcd;
     } else {
-        b = i / Q;
-        q = i - b * Q;
+        b = i / bps;
+        q = i - b * bps;
     }
-    const int64_t start = q * cq;
-    const int64_t n = std::max<int64_t>(0, std::min<int64_t>(inner, start + cq) - start);
+    const int64_t nu = inner / VEC;
     const f4 st = stats[b];
-    const int64_t o = b * inner + start;
-    normalize_range<VEC>(x + o, w ? w + start : nullptr, bias ? bias + start : nullptr, y + o, n, st);
+    const V* xv = reinterpret_cast<const V*>(x + b * inner);
+    V* yv = reinterpret_cast<V*>(y + b * inner);
+    V xr[R], wr[R], br[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t j = (q * R + r) * kLnThreads + threadIdx.x;
+        if (j < nu) {
+            xr[r] = ld_nt(xv + j);
+            wr[r] = w ? reinterpret_cast<const V*>(w)[j] : V(1.0f);
+            br[r] = bias ? reinterpret_cast<const V*>(bias)[j] : V(0.0f);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t j = (q * R + r) * kLnThreads + threadIdx.x;
+        if (j < nu) {
+            const V o = ((xr[r] - st.x) - st.y) * st.z * wr[r] + br[r];
+            if (NORMFWD_LN_NORM_NT_STORE)
+                st_nt(o, yv + j);
+            else
+                yv[j] = o;
+        }
+    }
+}
+
+// Sample-loop order: workgroup q owns row q of every sample; it loads its
+// row of weight/bias once and streams the samples through it, so weight and
+// bias cross HBM exactly once without relying on L2, and at any moment the
+// workgroups in flight cover one dense run of rows per sample.  (Measured:
+// 84 us inside the LN step against 92 us for the XCD-ordered one-row
+// kernel; part of the second read of x is served by the 256 MB MALL, which
+// is why the moments pass keeps ordinary, not streaming, loads.)
+template <int VEC>
+__global__ void __launch_bounds__(kLnThreads)
+ln_normalize_rows_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
+                         const f4* stats)
+{
+    using V = typename LnVec<VEC>::T;
+    constexpr int U = NORMFWD_LN_NORM_SAMPLE_UNROLL;
+    const int64_t nu = inner / VEC;
+    const int64_t j = (int64_t)blockIdx.x * kLnThreads + threadIdx.x;
+    if (j >= nu) return;
+    const V wv = w ? reinterpret_cast<const V*>(w)[j] : V(1.0f);
+    const V bv = bias ? reinterpret_cast<const V*>(bias)[j] : V(0.0f);
+    for (int64_t t0 = 0; t0 < outer; t0 += U) {
+        V xr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = t0 + u;
+            if (b < outer) xr[u] = ld_nt(reinterpret_cast<const V*>(x + b * inner) + j);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t b = t0 + u;
+            if (b < outer) {
+                const f4 st = stats[b];
+                const V o = ((xr[u] - st.x) - st.y) * st.z * wv + bv;
+                V* dst = reinterpret_cast<V*>(y + b * inner) + j;
+                if (NORMFWD_LN_NORM_NT_STORE)
+                    st_nt(o, dst);
+                else
+                    *dst = o;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- single-kernel variant
 
-template <int VEC>
-__global__ void __launch_bounds__(kLnThreads)
-ln_single_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
-                 int64_t chunk, int64_t P_cap, float eps, LnCtrl* ctrl, uint32_t* counter, uint32_t* flag,
-                 f4* stats, Partial* parts, float* mean_out, float* rstd_out)
+// Last arriver of sample t in the single kernel: merge its partials, store
+// the statistics, reset the sample's counter and announce flag[t] = target.
+__device__ void merge_and_announce(const Partial* parts, int64_t P, float eps, double* lds, f4* stats_t,
+                                   float* mean_out_t, float* rstd_out_t, uint32_t* counter, uint32_t* flag,
+                                   int64_t t, uint32_t target)
 {
+    double n, m, m2;
+    merge_partials<true>(parts, P, lds, n, m, m2);
+    if (threadIdx.x == 0) {
+        const f4 st = finish_stats(n, m, m2, eps);
+        float* sp = reinterpret_cast<float*>(stats_t);
+        dev_store(sp + 0, st.x);
+        dev_store(sp + 1, st.y);
+        dev_store(sp + 2, st.z);
+        if (mean_out_t) *mean_out_t = st.x;
+        if (rstd_out_t) *rstd_out_t = st.z;
+        dev_store(counter, 0u);
+        vmem_drain();
+        dev_store(&flag[t], target);
+    }
+}
+
+// Wait for flag[t] == target and return sample t's statistics (thread 0
+// only).  A spin limit turns a wait that cannot end into an error flag
+// instead of a hang.
+__device__ __forceinline__ f4 await_stats(const uint32_t* flag, const f4* stats, int64_t t, uint32_t target,
+                                          LnCtrl* ctrl)
+{
+    uint32_t it = 0;
+    while (dev_load(&flag[t]) != target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++it > kSpinLimit) {
+            dev_store(&ctrl->error, 1u);
+            break;
+        }
+    }
+    const float* sp = reinterpret_cast<const float*>(stats + t);
+    return f4{dev_load(sp + 0), dev_load(sp + 1), dev_load(sp + 2), 0.0f};
+}
+
+// Single-read schedule (one cooperative launch; LN page, turn 6 proposes
+// finishing the reduction in the last block to arrive).  Workgroup p owns
+// rows p, p + P, p + 2P, ... of 256 float4 in every sample (the interleaved
+// order that keeps the loads in flight dense), keeps its rows of x in VGPRs
+// (F4PT float4 per thread) from the moments pass to the normalize pass, so
+// x crosses HBM once, and keeps its rows of weight and bias in LDS for all
+// samples.  The pipeline runs one sample behind: iteration t delivers the
+// moments of sample t, issues the loads of sample t+1, then waits for the
+// statistics of sample t-1 (announced one iteration earlier, so normally
+// already there) and normalizes it.  Three register tiles are live.
+template <int F4PT>
+__global__ void __launch_bounds__(kLnThreads)
+ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
+                      int64_t P_cap, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats,
+                      Partial* parts, float* mean_out, float* rstd_out)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     __shared__ double lds[3 * kLnThreads];
     __shared__ int s_last;
+    __shared__ f4 s_stats;
+    f4* w_s = reinterpret_cast<f4*>(smem_raw);
+    f4* b_s = w_s + (w ? F4PT * kLnThreads : 0);
     const int64_t P = gridDim.x;
     const int64_t p = blockIdx.x;
-    const int64_t start = p * chunk;
-    const int64_t n = std::max<int64_t>(0, std::min<int64_t>(inner, start + chunk) - start);
-    const uint32_t target = __hip_atomic_load(&ctrl->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const int tid = threadIdx.x;
+    const int64_t nv = inner / 4;
+    const int64_t rows = ceil_div(nv, (int64_t)kLnThreads);
+    const uint32_t target = dev_load(&ctrl->gen) + 1u;
+
+    auto index = [&](int k) -> int64_t { return (p + (int64_t)k * P) * kLnThreads + tid; };
+    auto valid = [&](int k) -> bool { return p + (int64_t)k * P < rows && index(k) < nv; };
+
+    // weight / bias rows -> LDS: all loads in flight first, then the LDS stores
+    f4 prev[F4PT], cur[F4PT], nxt[F4PT];
+    for (int which = 0; which < 2; ++which) {
+        const float* src = which == 0 ? w : bias;
+        f4* dst = which == 0 ? w_s : b_s;
+        if (!src) continue;
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) nxt[k] = valid(k) ? reinterpret_cast<const f4*>(src)[index(k)] : f4(0.0f);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) dst[k * kLnThreads + tid] = nxt[k];
+    }
+    {
+        const f4* x4 = reinterpret_cast<const f4*>(x);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) {
+            cur[k] = valid(k) ? x4[index(k)] : f4(0.0f);
+            prev[k] = nxt[k] = f4(0.0f);
+        }
+    }
+    const int64_t n_mine = rows_owned_units(nv, p, P) * 4;
+    __syncthreads();
 
     for (int64_t t = 0; t <= outer; ++t) {
         if (t < outer) {
-            // phase 1: moments of chunk p of sample t
-            const float* xb = x + t * inner;
-            const float K = xb[0];
-            double s1 = 0.0, s2 = 0.0;
-            chunk_moments<VEC>(xb + start, n, K, lds, s1, s2);
-            if (threadIdx.x == 0) {
-                parts[t * P_cap + p] = make_partial(n, K, s1, s2);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                const uint32_t old =
-                    __hip_atomic_fetch_add(&counter[t], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-                s_last = (old == (uint32_t)(P - 1));
+            const float K = x[t * inner];
+            f4 a1 = f4(0.0f), a2 = f4(0.0f);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) {
+                const f4 d = valid(k) ? cur[k] - K : f4(0.0f);
+                a1 += d;
+                a2 += d * d;
             }
+            double s1 = 0.0, s2 = 0.0;
+            block_moments(a1, a2, lds, s1, s2);
+            uint32_t* counter = counters + (t % kRing) * kCounterStride;
+            if (tid == 0) s_last = deliver_partial(parts + t * P_cap + p, make_partial(n_mine, K, s1, s2), counter, P);
             __syncthreads();
-            if (s_last) {
-                // every partial of sample t has been released: merge in chunk order
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                merge_and_publish(parts + t * P_cap, P, eps, lds, stats + t, mean_out ? mean_out + t : nullptr,
-                                  rstd_out ? rstd_out + t : nullptr);
-                if (threadIdx.x == 0) {
-                    __hip_atomic_store(&counter[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                    __hip_atomic_store(&flag[t], target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                }
+            if (s_last)
+                merge_and_announce(parts + t * P_cap, P, eps, lds, stats + t, mean_out ? mean_out + t : nullptr,
+                                   rstd_out ? rstd_out + t : nullptr, counter, flag, t, target);
+            if (t + 1 < outer) {
+                const f4* x4 = reinterpret_cast<const f4*>(x + (t + 1) * inner);
+#pragma unroll
+                for (int k = 0; k < F4PT; ++k) nxt[k] = valid(k) ? x4[index(k)] : f4(0.0f);
             }
         }
         if (t >= 1) {
-            // phase 2: normalize chunk p of sample t-1 once its statistics are published
             const int64_t s = t - 1;
-            if (threadIdx.x == 0) {
-                uint32_t it = 0;
-                while (__hip_atomic_load(&flag[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != target) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++it > kSpinLimit) {
-                        __hip_atomic_store(&ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
+            if (tid == 0) s_stats = await_stats(flag, stats, s, target, ctrl);
+            __syncthreads();
+            const f4 st = s_stats;
+            f4* y4 = reinterpret_cast<f4*>(y + s * inner);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) {
+                if (valid(k)) {
+                    const f4 tt = ((prev[k] - st.x) - st.y) * st.z;
+                    const f4 wv = w ? w_s[k * kLnThreads + tid] : f4(1.0f);
+                    const f4 bv = bias ? b_s[k * kLnThreads + tid] : f4(0.0f);
+                    st_nt(tt * wv + bv, y4 + index(k));
                 }
             }
-            __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            const f4 st = stats[s];
-            const int64_t o = s * inner + start;
-            normalize_range<VEC>(x + o, w ? w + start : nullptr, bias ? bias + start : nullptr, y + o, n, st);
+        }
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) {
+            prev[k] = cur[k];
+            cur[k] = nxt[k];
         }
     }
     // completion: the last workgroup out resets the counter and advances the generation
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (uint32_t)(P - 1)) {
-            __hip_atomic_store(&ctrl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctrl->gen, target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        vmem_drain();
+        if (__hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1)) {
+            dev_store(&ctrl->done, 0u);
+            vmem_drain();
+            dev_store(&ctrl->gen, target);
         }
     }
 }
@@ -397,11 +627,9 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x);
     const dim3 grid((unsigned)(outer * lay.P));
     if (vec4)
-        hipLaunchKernelGGL(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.chunk, lay.P,
-                           lay.P_cap, parts);
+        hipLaunchKernelGGL(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts);
     else
-        hipLaunchKernelGGL(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.chunk, lay.P,
-                           lay.P_cap, parts);
+        hipLaunchKernelGGL(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ln_merge_kernel, dim3((unsigned)outer), dim3(kLnThreads), 0, st, parts, lay.P, lay.P_cap,
@@ -414,43 +642,117 @@ hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float
 {
     const f4* stats = reinterpret_cast<const f4*>(static_cast<const char*>(ws) + lay.off_stats);
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
-    // Q blocks per sample, each over a contiguous range of cq elements (a
-    // multiple of 4); Q is a multiple of 8 when the XCD mapping is used.
-    int64_t Q = std::max<int64_t>(1, ceil_div(inner, 16384));
+    const int64_t nu = vec4 ? inner / 4 : inner;
+    int64_t bps = ceil_div(nu, (int64_t)kLnThreads * NORMFWD_LN_NORM_ROWS);
+    // The XCD mapping needs a multiple of 8 rows per sample and pays off
+    // only when weight/bias are read for several samples.
     int xcd_map = 0;
-    if (Q >= 8) {
-        Q = ceil_div(Q, 8) * 8;
+    if (NORMFWD_LN_XCD_MAP && outer > 1 && bps >= 8 && (w || b)) {
+        bps = ceil_div(bps, 8) * 8;
         xcd_map = 1;
     }
-    const int64_t cq = ceil_div(ceil_div(inner, Q), 4) * 4;
-    const dim3 grid((unsigned)(outer * Q));
+    if (NORMFWD_LN_NORM_MODE == 1) {
+        const dim3 g((unsigned)ceil_div(nu, (int64_t)kLnThreads));
+        if (vec4)
+            hipLaunchKernelGGL(ln_normalize_rows_kernel<4>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
+        else
+            hipLaunchKernelGGL(ln_normalize_rows_kernel<1>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)(outer * bps));
     if (vec4)
-        hipLaunchKernelGGL(ln_normalize_kernel<4>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, Q, cq,
+        hipLaunchKernelGGL(ln_normalize_kernel<4>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
                            xcd_map, stats);
     else
-        hipLaunchKernelGGL(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, Q, cq,
+        hipLaunchKernelGGL(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
                            xcd_map, stats);
     return hipGetLastError();
 }
 
-// Co-resident workgroups of ln_single_kernel per device (queried once).
-static int single_capacity(bool vec4)
+struct DeviceInfo {
+    int cus = 0;
+    int max_lds_per_block = 0;
+};
+
+static bool device_info(DeviceInfo& out)
 {
     static std::mutex mu;
-    static int cap[2][64] = {};
+    static DeviceInfo info[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
     std::lock_guard<std::mutex> lock(mu);
-    int& c = cap[vec4 ? 1 : 0][dev];
-    if (c == 0) {
-        int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        const void* fn = vec4 ? reinterpret_cast<const void*>(&ln_single_kernel<4>)
-                              : reinterpret_cast<const void*>(&ln_single_kernel<1>);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kLnThreads, 0) != hipSuccess) return 0;
-        c = cus * per_cu;
+    DeviceInfo& d = info[dev];
+    if (d.cus == 0) {
+        if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+        if (hipDeviceGetAttribute(&d.max_lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+            return false;
     }
-    return c;
+    out = d;
+    return true;
+}
+
+// Co-resident workgroups of `fn` with `lds` bytes of dynamic LDS on this
+// device (queried once per device, kernel and LDS size).
+static int coresident(const void* fn, size_t lds)
+{
+    struct Entry {
+        int dev;
+        const void* fn;
+        size_t lds;
+        int cap;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int n_cache = 0;
+    DeviceInfo d;
+    if (!device_info(d)) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i)
+        if (cache[i].dev == dev && cache[i].fn == fn && cache[i].lds == lds) return cache[i].cap;
+    int cap = 0;
+    if (lds == 0 || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kLnThreads, lds) == hipSuccess)
+            cap = d.cus * per_cu;
+    }
+    (void)hipGetLastError();
+    if (n_cache < 64) cache[n_cache++] = Entry{dev, fn, lds, cap};
+    return cap;
+}
+
+#ifndef NORMFWD_LN_HOLD_F4PT
+#define NORMFWD_LN_HOLD_F4PT 16
+#endif
+
+template <int F4PT>
+static bool try_launch_hold(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner,
+                            float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats, Partial* parts,
+                            int64_t P_cap, float* mean_out, float* rstd_out, hipStream_t st, hipError_t& err)
+{
+    DeviceInfo d;
+    if (!device_info(d)) return false;
+    const int64_t rows = ceil_div(inner / 4, (int64_t)kLnThreads);
+    const int64_t P = ceil_div(rows, (int64_t)F4PT);
+    if (P > P_cap) return false;
+    const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * kLnThreads * sizeof(f4);
+    if (lds + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
+    const void* fn = reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>);
+    if (coresident(fn, lds) < P) return false;
+    int64_t pcap = P_cap;
+    void* args[] = {(void*)&x, (void*)&w, (void*)&b, (void*)&y, (void*)&outer, (void*)&inner, (void*)&pcap,
+                    (void*)&eps, (void*)&ctrl, (void*)&counters, (void*)&flag, (void*)&stats, (void*)&parts,
+                    (void*)&mean_out, (void*)&rstd_out};
+    err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(kLnThreads), args, lds, st);
+    if (err == hipSuccess) err = hipGetLastError();
+    return true;
+}
+
+bool ln_single_supported(int64_t inner, const float* x, const float* w, const float* b, const float* y)
+{
+    return (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
 }
 
 hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
@@ -459,28 +761,29 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
 {
     char* base = static_cast<char*>(ws);
     LnCtrl* ctrl = reinterpret_cast<LnCtrl*>(base + lay.off_ctrl);
-    uint32_t* counter = reinterpret_cast<uint32_t*>(base + lay.off_counter);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(base + lay.off_counter);
     uint32_t* flag = reinterpret_cast<uint32_t*>(base + lay.off_flag);
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
-    const bool vec4 = (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
-    const int cap = single_capacity(vec4);
-    if (cap <= 0) return hipErrorInvalidDevice;
-    // One workgroup per chunk index; at most the co-resident count, at most
-    // the workspace's partial slots, and chunks of at least 1024 elements.
-    int64_t P = std::min<int64_t>({(int64_t)cap, lay.P_cap, std::max<int64_t>(1, ceil_div(inner, 1024))});
-    // Prefer a multiple of 256 workgroups (whole waves of CUs) when large.
-    if (P > 256) P = (P / 256) * 256;
-    const int64_t chunk = ceil_div(ceil_div(inner, P), 4) * 4;
-    int64_t pcap = lay.P_cap;
-    void* args[] = {(void*)&x, (void*)&w, (void*)&b, (void*)&y, (void*)&outer, (void*)&inner, (void*)&chunk,
-                    (void*)&pcap, (void*)&eps, (void*)&ctrl, (void*)&counter, (void*)&flag, (void*)&stats,
-                    (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
-    const void* fn = vec4 ? reinterpret_cast<const void*>(&ln_single_kernel<4>)
-                          : reinterpret_cast<const void*>(&ln_single_kernel<1>);
-    hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(kLnThreads), args, 0, st);
+
+    // The single-read kernel, when a co-resident grid can hold every
+    // sample's chunks (tuned register tile first, then the others).
+    if (ln_single_supported(inner, x, w, b, y)) {
+        hipError_t err = hipSuccess;
+#define NORMFWD_TRY_HOLD(F)                                                                                      \
+    if (try_launch_hold<F>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, lay.P_cap, mean_out, \
+                           rstd_out, st, err))                                                                   \
+        return err;
+        NORMFWD_TRY_HOLD(NORMFWD_LN_HOLD_F4PT)
+        NORMFWD_TRY_HOLD(4)
+        NORMFWD_TRY_HOLD(8)
+        NORMFWD_TRY_HOLD(16)
+#undef NORMFWD_TRY_HOLD
+    }
+    // Shapes the single-read kernel cannot hold run the split schedule.
+    hipError_t e = launch_ln_stats(x, outer, inner, eps, ws, lay, mean_out, rstd_out, st);
     if (e != hipSuccess) return e;
-    return hipGetLastError();
+    return launch_ln_apply(x, w, b, y, outer, inner, ws, lay, st);
 }
 
 }  // namespace normfwd

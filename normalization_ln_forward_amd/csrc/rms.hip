@@ -23,8 +23,21 @@
 
 #include <algorithm>
 
+// Channels per wave and 64-lane position segments per lane for the
+// register-held kernel (C = 64: 8 waves of 8 channels, 4 KiB per channel
+// row segment; the fastest of the shapes measured on MI355X).
 #ifndef NORMFWD_RMS_CPW
-#define NORMFWD_RMS_CPW 16
+#define NORMFWD_RMS_CPW 8
+#endif
+#ifndef NORMFWD_RMS_PPL
+#define NORMFWD_RMS_PPL 4
+#endif
+// Streaming (nontemporal) hints on the x loads and y stores.
+#ifndef NORMFWD_RMS_NT_LOAD
+#define NORMFWD_RMS_NT_LOAD 1
+#endif
+#ifndef NORMFWD_RMS_NT_STORE
+#define NORMFWD_RMS_NT_STORE 1
 #endif
 
 namespace normfwd {
@@ -36,53 +49,70 @@ struct VecOf<4> { using T = f4; };
 template <>
 struct VecOf<1> { using T = float; };
 
-template <int CPW, int VEC>
-__global__ void __launch_bounds__(1024)
+// Register budget per lane is CPW * PPL vectors; the block-size bound keeps
+// the compiler's VGPR limit (512 / waves-per-SIMD) above that.
+constexpr int hold_max_threads(int vecs) { return vecs <= 16 ? 1024 : vecs <= 32 ? 512 : 256; }
+
+template <int CPW, int PPL, int VEC>
+__global__ void __launch_bounds__(hold_max_threads(CPW * PPL))
 rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
 {
     using V = typename VecOf<VEC>::T;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    V* part = reinterpret_cast<V*>(smem_raw);  // [nwaves][64]
+    V* part = reinterpret_cast<V*>(smem_raw);  // [nwaves][PPL][64]
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
     const int64_t b = blockIdx.x / tiles;
     const int64_t tile = blockIdx.x - b * tiles;
-    const int64_t s = (tile * kWave + lane) * VEC;
-    const bool active = s < S;  // VEC == 4 implies S % 4 == 0: a lane's 4 positions are all in range
+    // position of (lane, j): the wave reads PPL adjacent 64*VEC-position segments per channel
+    const int64_t s0 = tile * (kWave * PPL * VEC) + (int64_t)lane * VEC;
     const int c0 = wave * CPW;
-    const int64_t base = (b * C + c0) * S + s;
+    const int64_t base = (b * C + c0) * S + s0;
 
-    V v[CPW];
-    V acc = V(0.0f);
+    V v[CPW][PPL];
 #pragma unroll
-    for (int k = 0; k < CPW; ++k) {
-        if (active && c0 + k < C)
-            v[k] = ld_nt(reinterpret_cast<const V*>(x + base + (int64_t)k * S));
-        else
-            v[k] = V(0.0f);
+    for (int k = 0; k < CPW; ++k)
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+            const bool ok = (s0 + j * kWave * VEC < S) && (c0 + k < C);  // VEC == 4 implies S % 4 == 0
+            const V* src = reinterpret_cast<const V*>(x + base + (int64_t)k * S + j * kWave * VEC);
+            v[k][j] = ok ? (NORMFWD_RMS_NT_LOAD ? ld_nt(src) : *src) : V(0.0f);
+        }
+    V acc[PPL];
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+        acc[j] = V(0.0f);
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) acc[j] += v[k][j] * v[k][j];
+        part[(wave * PPL + j) * kWave + lane] = acc[j];
     }
-#pragma unroll
-    for (int k = 0; k < CPW; ++k) acc += v[k] * v[k];
-
-    part[wave * kWave + lane] = acc;
     __syncthreads();
-    V tot = part[lane];
-    for (int w = 1; w < nwaves; ++w) tot += part[w * kWave + lane];
-
-    V inv;
-    if constexpr (VEC == 4) {
-        inv.x = 1.0f / sqrtf(tot.x / (float)C + eps);
-        inv.y = 1.0f / sqrtf(tot.y / (float)C + eps);
-        inv.z = 1.0f / sqrtf(tot.z / (float)C + eps);
-        inv.w = 1.0f / sqrtf(tot.w / (float)C + eps);
-    } else {
-        inv = 1.0f / sqrtf(tot / (float)C + eps);
-    }
 #pragma unroll
-    for (int k = 0; k < CPW; ++k) {
-        if (active && c0 + k < C) st_nt(v[k] * inv, reinterpret_cast<V*>(y + base + (int64_t)k * S));
+    for (int j = 0; j < PPL; ++j) {
+        V tot = part[j * kWave + lane];
+        for (int w = 1; w < nwaves; ++w) tot += part[(w * PPL + j) * kWave + lane];
+        V inv;
+        if constexpr (VEC == 4) {
+            inv.x = 1.0f / sqrtf(tot.x / (float)C + eps);
+            inv.y = 1.0f / sqrtf(tot.y / (float)C + eps);
+            inv.z = 1.0f / sqrtf(tot.z / (float)C + eps);
+            inv.w = 1.0f / sqrtf(tot.w / (float)C + eps);
+        } else {
+            inv = 1.0f / sqrtf(tot / (float)C + eps);
+        }
+        const bool okj = s0 + j * kWave * VEC < S;
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            if (okj && c0 + k < C) {
+                V* dst = reinterpret_cast<V*>(y + base + (int64_t)k * S + j * kWave * VEC);
+                if (NORMFWD_RMS_NT_STORE)
+                    st_nt(v[k][j] * inv, dst);
+                else
+                    *dst = v[k][j] * inv;
+            }
+        }
     }
 }
 
@@ -136,19 +166,19 @@ rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, 
 // larger tensors are launched in batches of whole samples.
 constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
 
-template <int CPW, int VEC>
+template <int CPW, int PPL, int VEC>
 static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
                               hipStream_t st)
 {
     const int nwaves = (int)ceil_div(C, CPW);
-    const int64_t tiles = ceil_div(S, (int64_t)kWave * VEC);
-    const size_t lds = (size_t)nwaves * kWave * sizeof(typename VecOf<VEC>::T);
+    const int64_t tiles = ceil_div(S, (int64_t)kWave * PPL * VEC);
+    const size_t lds = (size_t)nwaves * PPL * kWave * sizeof(typename VecOf<VEC>::T);
     const int64_t per_launch = std::max<int64_t>(1, kMaxGridItems / (tiles * nwaves * kWave));
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
         const int64_t off = b0 * C * S;
-        hipLaunchKernelGGL((rms_ch_hold_kernel<CPW, VEC>), dim3((unsigned)(nb * tiles)), dim3(nwaves * kWave),
-                           lds, st, x + off, y + off, (int)C, S, tiles, eps);
+        hipLaunchKernelGGL((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
+                           dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -176,10 +206,12 @@ template <int VEC>
 static hipError_t launch_vec(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
                              hipStream_t st)
 {
-    // Register-held kernel while C fits in at most 16 waves of CPW channels.
-    constexpr int cpw = NORMFWD_RMS_CPW;
-    if (C <= 16 * cpw) return launch_hold<cpw, VEC>(x, y, B, C, S, eps, st);
-    if (C <= 16 * 32) return launch_hold<32, VEC>(x, y, B, C, S, eps, st);
+    // Register-held kernel: the tuned shape when its waves fit one block,
+    // 16 channels per wave (up to 16 waves) beyond that, streaming above.
+    constexpr int cpw = NORMFWD_RMS_CPW, ppl = NORMFWD_RMS_PPL;
+    if (ceil_div(C, cpw) * kWave <= hold_max_threads(cpw * ppl))
+        return launch_hold<cpw, ppl, VEC>(x, y, B, C, S, eps, st);
+    if (C <= 16 * 16) return launch_hold<16, 1, VEC>(x, y, B, C, S, eps, st);
     return launch_stream<VEC>(x, y, B, C, S, eps, st);
 }
 

@@ -1,0 +1,145 @@
+"""Turn rocprofv3 output into the short summaries kept under profiles/.
+
+    python -m normalization_ln_forward_amd.profiling stats <kernel_stats.csv> --command "<cmd>"
+        Markdown table of per-kernel call count and average / min / max
+        duration from `rocprofv3 --kernel-trace --stats --output-format csv`.
+
+    python -m normalization_ln_forward_amd.profiling traffic <fetch_counter_collection.csv>
+        <write_counter_collection.csv> --copy-mib N --kernels k1,k2 --command "<cmd>" [--json out]
+        HBM bytes per launch of the named kernels from two `rocprofv3 --pmc`
+        passes (FETCH_SIZE, then WRITE_SIZE).  Each counter is scaled by what
+        it reads for the plain device copy of N MiB the same command ran
+        (torch's copy kernel: N MiB read, N MiB written), so the result is in
+        bytes whatever unit the counter uses.  With --json, the entries are
+        written to that file together with the hash of the kernel sources, so
+        bench.py reports them only while the kernels are unchanged.
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+# Source files whose text determines each kernel's code.
+KERNEL_SOURCES = {
+    "ln_partial_kernel": ["ln.hip", "common.hpp"],
+    "ln_merge_kernel": ["ln.hip", "common.hpp"],
+    "ln_normalize_rows_kernel": ["ln.hip", "common.hpp"],
+    "ln_normalize_kernel": ["ln.hip", "common.hpp"],
+    "ln_single_hold_kernel": ["ln.hip", "common.hpp"],
+    "gn_fast_kernel": ["gn.hip", "common.hpp"],
+    "rms_ch_hold_kernel": ["rms.hip", "common.hpp"],
+    "fc_mfma_kernel": ["fc.hip", "common.hpp"],
+}
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name):
+    m = re.search(r"normfwd::(\w+)(<[^(]*>)?", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    m = re.search(r"(\w+)\(", name)
+    return (m.group(1) if m else name)[:60]
+
+
+def stats_markdown(path, command):
+    rows = list(csv.DictReader(open(path)))
+    out = [f"Command: `{command}`", "",
+           "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_rows(path, counter):
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def _copy_value(per, copy_mib):
+    """Median counter value over the copy-reference dispatches (torch copy kernels of copy_mib)."""
+    vals = []
+    for name, vs in per.items():
+        if "copy" in name.lower() and "normfwd" not in name:
+            vals.extend(vs)
+    if not vals:
+        raise SystemExit("no copy-reference dispatch found")
+    # the reference copies are the largest copy dispatches in the run
+    vals.sort()
+    top = vals[-3:]
+    return statistics.median(top)
+
+
+def traffic(fetch_csv, write_csv, copy_mib, kernels):
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * (1 << 20)
+    f_scale = copy_bytes / _copy_value(fetch, copy_mib)
+    w_scale = copy_bytes / _copy_value(write, copy_mib)
+    out = {}
+    for k in kernels:
+        fv = [v for n, vs in fetch.items() if short_name(n).split("<")[0] == k for v in vs]
+        wv = [v for n, vs in write.items() if short_name(n).split("<")[0] == k for v in vs]
+        if not fv or not wv:
+            continue
+        fb = statistics.mean(fv) * f_scale
+        wb = statistics.mean(wv) * w_scale
+        out[k] = {"fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                  "hbm_bytes_per_launch": round(fb + wb), "dispatches": len(fv),
+                  "fetch_scale": f_scale, "write_scale": w_scale,
+                  "source_sha": source_sha(KERNEL_SOURCES.get(k, ["ln.hip"]))}
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--copy-mib", type=int, required=True)
+    b.add_argument("--kernels", required=True)
+    b.add_argument("--command", required=True)
+    b.add_argument("--json")
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        sys.stdout.write(stats_markdown(args.csv, args.command))
+        return
+    res = traffic(args.fetch_csv, args.write_csv, args.copy_mib, args.kernels.split(","))
+    for k, v in res.items():
+        v["command"] = args.command
+    if args.json:
+        old = {}
+        if os.path.exists(args.json):
+            with open(args.json) as f:
+                old = json.load(f)
+        old.update(res)
+        with open(args.json, "w") as f:
+            json.dump(old, f, indent=1, sort_keys=True)
+            f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -273,3 +273,22 @@ def test_fc_gn_full_size_sampled_rows():
     ref = oracle.fc_gn_lrelu_x2(_np(d["x"][rows]), _np(d["W"]), _np(d["b"]), _np(d["gamma"]), _np(d["beta"]), 512)
     rep = _assert_close(_np(y[rows]), ref, rtol=RTOL_FC, what="fc full")
     _say(f"  max_abs={rep['max_abs']:.3e} max_rel={rep['max_rel']:.3e}")
+
+
+def test_prepared_calls_match_direct_calls():
+    """nf.prepare re-issues exactly the marshalled C call (used by the benchmark's launch loops)."""
+    _say("prepared calls")
+    d = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(32, 8192), seed=21)
+    y1 = nf.gn_lrelu_x2_forward(d["x"], d["gamma"], d["beta"], 512)
+    y2 = torch.empty_like(y1)
+    call = nf.prepare(nf.gn_lrelu_x2_forward, d["x"], d["gamma"], d["beta"], 512, out=y2)
+    call()
+    assert torch.equal(y1, y2)
+    l = synth.make("ln_16x64x256x256", device="cuda", shape=(2, 64, 64, 64), seed=22)
+    for variant in (0, 1):
+        z1 = nf.ln_forward(l["x"], l["weight"], l["bias"], variant=variant)
+        z2 = torch.zeros_like(z1)
+        run = nf.prepare(nf.ln_forward, l["x"], l["weight"], l["bias"], variant=variant, out=z2)
+        run()
+        run()
+        assert torch.equal(z1, z2)
