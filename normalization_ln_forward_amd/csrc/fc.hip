@@ -7,10 +7,12 @@
 // operands are K-contiguous, so a workgroup stages a BM x BK tile of x and a
 // BN x BK tile of W in LDS (rows padded by 4 floats against bank conflicts)
 // and each of its four waves computes a 64 x 64 block of h as 2 x 2 MFMA
-// tiles.  Within one MFMA the two k values a lane pair contributes are free
+// tiles; LDS is double-buffered so the next K slice loads during the MFMAs.  Within one MFMA the two k values a lane pair contributes are free
 // to choose as long as x and W agree, so each lane reads 4 consecutive k of
 // its row with one 128-bit LDS read and feeds them to 4 successive MFMAs.
-// h goes to the workspace; the GroupNorm kernel then reads it back.
+// With 16- or 32-channel groups the GroupNorm epilogue runs on the
+// accumulators and y is written directly; otherwise h goes to the
+// workspace and the GroupNorm kernel reads it back.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -18,20 +20,93 @@ namespace normfwd {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kPad = 4;
+#ifndef NORMFWD_FC_BK
+#define NORMFWD_FC_BK 32
+#endif
+#ifndef NORMFWD_FC_PAD
+#define NORMFWD_FC_PAD 4
+#endif
+// GroupNorm epilogue inside the GEMM for 16- and 32-channel groups.
+#ifndef NORMFWD_FC_FUSE
+#define NORMFWD_FC_FUSE 1
+#endif
+constexpr int kBM = 128, kBN = 128, kBK = NORMFWD_FC_BK, kPad = NORMFWD_FC_PAD;
 constexpr int kLdsRow = kBK + kPad;
 
+// One K slice of x (BM x BK) and of W (BN x BK): kSliceVecs float4 of each per thread.
+constexpr int kSliceVecs = kBM * kBK / 4 / 256;
+constexpr int kVecsPerRow = kBK / 4;
+
 template <bool VEC>
+__device__ __forceinline__ void load_slice(const float* __restrict__ x, const float* __restrict__ W, int M, int N,
+                                           int K, int m0, int n0, int k0, f4 (&a)[kSliceVecs], f4 (&b)[kSliceVecs])
+{
+#pragma unroll
+    for (int u = 0; u < kSliceVecs; ++u) {
+        const int idx = threadIdx.x + 256 * u;
+        const int r = idx / kVecsPerRow, c = (idx % kVecsPerRow) * 4;
+        const int k = k0 + c;
+        a[u] = f4(0.0f);
+        b[u] = f4(0.0f);
+        if constexpr (VEC) {  // K % 4 == 0 and 16-byte aligned rows
+            if (m0 + r < M && k < K) a[u] = *reinterpret_cast<const f4*>(x + (int64_t)(m0 + r) * K + k);
+            if (n0 + r < N && k < K) b[u] = *reinterpret_cast<const f4*>(W + (int64_t)(n0 + r) * K + k);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (m0 + r < M && k + q < K) a[u][q] = x[(int64_t)(m0 + r) * K + k + q];
+                if (n0 + r < N && k + q < K) b[u][q] = W[(int64_t)(n0 + r) * K + k + q];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void store_slice(float* As, float* Bs, const f4 (&a)[kSliceVecs], const f4 (&b)[kSliceVecs])
+{
+#pragma unroll
+    for (int u = 0; u < kSliceVecs; ++u) {
+        const int idx = threadIdx.x + 256 * u;
+        const int r = idx / kVecsPerRow, c = (idx % kVecsPerRow) * 4;
+        *reinterpret_cast<f4*>(As + r * kLdsRow + c) = a[u];
+        *reinterpret_cast<f4*>(Bs + r * kLdsRow + c) = b[u];
+    }
+}
+
+// Software pipeline over K: while the waves multiply slice k out of one LDS
+// buffer, the loads of slice k+1 are in flight into registers; they are
+// written to the other buffer afterwards, so one barrier per slice
+// suffices.  (Prefetching two slices ahead doubled the register footprint
+// and halved occupancy; measured slower.)
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), fixed order,
+// every lane gets the total: quad butterflies, then rotations by 4 and 8
+// within the row.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_xor1(v);
+    v += dpp_xor2(v);
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+    return v;
+}
+
+// GM = 0: write h = x W^T + b to `out`.  GM = 16 or 32 (channels per group):
+// the GroupNorm -> LeakyReLU -> x + x epilogue runs on the accumulators and
+// `out` receives y; h never goes to memory.  In a 32 x 32 MFMA tile a lane
+// holds one column (channel) for 16 rows, so the 16 channels of a group
+// are the 16 lanes of one DPP row (GM = 32: two adjacent DPP rows), and
+// each row's group statistics are a 16-lane (32-lane) reduction per
+// register, two-pass in registers.
+template <bool VEC, int GM>
 __global__ void __launch_bounds__(256)
 fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
-               float* __restrict__ h, int M, int N, int K)
+               const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ out, int M,
+               int N, int K, float eps, float slope)
 {
-    __shared__ __attribute__((aligned(16))) float As[kBM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) float Bs[kBN * kLdsRow];
+    __shared__ __attribute__((aligned(16))) float As[2][kBM * kLdsRow];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kBN * kLdsRow];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * kBM;
     const int n0 = blockIdx.x * kBN;
@@ -44,35 +119,24 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f16v(0.0f);
 
-    for (int k0 = 0; k0 < K; k0 += kBK) {
-        // stage: each of A and B is 128 rows x 8 float4
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u;
-            const int r = idx >> 3, c = (idx & 7) * 4;
-            const int k = k0 + c;
-            f4 a = f4(0.0f), b = f4(0.0f);
-            if constexpr (VEC) {  // K % 4 == 0 and 16-byte aligned rows
-                if (m0 + r < M && k < K) a = *reinterpret_cast<const f4*>(x + (int64_t)(m0 + r) * K + k);
-                if (n0 + r < N && k < K) b = *reinterpret_cast<const f4*>(W + (int64_t)(n0 + r) * K + k);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (m0 + r < M && k + q < K) a[q] = x[(int64_t)(m0 + r) * K + k + q];
-                    if (n0 + r < N && k + q < K) b[q] = W[(int64_t)(n0 + r) * K + k + q];
-                }
-            }
-            *reinterpret_cast<f4*>(As + r * kLdsRow + c) = a;
-            *reinterpret_cast<f4*>(Bs + r * kLdsRow + c) = b;
-        }
-        __syncthreads();
+    f4 ra[kSliceVecs], rb[kSliceVecs];
+    load_slice<VEC>(x, W, M, N, K, m0, n0, 0, ra, rb);
+    store_slice(As[0], Bs[0], ra, rb);
+    __syncthreads();
+
+    const int nk = (K + kBK - 1) / kBK;
+    for (int it = 0; it < nk; ++it) {
+        const int cur = it & 1;
+        if (it + 1 < nk) load_slice<VEC>(x, W, M, N, K, m0, n0, (it + 1) * kBK, ra, rb);
+        const float* A = As[cur];
+        const float* B = Bs[cur];
 #pragma unroll
         for (int kq = 0; kq < kBK / 8; ++kq) {
             f4 av[2], bv[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                av[t] = *reinterpret_cast<const f4*>(As + (wm * 64 + t * 32 + li) * kLdsRow + kq * 8 + lh * 4);
-                bv[t] = *reinterpret_cast<const f4*>(Bs + (wn * 64 + t * 32 + li) * kLdsRow + kq * 8 + lh * 4);
+                av[t] = *reinterpret_cast<const f4*>(A + (wm * 64 + t * 32 + li) * kLdsRow + kq * 8 + lh * 4);
+                bv[t] = *reinterpret_cast<const f4*>(B + (wn * 64 + t * 32 + li) * kLdsRow + kq * 8 + lh * 4);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -82,6 +146,7 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][e], bv[j][e], acc[i][j], 0, 0, 0);
         }
+        if (it + 1 < nk) store_slice(As[cur ^ 1], Bs[cur ^ 1], ra, rb);
         __syncthreads();
     }
 
@@ -92,14 +157,49 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = n0 + wn * 64 + j * 32 + li;
-            if (col >= N) continue;
-            const float bb = bias ? bias[col] : 0.0f;
+            const bool col_ok = col < N;
+            const float bb = (bias && col_ok) ? bias[col] : 0.0f;
+            if constexpr (GM == 0) {
+                if (!col_ok) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                if (row < M) h[(int64_t)row * N + col] = acc[i][j][r] + bb;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                    if (row < M) out[(int64_t)row * N + col] = acc[i][j][r] + bb;
+                }
+            } else {
+                const float g = (gamma && col_ok) ? gamma[col] : 1.0f;
+                const float be = (beta && col_ok) ? beta[col] : 0.0f;
+                constexpr float inv_m = 1.0f / GM;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float hv = acc[i][j][r] + bb;
+                    float s1 = row16_sum(hv);
+                    if constexpr (GM == 32) s1 += __shfl_xor(s1, 16);
+                    const float d = hv - s1 * inv_m;
+                    float s2 = row16_sum(d * d);
+                    if constexpr (GM == 32) s2 += __shfl_xor(s2, 16);
+                    const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
+                    const float z = d * rstd * g + be;
+                    const float a = z > 0.0f ? z : slope * z;
+                    const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                    if (row < M && col_ok) out[(int64_t)row * N + col] = a + a;
+                }
             }
         }
+}
+
+template <int GM>
+static hipError_t launch_gemm(bool vec, dim3 grid, const float* x, const float* W, const float* b, const float* gamma,
+                              const float* beta, float* out, int64_t N, int64_t K, int64_t C, float eps, float slope,
+                              hipStream_t st)
+{
+    if (vec)
+        hipLaunchKernelGGL((fc_mfma_kernel<true, GM>), grid, dim3(256), 0, st, x, W, b, gamma, beta, out, (int)N,
+                           (int)C, (int)K, eps, slope);
+    else
+        hipLaunchKernelGGL((fc_mfma_kernel<false, GM>), grid, dim3(256), 0, st, x, W, b, gamma, beta, out, (int)N,
+                           (int)C, (int)K, eps, slope);
+    return hipGetLastError();
 }
 
 hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
@@ -109,13 +209,14 @@ hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const fl
     // The tile loader reads 16-byte vectors along K when rows allow it.
     auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const bool vec = K % 4 == 0 && al(x) && al(W);
-    float* h = static_cast<float*>(ws);
     const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, kBM));
-    if (vec)
-        hipLaunchKernelGGL(fc_mfma_kernel<true>, grid, dim3(256), 0, st, x, W, b, h, (int)N, (int)C, (int)K);
-    else
-        hipLaunchKernelGGL(fc_mfma_kernel<false>, grid, dim3(256), 0, st, x, W, b, h, (int)N, (int)C, (int)K);
-    hipError_t e = hipGetLastError();
+    const int64_t M = C / G;
+    // Groups of 16 or 32 channels fit in the GEMM epilogue (tiles are 32
+    // channels wide and start at multiples of 32).
+    if (NORMFWD_FC_FUSE && M == 16) return launch_gemm<16>(vec, grid, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+    if (NORMFWD_FC_FUSE && M == 32) return launch_gemm<32>(vec, grid, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+    float* h = static_cast<float*>(ws);
+    hipError_t e = launch_gemm<0>(vec, grid, x, W, b, nullptr, nullptr, h, N, K, C, eps, slope, st);
     if (e != hipSuccess) return e;
     return launch_gn_lrelu_x2(h, gamma, beta, y, N, C, G, eps, slope, st);
 }

@@ -248,10 +248,13 @@ def test_ln_in_place(variant):
 # ---------------------------------------------------------------- fc -> GroupNorm epilogue
 
 FC_CASES = [
-    # (N, K, C, G)
-    (100, 96, 384, 24),     # ragged row tile (100 < 128), 3 column tiles
-    (130, 70, 256, 16),     # K % 4 != 0 -> scalar tile loader, 2 row tiles
-    (64, 512, 160, 10),     # ragged column tile, M = 16
+    # (N, K, C, G)                 16- and 32-channel groups use the fused GEMM epilogue
+    (100, 96, 384, 24),     # M = 16 fused; ragged row tile (100 < 128), 3 column tiles
+    (130, 70, 256, 16),     # M = 16 fused; K % 4 != 0 -> scalar tile loader, 2 row tiles
+    (64, 512, 160, 10),     # M = 16 fused; ragged column tile
+    (96, 128, 256, 8),      # M = 32 fused
+    (70, 64, 256, 32),      # M = 8: GEMM writes h, then the GroupNorm kernel
+    (40, 36, 512, 8),       # M = 64: GEMM writes h, then the GroupNorm kernel
 ]
 
 
