@@ -52,6 +52,18 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
 
+// ---------------------------------------------------------------- XCD-aware order
+
+// Workgroups are dispatched to the 8 XCDs round-robin by index, so in index
+// order neighbouring workgroups land on different XCDs (each with its own L2
+// and TLB).  This remap hands XCD k the k-th contiguous eighth of the grid
+// (a bijection when the grid is a multiple of 8; identity otherwise).
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t blk, int64_t nblocks)
+{
+    if (nblocks % 8 != 0) return blk;
+    return (blk & 7) * (nblocks >> 3) + (blk >> 3);
+}
+
 // ---------------------------------------------------------------- helpers
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

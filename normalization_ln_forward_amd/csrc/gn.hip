@@ -28,6 +28,9 @@
 #ifndef NORMFWD_GN_ITEMS
 #define NORMFWD_GN_ITEMS 8
 #endif
+#ifndef NORMFWD_GN_XCD
+#define NORMFWD_GN_XCD 0
+#endif
 // Streaming (nontemporal) hints on the x loads and y stores.
 #ifndef NORMFWD_GN_NT_LOAD
 #define NORMFWD_GN_NT_LOAD 1
@@ -50,7 +53,8 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
                int64_t n_tiles, int64_t tiles_per_row, int64_t C4, int M, float eps, float slope)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t tile = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t blk = NORMFWD_GN_XCD ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int64_t tile = blk * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (tile >= n_tiles) return;  // whole wave leaves together
     const int64_t row = tile / tiles_per_row;
     const int64_t c4_0 = (tile - row * tiles_per_row) * (ITEMS * kWave) + lane;

@@ -86,6 +86,9 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 #ifndef NORMFWD_LN_NORM_SAMPLE_UNROLL
 #define NORMFWD_LN_NORM_SAMPLE_UNROLL 2
 #endif
+#ifndef NORMFWD_LN_XCD_CONTIG
+#define NORMFWD_LN_XCD_CONTIG 0
+#endif
 #ifndef NORMFWD_LN_XCD_MAP
 #define NORMFWD_LN_XCD_MAP 1
 #endif
@@ -303,8 +306,9 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
     using V = typename LnVec<VEC>::T;
     constexpr int U = NORMFWD_LN_PARTIAL_UNROLL;
     __shared__ double red[2 * kLnThreads / kWave];
-    const int64_t b = blockIdx.x / P;
-    const int64_t p = blockIdx.x - b * P;
+    const int64_t blk = NORMFWD_LN_XCD_CONTIG ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int64_t b = blk / P;
+    const int64_t p = blk - b * P;
     const float* xb = x + b * inner;
     const V* xv = reinterpret_cast<const V*>(xb);
     const int64_t nu = inner / VEC;
@@ -419,7 +423,8 @@ ln_normalize_rows_kernel(const float* x, const float* w, const float* bias, floa
     using V = typename LnVec<VEC>::T;
     constexpr int U = NORMFWD_LN_NORM_SAMPLE_UNROLL;
     const int64_t nu = inner / VEC;
-    const int64_t j = (int64_t)blockIdx.x * kLnThreads + threadIdx.x;
+    const int64_t blk = NORMFWD_LN_XCD_CONTIG ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int64_t j = blk * kLnThreads + threadIdx.x;
     if (j >= nu) return;
     const V wv = w ? reinterpret_cast<const V*>(w)[j] : V(1.0f);
     const V bv = bias ? reinterpret_cast<const V*>(bias)[j] : V(0.0f);
