@@ -135,6 +135,9 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
     if (s != NORMFWD_OK) return s;
     (void)hipGetLastError();
     hipStream_t st = (hipStream_t)stream;
+    hipError_t re = hipSuccess;
+    if (normfwd::launch_ln_rows(x, weight, bias, y, outer, inner, eps, mean_out, rstd_out, st, re))
+        return hip_status(re, "ln_forward (one workgroup per sample) launch");
     if (variant == 1)
         return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
                                                     rstd_out, st),

@@ -30,6 +30,10 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
                            const LnLayout& lay, float* mean_out, float* rstd_out, hipStream_t st);
 hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float* y, int64_t outer,
                            int64_t inner, const void* ws, const LnLayout& lay, hipStream_t st);
+// One workgroup per sample when the sample fits its registers (inner <=
+// 8192 with 128-bit access, <= 2048 otherwise); false if it does not.
+bool launch_ln_rows(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner, float eps,
+                    float* mean_out, float* rstd_out, hipStream_t st, hipError_t& err);
 hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                             int64_t inner, float eps, void* ws, const LnLayout& lay, float* mean_out,
                             float* rstd_out, hipStream_t st);

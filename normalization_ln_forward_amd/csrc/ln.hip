@@ -451,6 +451,92 @@ ln_normalize_rows_kernel(const float* x, const float* w, const float* bias, floa
     }
 }
 
+// ---------------------------------------------------------------- one workgroup per sample
+
+// Sum of one double per thread over the workgroup, fixed order; valid in
+// every thread on return.  red: LDS of NT/64 + 1 doubles.
+__device__ __forceinline__ double block_sum(double v, double* red)
+{
+    v = wave_sum(v);
+    const int wave = threadIdx.x / kWave;
+    __syncthreads();  // red may still be read from a previous use
+    if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
+    __syncthreads();
+    double t = red[0];
+    for (int w = 1; w < kLnThreads / kWave; ++w) t += red[w];
+    return t;
+}
+
+// Samples of at most 256 * UPT units (a unit is one float4, or one float
+// on the scalar path): one workgroup holds the whole sample in VGPRs, takes
+// the two passes over registers (mean of d = x - K with K the sample's first
+// element, then the sum of (d - mean_d)^2) and writes y; x is read once and
+// no workspace is involved.  This is the shape of LayerNorm used in
+// transformer blocks (many samples of a few thousand elements).
+template <int VEC, int UPT>
+__global__ void __launch_bounds__(kLnThreads)
+ln_row_kernel(const float* x, const float* w, const float* bias, float* y, int64_t inner, float eps,
+              float* mean_out, float* rstd_out)
+{
+    using V = typename LnVec<VEC>::T;
+    __shared__ double red[kLnThreads / kWave];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * inner;
+    const V* xv = reinterpret_cast<const V*>(xr);
+    const int64_t nu = inner / VEC;
+    const float K = xr[0];
+    V v[UPT];
+    V a = V(0.0f);
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        const int64_t j = threadIdx.x + (int64_t)k * kLnThreads;
+        v[k] = j < nu ? xv[j] : V(K);
+        a += v[k] - K;
+    }
+    double t;
+    if constexpr (VEC == 4)
+        t = ((double)a.x + (double)a.y) + ((double)a.z + (double)a.w);
+    else
+        t = (double)a;
+    const double n = (double)inner;
+    const double mean_d = block_sum(t, red) / n;
+    const float md = (float)mean_d;
+    V q = V(0.0f);
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        const V e = (v[k] - K) - md;  // padding lanes hold K: e = -md, masked below
+        const int64_t j = threadIdx.x + (int64_t)k * kLnThreads;
+        if (j < nu) q += e * e;
+    }
+    if constexpr (VEC == 4)
+        t = ((double)q.x + (double)q.y) + ((double)q.z + (double)q.w);
+    else
+        t = (double)q;
+    // sum of (d - md)^2 = sum of (d - mean_d)^2 + n (mean_d - md)^2
+    const double dm = mean_d - (double)md;
+    const double var = fmax(block_sum(t, red) / n - dm * dm, 0.0);
+    const double mean = (double)K + mean_d;
+    const double rstd = 1.0 / sqrt(var + (double)eps);
+    const float hi = (float)mean;
+    const float lo = (float)(mean - (double)hi);
+    const float rs = (float)rstd;
+    if (threadIdx.x == 0) {
+        if (mean_out) mean_out[row] = hi;
+        if (rstd_out) rstd_out[row] = rs;
+    }
+    V* yv = reinterpret_cast<V*>(y + row * inner);
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        const int64_t j = threadIdx.x + (int64_t)k * kLnThreads;
+        if (j < nu) {
+            const V tt = ((v[k] - hi) - lo) * rs;
+            const V wv = w ? reinterpret_cast<const V*>(w)[j] : V(1.0f);
+            const V bv = bias ? reinterpret_cast<const V*>(bias)[j] : V(0.0f);
+            st_nt(tt * wv + bv, yv + j);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- single-kernel variant
 
 // Last arriver of sample t in the single kernel: merge its partials, store
@@ -656,7 +742,10 @@ hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float
         bps = ceil_div(bps, 8) * 8;
         xcd_map = 1;
     }
-    if (NORMFWD_LN_NORM_MODE == 1) {
+    // The sample loop needs enough rows per sample to fill the GPU (each of
+    // its workgroups walks all `outer` samples); short samples use one row
+    // per workgroup.
+    if (NORMFWD_LN_NORM_MODE == 1 && ceil_div(nu, (int64_t)kLnThreads) >= 1024) {
         const dim3 g((unsigned)ceil_div(nu, (int64_t)kLnThreads));
         if (vec4)
             hipLaunchKernelGGL(ln_normalize_rows_kernel<4>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
@@ -672,6 +761,34 @@ hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float
         hipLaunchKernelGGL(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
                            xcd_map, stats);
     return hipGetLastError();
+}
+
+bool launch_ln_rows(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner, float eps,
+                    float* mean_out, float* rstd_out, hipStream_t st, hipError_t& err)
+{
+    const bool vec4 = (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
+    const int64_t nu = vec4 ? inner / 4 : inner;
+    const dim3 grid((unsigned)outer);
+#define NORMFWD_ROWS(VEC, U)                                                                                    \
+    if (nu <= (int64_t)kLnThreads * (U)) {                                                                      \
+        hipLaunchKernelGGL((ln_row_kernel<VEC, U>), grid, dim3(kLnThreads), 0, st, x, w, b, y, inner, eps, mean_out, \
+                           rstd_out);                                                                           \
+        err = hipGetLastError();                                                                                \
+        return true;                                                                                            \
+    }
+    if (vec4) {
+        NORMFWD_ROWS(4, 1)
+        NORMFWD_ROWS(4, 2)
+        NORMFWD_ROWS(4, 4)
+        NORMFWD_ROWS(4, 8)
+    } else {
+        NORMFWD_ROWS(1, 1)
+        NORMFWD_ROWS(1, 2)
+        NORMFWD_ROWS(1, 4)
+        NORMFWD_ROWS(1, 8)
+    }
+#undef NORMFWD_ROWS
+    return false;
 }
 
 struct DeviceInfo {

@@ -196,6 +196,36 @@ def test_ln_parity(outer, inner, affine, variant):
     np.testing.assert_allclose(_np(rstd), 1.0 / np.sqrt(ov + np.float32(1e-5)), rtol=1e-5)
 
 
+LN_ROW_CASES = [
+    # (outer, inner, dist)  one workgroup per sample (inner <= 8192 vectorized, <= 2048 scalar)
+    (64, 4096, "n01"),
+    (1000, 768, "n01"),
+    (33, 2047, "n01"),          # scalar path
+    (7, 8192, "n01"),           # largest vectorized row
+    (9, 8196, "n01"),           # just above: split schedule, one row per normalize workgroup
+    (300, 20000, "n01"),        # split, many samples of a few rows each
+    (64, 4096, "stress"),       # N(100, 0.01) in the row kernel
+    (16, 1000, "stress"),
+]
+
+
+@pytest.mark.parametrize("outer,inner,dist", LN_ROW_CASES)
+def test_ln_many_short_samples(outer, inner, dist):
+    _say(f"ln rows outer={outer} inner={inner} dist={dist}")
+    name = "ln_stress_16x64x256x256" if dist == "stress" else "ln_16x64x256x256"
+    d = synth.make(name, device="cuda", shape=(outer, inner), seed=outer + inner, normalized_ndim=1)
+    mean = torch.empty(outer, device="cuda")
+    rstd = torch.empty(outer, device="cuda")
+    y = nf.ln_forward(d["x"], d["weight"], d["bias"], eps=1e-5, mean_out=mean, rstd_out=rstd)
+    ref, om, ov = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]), eps=1e-5, return_stats=True)
+    _assert_close(_np(y), ref, what="ln rows")
+    np.testing.assert_allclose(_np(mean), om, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(_np(rstd), 1.0 / np.sqrt(ov + np.float32(1e-5)), rtol=1e-5)
+    x = d["x"].clone()
+    nf.ln_forward(x, d["weight"], d["bias"], out=x)  # in place
+    assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("name", ["ln_16x64x256x256", "ln_stress_16x64x256x256"])
 @pytest.mark.parametrize("variant", [0, 1])
 def test_ln_full_size(name, variant):
