@@ -221,20 +221,15 @@ __device__ __forceinline__ bool deliver_partial(Partial* part, const Partial& v,
 
 // Merge parts[0, P) in a fixed order: thread t folds partials t, t + 256,
 // ..., then a fixed tree over the threads.  The result is valid in thread 0.
-// Coherent: read the partials with device-coherent loads (they were written
-// by other workgroups of the same launch).  lds: 3 * 256 doubles.
-template <bool Coherent>
+// The partials were written by other workgroups of the same launch, so they
+// are read with device-coherent loads.  lds: 3 * 256 doubles.
 __device__ void merge_partials(const Partial* parts, int64_t P, double* lds, double& n, double& m, double& m2)
 {
     n = 0.0;
     m = 0.0;
     m2 = 0.0;
-    for (int64_t j = threadIdx.x; j < P; j += kLnThreads) {
-        if constexpr (Coherent)
-            chan_merge(n, m, m2, dev_load(&parts[j].n), dev_load(&parts[j].mean), dev_load(&parts[j].m2));
-        else
-            chan_merge(n, m, m2, parts[j].n, parts[j].mean, parts[j].m2);
-    }
+    for (int64_t j = threadIdx.x; j < P; j += kLnThreads)
+        chan_merge(n, m, m2, dev_load(&parts[j].n), dev_load(&parts[j].mean), dev_load(&parts[j].m2));
     double* ln_ = lds;
     double* lm = lds + kLnThreads;
     double* lm2 = lds + 2 * kLnThreads;
@@ -342,16 +337,22 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
     if (threadIdx.x == 0) parts[b * P_cap + p] = make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2);
 }
 
-// One workgroup per sample: merge its P partials in partial order into
-// (mean hi, mean lo, rstd).
-__global__ void __launch_bounds__(kLnThreads)
+// One wave per sample: lane l folds partials l, l + 64, ... in order, then a
+// fixed butterfly over the 64 lanes (shuffles, no LDS or barriers) merges
+// the lanes' results; lane 0 writes (mean hi, mean lo, rstd).
+__global__ void __launch_bounds__(kWave)
 ln_merge_kernel(const Partial* parts, int64_t P, int64_t P_cap, float eps, f4* stats, float* mean_out,
                 float* rstd_out)
 {
-    __shared__ double lds[3 * kLnThreads];
     const int64_t b = blockIdx.x;
-    double n, m, m2;
-    merge_partials<false>(parts + b * P_cap, P, lds, n, m, m2);
+    const Partial* pb = parts + b * P_cap;
+    double n = 0.0, m = 0.0, m2 = 0.0;
+    for (int64_t j = threadIdx.x; j < P; j += kWave) chan_merge(n, m, m2, pb[j].n, pb[j].mean, pb[j].m2);
+#pragma unroll
+    for (int mask = 1; mask < kWave; mask <<= 1) {
+        const double on = __shfl_xor(n, mask), om = __shfl_xor(m, mask), om2 = __shfl_xor(m2, mask);
+        chan_merge(n, m, m2, on, om, om2);
+    }
     if (threadIdx.x == 0) {
         const f4 st = finish_stats(n, m, m2, eps);
         stats[b] = st;
@@ -546,7 +547,7 @@ __device__ void merge_and_announce(const Partial* parts, int64_t P, float eps, d
                                    int64_t t, uint32_t target)
 {
     double n, m, m2;
-    merge_partials<true>(parts, P, lds, n, m, m2);
+    merge_partials(parts, P, lds, n, m, m2);
     if (threadIdx.x == 0) {
         const f4 st = finish_stats(n, m, m2, eps);
         float* sp = reinterpret_cast<float*>(stats_t);
@@ -723,8 +724,8 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
         hipLaunchKernelGGL(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ln_merge_kernel, dim3((unsigned)outer), dim3(kLnThreads), 0, st, parts, lay.P, lay.P_cap,
-                       eps, stats, mean_out, rstd_out);
+    hipLaunchKernelGGL(ln_merge_kernel, dim3((unsigned)outer), dim3(kWave), 0, st, parts, lay.P, lay.P_cap, eps,
+                       stats, mean_out, rstd_out);
     return hipGetLastError();
 }
 
