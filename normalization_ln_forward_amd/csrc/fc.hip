@@ -6,10 +6,11 @@
 // fp32 products with fp32 accumulation; no reduced-precision inputs).  Both
 // operands are K-contiguous, so a workgroup stages a BM x BK tile of x and a
 // BN x BK tile of W in LDS (rows padded by 4 floats against bank conflicts)
-// and each of its four waves computes a 64 x 64 block of h as 2 x 2 MFMA
-// tiles; LDS is double-buffered so the next K slice loads during the MFMAs.  Within one MFMA the two k values a lane pair contributes are free
-// to choose as long as x and W agree, so each lane reads 4 consecutive k of
-// its row with one 128-bit LDS read and feeds them to 4 successive MFMAs.
+// and each of its waves computes a 64 x 64 block of h as 2 x 2 MFMA tiles;
+// LDS is double-buffered so the next K slice loads during the MFMAs.
+// Within one MFMA the two k values a lane pair contributes are free to
+// choose as long as x and W agree, so each lane reads 4 consecutive k of its
+// row with one 128-bit LDS read and feeds them to 4 successive MFMAs.
 // With 16- or 32-channel groups the GroupNorm epilogue runs on the
 // accumulators and y is written directly; otherwise h goes to the
 // workspace and the GroupNorm kernel reads it back.
@@ -30,53 +31,72 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 #ifndef NORMFWD_FC_FUSE
 #define NORMFWD_FC_FUSE 1
 #endif
-constexpr int kBM = 128, kBN = 128, kBK = NORMFWD_FC_BK, kPad = NORMFWD_FC_PAD;
+#ifndef NORMFWD_FC_WM
+#define NORMFWD_FC_WM 4
+#endif
+constexpr int kBN = 128, kBK = NORMFWD_FC_BK, kPad = NORMFWD_FC_PAD;
 constexpr int kLdsRow = kBK + kPad;
-
-// One K slice of x (BM x BK) and of W (BN x BK): kSliceVecs float4 of each per thread.
-constexpr int kSliceVecs = kBM * kBK / 4 / 256;
 constexpr int kVecsPerRow = kBK / 4;
 
+// Workgroup of WM x 2 waves, each computing 64 x 64 of h: a BM = 64 WM by
+// BN = 128 output tile.  One K slice is BM x BK of x and BN x BK of W.
+template <int WM>
+struct Tile {
+    static constexpr int kThreads = 128 * WM;
+    static constexpr int kBM = 64 * WM;
+    static constexpr int kVecsA = kBM * kBK / 4 / kThreads;
+    static constexpr int kVecsB = kBN * kBK / 4 / kThreads;
+};
+
 template <bool VEC>
+__device__ __forceinline__ f4 load_row_vec(const float* __restrict__ p, int rows, int K, int r, int k)
+{
+    f4 v = f4(0.0f);
+    if constexpr (VEC) {  // K % 4 == 0 and 16-byte aligned rows
+        if (r < rows && k < K) v = *reinterpret_cast<const f4*>(p + (int64_t)r * K + k);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (r < rows && k + q < K) v[q] = p[(int64_t)r * K + k + q];
+    }
+    return v;
+}
+
+template <bool VEC, int WM>
 __device__ __forceinline__ void load_slice(const float* __restrict__ x, const float* __restrict__ W, int M, int N,
-                                           int K, int m0, int n0, int k0, f4 (&a)[kSliceVecs], f4 (&b)[kSliceVecs])
+                                           int K, int m0, int n0, int k0, f4 (&a)[Tile<WM>::kVecsA],
+                                           f4 (&b)[Tile<WM>::kVecsB])
 {
+    using T = Tile<WM>;
 #pragma unroll
-    for (int u = 0; u < kSliceVecs; ++u) {
-        const int idx = threadIdx.x + 256 * u;
-        const int r = idx / kVecsPerRow, c = (idx % kVecsPerRow) * 4;
-        const int k = k0 + c;
-        a[u] = f4(0.0f);
-        b[u] = f4(0.0f);
-        if constexpr (VEC) {  // K % 4 == 0 and 16-byte aligned rows
-            if (m0 + r < M && k < K) a[u] = *reinterpret_cast<const f4*>(x + (int64_t)(m0 + r) * K + k);
-            if (n0 + r < N && k < K) b[u] = *reinterpret_cast<const f4*>(W + (int64_t)(n0 + r) * K + k);
-        } else {
+    for (int u = 0; u < T::kVecsA; ++u) {
+        const int idx = threadIdx.x + T::kThreads * u;
+        a[u] = load_row_vec<VEC>(x, M, K, m0 + idx / kVecsPerRow, k0 + (idx % kVecsPerRow) * 4);
+    }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (m0 + r < M && k + q < K) a[u][q] = x[(int64_t)(m0 + r) * K + k + q];
-                if (n0 + r < N && k + q < K) b[u][q] = W[(int64_t)(n0 + r) * K + k + q];
-            }
-        }
+    for (int u = 0; u < T::kVecsB; ++u) {
+        const int idx = threadIdx.x + T::kThreads * u;
+        b[u] = load_row_vec<VEC>(W, N, K, n0 + idx / kVecsPerRow, k0 + (idx % kVecsPerRow) * 4);
     }
 }
 
-__device__ __forceinline__ void store_slice(float* As, float* Bs, const f4 (&a)[kSliceVecs], const f4 (&b)[kSliceVecs])
+template <int WM>
+__device__ __forceinline__ void store_slice(float* As, float* Bs, const f4 (&a)[Tile<WM>::kVecsA],
+                                            const f4 (&b)[Tile<WM>::kVecsB])
 {
+    using T = Tile<WM>;
 #pragma unroll
-    for (int u = 0; u < kSliceVecs; ++u) {
-        const int idx = threadIdx.x + 256 * u;
-        const int r = idx / kVecsPerRow, c = (idx % kVecsPerRow) * 4;
-        *reinterpret_cast<f4*>(As + r * kLdsRow + c) = a[u];
-        *reinterpret_cast<f4*>(Bs + r * kLdsRow + c) = b[u];
+    for (int u = 0; u < T::kVecsA; ++u) {
+        const int idx = threadIdx.x + T::kThreads * u;
+        *reinterpret_cast<f4*>(As + (idx / kVecsPerRow) * kLdsRow + (idx % kVecsPerRow) * 4) = a[u];
+    }
+#pragma unroll
+    for (int u = 0; u < T::kVecsB; ++u) {
+        const int idx = threadIdx.x + T::kThreads * u;
+        *reinterpret_cast<f4*>(Bs + (idx / kVecsPerRow) * kLdsRow + (idx % kVecsPerRow) * 4) = b[u];
     }
 }
 
-// Software pipeline over K: while the waves multiply slice k out of one LDS
-// buffer, the loads of slice k+1 are in flight into registers; they are
-// written to the other buffer afterwards, so one barrier per slice
-// suffices.  (Prefetching two slices ahead doubled the register footprint
-// and halved occupancy; measured slower.)
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), fixed order,
 // every lane gets the total: quad butterflies, then rotations by 4 and 8
 // within the row.
@@ -96,19 +116,26 @@ __device__ __forceinline__ float row16_sum(float v)
 // are the 16 lanes of one DPP row (GM = 32: two adjacent DPP rows), and
 // each row's group statistics are a 16-lane (32-lane) reduction per
 // register, two-pass in registers.
-template <bool VEC, int GM>
-__global__ void __launch_bounds__(256)
+//
+// Software pipeline over K: while the waves multiply slice k out of one LDS
+// buffer, the loads of slice k+1 are in flight into registers; they are
+// written to the other buffer afterwards, so one barrier per slice
+// suffices.  (Prefetching two slices ahead doubled the register footprint
+// and halved occupancy; measured slower.)
+template <bool VEC, int GM, int WM>
+__global__ void __launch_bounds__(Tile<WM>::kThreads)
 fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
                const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ out, int M,
                int N, int K, float eps, float slope)
 {
-    __shared__ __attribute__((aligned(16))) float As[2][kBM * kLdsRow];
+    using T = Tile<WM>;
+    __shared__ __attribute__((aligned(16))) float As[2][T::kBM * kLdsRow];
     __shared__ __attribute__((aligned(16))) float Bs[2][kBN * kLdsRow];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * kBM;
+    const int m0 = blockIdx.y * T::kBM;
     const int n0 = blockIdx.x * kBN;
     const int li = lane & 31;  // row / column inside a 32 x 32 tile
     const int lh = lane >> 5;  // which half of the k pair
@@ -119,15 +146,15 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f16v(0.0f);
 
-    f4 ra[kSliceVecs], rb[kSliceVecs];
-    load_slice<VEC>(x, W, M, N, K, m0, n0, 0, ra, rb);
-    store_slice(As[0], Bs[0], ra, rb);
+    f4 ra[T::kVecsA], rb[T::kVecsB];
+    load_slice<VEC, WM>(x, W, M, N, K, m0, n0, 0, ra, rb);
+    store_slice<WM>(As[0], Bs[0], ra, rb);
     __syncthreads();
 
     const int nk = (K + kBK - 1) / kBK;
     for (int it = 0; it < nk; ++it) {
         const int cur = it & 1;
-        if (it + 1 < nk) load_slice<VEC>(x, W, M, N, K, m0, n0, (it + 1) * kBK, ra, rb);
+        if (it + 1 < nk) load_slice<VEC, WM>(x, W, M, N, K, m0, n0, (it + 1) * kBK, ra, rb);
         const float* A = As[cur];
         const float* B = Bs[cur];
 #pragma unroll
@@ -146,7 +173,7 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][e], bv[j][e], acc[i][j], 0, 0, 0);
         }
-        if (it + 1 < nk) store_slice(As[cur ^ 1], Bs[cur ^ 1], ra, rb);
+        if (it + 1 < nk) store_slice<WM>(As[cur ^ 1], Bs[cur ^ 1], ra, rb);
         __syncthreads();
     }
 
@@ -189,16 +216,19 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
 }
 
 template <int GM>
-static hipError_t launch_gemm(bool vec, dim3 grid, const float* x, const float* W, const float* b, const float* gamma,
+static hipError_t launch_gemm(bool vec, const float* x, const float* W, const float* b, const float* gamma,
                               const float* beta, float* out, int64_t N, int64_t K, int64_t C, float eps, float slope,
                               hipStream_t st)
 {
+    constexpr int WM = NORMFWD_FC_WM;
+    using T = Tile<WM>;
+    const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, T::kBM));
     if (vec)
-        hipLaunchKernelGGL((fc_mfma_kernel<true, GM>), grid, dim3(256), 0, st, x, W, b, gamma, beta, out, (int)N,
-                           (int)C, (int)K, eps, slope);
+        hipLaunchKernelGGL((fc_mfma_kernel<true, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
+                           (int)N, (int)C, (int)K, eps, slope);
     else
-        hipLaunchKernelGGL((fc_mfma_kernel<false, GM>), grid, dim3(256), 0, st, x, W, b, gamma, beta, out, (int)N,
-                           (int)C, (int)K, eps, slope);
+        hipLaunchKernelGGL((fc_mfma_kernel<false, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
+                           (int)N, (int)C, (int)K, eps, slope);
     return hipGetLastError();
 }
 
@@ -209,14 +239,13 @@ hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const fl
     // The tile loader reads 16-byte vectors along K when rows allow it.
     auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const bool vec = K % 4 == 0 && al(x) && al(W);
-    const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, kBM));
     const int64_t M = C / G;
     // Groups of 16 or 32 channels fit in the GEMM epilogue (tiles are 32
     // channels wide and start at multiples of 32).
-    if (NORMFWD_FC_FUSE && M == 16) return launch_gemm<16>(vec, grid, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
-    if (NORMFWD_FC_FUSE && M == 32) return launch_gemm<32>(vec, grid, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+    if (NORMFWD_FC_FUSE && M == 16) return launch_gemm<16>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+    if (NORMFWD_FC_FUSE && M == 32) return launch_gemm<32>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
     float* h = static_cast<float*>(ws);
-    hipError_t e = launch_gemm<0>(vec, grid, x, W, b, nullptr, nullptr, h, N, K, C, eps, slope, st);
+    hipError_t e = launch_gemm<0>(vec, x, W, b, nullptr, nullptr, h, N, K, C, eps, slope, st);
     if (e != hipSuccess) return e;
     return launch_gn_lrelu_x2(h, gamma, beta, y, N, C, G, eps, slope, st);
 }
