@@ -287,7 +287,7 @@ def cpu_baseline(base, seconds, log):
         oracle.ln(x, w, b, eps=1e-5)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 100:
+        if el >= seconds or reps >= 2000:
             break
     per = el / reps
     log(f"[bench] oracle LN: {per:.3f} s per full workload ({reps} reps, {oracle.num_threads()} threads)")
