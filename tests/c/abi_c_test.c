@@ -1,0 +1,169 @@
+/*
+ * The C ABI used from plain C, with no torch and no Python: device memory
+ * from hipMalloc, results checked against the fp64 oracle (test
+ * infrastructure, linked from oracle/liboracle.so).
+ *
+ *   abi_c_test validate   argument validation only (no GPU work; runs anywhere)
+ *   abi_c_test run        LayerNorm, GroupNorm+LeakyReLU+x2 and channel RMSNorm on the GPU
+ *
+ * Inputs come from a 64-bit linear congruential generator (Knuth's MMIX
+ * constants) mapped to [-2, 2); the same host arrays feed the GPU and the
+ * oracle.  Exit status 0 = pass.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "normfwd.h"
+
+void oracle_ln(const double* x, const double* w, const double* b, int64_t outer, int64_t inner, double eps,
+               double* y, double* mean_out, double* var_out);
+void oracle_gn_lrelu_x2(const double* x, const double* gamma, const double* beta, int64_t N, int64_t C, int64_t G,
+                        double eps, double slope, double* y, double* mean_out, double* var_out);
+void oracle_rms_ch(const double* x, int64_t B, int64_t C, int64_t S, double eps, double* y, double* ms_out);
+
+static uint64_t g_state = 0x9E3779B97F4A7C15ull;
+static float next_uniform(void)
+{
+    g_state = g_state * 6364136223846793005ull + 1442695040888963407ull;
+    return (float)((g_state >> 40) * (1.0 / 16777216.0)) * 4.0f - 2.0f;
+}
+
+static float* host_random(size_t n)
+{
+    float* p = (float*)malloc(n * sizeof(float));
+    for (size_t i = 0; i < n; ++i) p[i] = next_uniform();
+    return p;
+}
+
+static double* promote(const float* p, size_t n)
+{
+    double* d = (double*)malloc(n * sizeof(double));
+    for (size_t i = 0; i < n; ++i) d[i] = p[i];
+    return d;
+}
+
+static float* to_device(const float* h, size_t n)
+{
+    void* d = NULL;
+    if (hipMalloc(&d, n * sizeof(float)) != hipSuccess) return NULL;
+    if (h && hipMemcpy(d, h, n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) return NULL;
+    return (float*)d;
+}
+
+/* |g - o| <= 1e-4 + 1e-4 |o| everywhere */
+static int compare(const char* what, const float* g, const double* o, size_t n)
+{
+    double worst = 0.0;
+    size_t bad = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const double e = fabs((double)g[i] - o[i]);
+        if (!(e <= 1e-4 + 1e-4 * fabs(o[i]))) ++bad;
+        if (e > worst) worst = e;
+    }
+    printf("%-22s n=%zu max_abs=%.3e bad=%zu\n", what, n, worst, bad);
+    return bad == 0 ? 0 : 1;
+}
+
+static int validate(void)
+{
+    int fails = 0;
+    float* fake = (float*)(uintptr_t)0x100000;
+    void* ws = (void*)(uintptr_t)0x200000;
+    fails += ln_forward(NULL, NULL, NULL, fake, 2, 8, 1e-5f, ws, 1 << 20, NULL, NULL, 0, NULL) != NORMFWD_ERR_INVALID;
+    fails += ln_forward(fake, NULL, NULL, fake, 2, 8, 1e-5f, NULL, 1 << 20, NULL, NULL, 0, NULL) != NORMFWD_ERR_WORKSPACE;
+    fails += gn_lrelu_x2_forward(fake, NULL, NULL, fake, 4, 10, 3, 1e-5f, 0.01f, NULL) != NORMFWD_ERR_INVALID;
+    fails += rmsnorm_ch_forward(fake, fake, 2, 0, 4, 1e-5f, NULL) != NORMFWD_ERR_INVALID;
+    fails += strlen(normfwd_last_error()) == 0;
+    fails += strcmp(normfwd_status_string(NORMFWD_OK), "NORMFWD_OK") != 0;
+    printf("validate: %s\n", fails ? "FAIL" : "ok");
+    return fails ? 1 : 0;
+}
+
+static int run(void)
+{
+    int fails = 0;
+    hipStream_t st;
+    if (hipStreamCreate(&st) != hipSuccess) return 2;
+
+    /* LayerNorm [5, 70000] with affine */
+    {
+        const int64_t outer = 5, inner = 70000;
+        const size_t n = (size_t)(outer * inner);
+        float *x = host_random(n), *w = host_random((size_t)inner), *b = host_random((size_t)inner);
+        float* y = (float*)malloc(n * sizeof(float));
+        float *dx = to_device(x, n), *dw = to_device(w, (size_t)inner), *db = to_device(b, (size_t)inner);
+        float* dy = to_device(NULL, n);
+        const size_t wsb = ln_forward_workspace_size(outer, inner);
+        void* dws = NULL;
+        if (!dx || !dw || !db || !dy || hipMalloc(&dws, wsb) != hipSuccess) return 2;
+        if (ln_forward_workspace_init(dws, wsb, st) != NORMFWD_OK) return 3;
+        for (int variant = 0; variant < 2; ++variant) {
+            if (ln_forward(dx, dw, db, dy, outer, inner, 1e-5f, dws, wsb, NULL, NULL, variant, st) != NORMFWD_OK) {
+                printf("ln_forward: %s\n", normfwd_last_error());
+                return 3;
+            }
+            hipStreamSynchronize(st);
+            hipMemcpy(y, dy, n * sizeof(float), hipMemcpyDeviceToHost);
+            double *xd = promote(x, n), *wd = promote(w, (size_t)inner), *bd = promote(b, (size_t)inner);
+            double* o = (double*)malloc(n * sizeof(double));
+            oracle_ln(xd, wd, bd, outer, inner, (double)1e-5f, o, NULL, NULL);
+            fails += compare(variant ? "ln_forward single" : "ln_forward split", y, o, n);
+            free(xd); free(wd); free(bd); free(o);
+        }
+        hipFree(dx); hipFree(dw); hipFree(db); hipFree(dy); hipFree(dws);
+        free(x); free(w); free(b); free(y);
+    }
+    /* GroupNorm + LeakyReLU + x2 [37, 8192], 512 groups */
+    {
+        const int64_t N = 37, C = 8192, G = 512;
+        const size_t n = (size_t)(N * C);
+        float *x = host_random(n), *g = host_random((size_t)C), *b = host_random((size_t)C);
+        float* y = (float*)malloc(n * sizeof(float));
+        float *dx = to_device(x, n), *dg = to_device(g, (size_t)C), *db = to_device(b, (size_t)C);
+        float* dy = to_device(NULL, n);
+        if (!dx || !dg || !db || !dy) return 2;
+        if (gn_lrelu_x2_forward(dx, dg, db, dy, N, C, G, 1e-5f, 0.01f, st) != NORMFWD_OK) return 3;
+        hipStreamSynchronize(st);
+        hipMemcpy(y, dy, n * sizeof(float), hipMemcpyDeviceToHost);
+        double *xd = promote(x, n), *gd = promote(g, (size_t)C), *bd = promote(b, (size_t)C);
+        double* o = (double*)malloc(n * sizeof(double));
+        oracle_gn_lrelu_x2(xd, gd, bd, N, C, G, (double)1e-5f, (double)0.01f, o, NULL, NULL);
+        fails += compare("gn_lrelu_x2_forward", y, o, n);
+        free(xd); free(gd); free(bd); free(o);
+        hipFree(dx); hipFree(dg); hipFree(db); hipFree(dy);
+        free(x); free(g); free(b); free(y);
+    }
+    /* RMSNorm over dim 1 of [3, 64, 5000] */
+    {
+        const int64_t B = 3, C = 64, S = 5000;
+        const size_t n = (size_t)(B * C * S);
+        float* x = host_random(n);
+        float* y = (float*)malloc(n * sizeof(float));
+        float *dx = to_device(x, n), *dy = to_device(NULL, n);
+        if (!dx || !dy) return 2;
+        if (rmsnorm_ch_forward(dx, dy, B, C, S, 1e-5f, st) != NORMFWD_OK) return 3;
+        hipStreamSynchronize(st);
+        hipMemcpy(y, dy, n * sizeof(float), hipMemcpyDeviceToHost);
+        double* xd = promote(x, n);
+        double* o = (double*)malloc(n * sizeof(double));
+        oracle_rms_ch(xd, B, C, S, (double)1e-5f, o, NULL);
+        fails += compare("rmsnorm_ch_forward", y, o, n);
+        free(xd); free(o);
+        hipFree(dx); hipFree(dy);
+        free(x); free(y);
+    }
+    hipStreamDestroy(st);
+    printf("run: %s\n", fails ? "FAIL" : "ok");
+    return fails ? 1 : 0;
+}
+
+int main(int argc, char** argv)
+{
+    if (argc > 1 && strcmp(argv[1], "run") == 0) return run();
+    return validate();
+}

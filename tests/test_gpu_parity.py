@@ -325,3 +325,39 @@ def test_prepared_calls_match_direct_calls():
         run()
         run()
         assert torch.equal(z1, z2)
+
+
+def test_captured_graph_replays_match_eager():
+    """The split LayerNorm, GN, RMS and fc+GN calls captured in one HIP graph (via torch's graph API on the
+    capturing stream) replay correctly several times, with eager work and synchronizations in between."""
+    _say("graph capture")
+    l = synth.make("ln_16x64x256x256", device="cuda", shape=(4, 70000), normalized_ndim=1, seed=31)
+    g = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(64, 8192), seed=32)
+    r = synth.make("rms_ch_112x64x512x512", device="cuda", shape=(2, 64, 4096), seed=33)
+    f = synth.make("fc_gn_1024x8192x8192", device="cuda", shape=(128, 256), hidden=512, seed=34)
+    ln_eager = nf.ln_forward(l["x"], l["weight"], l["bias"])
+    gn_eager = nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512)
+    rms_eager = nf.rmsnorm_ch_forward(r["x"])
+    fc_eager = nf.fc_gn_forward(f["x"], f["W"], f["b"], f["gamma"], f["beta"], 32)
+    outs = [torch.empty_like(t) for t in (ln_eager, gn_eager, rms_eager, fc_eager)]
+    _, ws = nf.alloc_workspace(nf.ln_forward_workspace_size(4, 70000), "cuda")
+    nf.ln_forward_workspace_init(ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            nf.ln_forward(l["x"], l["weight"], l["bias"], out=outs[0], workspace=ws)
+            nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512, out=outs[1])
+            nf.rmsnorm_ch_forward(r["x"], out=outs[2])
+            nf.fc_gn_forward(f["x"], f["W"], f["b"], f["gamma"], f["beta"], 32, out=outs[3])
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e, name in zip(outs, (ln_eager, gn_eager, rms_eager, fc_eager), ("ln", "gn", "rms", "fc")):
+            assert torch.equal(o, e), f"replay {rep}: {name} differs from eager"
