@@ -4,7 +4,9 @@ RMSNorm (plus fc -> GroupNorm) as hand-written HIP kernels for MI355X
 
 The Python functions here are a thin ctypes binding with the same names as
 the C entry points; they check arguments, allocate outputs with torch and
-enqueue the HIP kernels on the current stream.
+enqueue the HIP kernels on the current stream.  ``modules`` holds
+torch.nn.Module front ends with the constructor arguments of the layers
+the kernels replace.
 """
 from ._lib import (  # noqa: F401
     NormFwdError,
@@ -20,3 +22,4 @@ from ._lib import (  # noqa: F401
     prepare,
     rmsnorm_ch_forward,
 )
+from . import modules  # noqa: F401,E402

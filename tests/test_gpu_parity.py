@@ -361,3 +361,26 @@ def test_captured_graph_replays_match_eager():
         torch.cuda.synchronize()
         for o, e, name in zip(outs, (ln_eager, gn_eager, rms_eager, fc_eager), ("ln", "gn", "rms", "fc")):
             assert torch.equal(o, e), f"replay {rep}: {name} differs from eager"
+
+
+def test_modules_match_the_functions():
+    """The nn.Module front ends (the pages' constructor arguments) call the same kernels."""
+    _say("modules")
+    from normalization_ln_forward_amd import modules
+
+    x = synth.make("ln_16x64x256x256", device="cuda", shape=(2, 8, 16, 16), seed=41)["x"]
+    ln = modules.LayerNorm((8, 16, 16), eps=1e-5, device="cuda")
+    with torch.no_grad():
+        ln.weight.normal_(1.0, 0.1)
+        ln.bias.normal_(0.0, 0.1)
+    assert torch.equal(ln(x), nf.ln_forward(x, ln.weight.detach(), ln.bias.detach()))
+    _assert_close(_np(ln(x)), oracle.ln(_np(x), _np(ln.weight), _np(ln.bias)), what="module ln")
+    rms = modules.RMSNormChannel(8)
+    _assert_close(_np(rms(x)), oracle.rms_ch(_np(x)), what="module rms")
+    g = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(4, 256), seed=42)["x"]
+    gn = modules.GroupNormLeakyReLUx2(256, 16, device="cuda")
+    _assert_close(_np(gn(g)), oracle.gn_lrelu_x2(_np(g), None, None, 16), what="module gn")
+    fc = modules.FcGroupNormLeakyReLUx2(64, 128, 8, device="cuda")
+    xf = synth.make("fc_gn_1024x8192x8192", device="cuda", shape=(16, 64), hidden=128, seed=43)["x"]
+    ref = oracle.fc_gn_lrelu_x2(_np(xf), _np(fc.fc_weight), _np(fc.fc_bias), None, None, 8)
+    _assert_close(_np(fc(xf)), ref, rtol=RTOL_FC, what="module fc_gn")
