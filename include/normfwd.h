@@ -65,14 +65,19 @@ const char* normfwd_last_error(void);
  *   mean_out  [outer] fp32 or NULL: the sample mean, rounded to fp32
  *   rstd_out  [outer] fp32 or NULL: 1 / sqrt(var + eps), rounded to fp32
  *   workspace device buffer of at least ln_forward_workspace_size(outer,
- *             inner) bytes, 256-byte aligned, zeroed once by
- *             ln_forward_workspace_init() before its first use (each call
- *             leaves it ready for the next).  It holds per-workgroup partial
- *             moments, per-sample statistics and the arrival counters the
- *             kernels synchronize on.  One workspace must not be used by two
- *             calls that may run concurrently.
- *   variant   0 = split: a partial-moments kernel, a per-sample merge kernel
- *                 and a normalize kernel;
+ *             inner) bytes, 256-byte aligned, zeroed by
+ *             ln_forward_workspace_init() before its first use with a given
+ *             (outer, inner); each call leaves it ready for the next call of
+ *             the same (outer, inner).  Where its regions lie depends on the
+ *             shape, so before a workspace serves another shape it must be
+ *             zeroed again.  It holds per-workgroup partial moments,
+ *             per-sample statistics and the arrival counters the kernels
+ *             synchronize on.  One workspace must not be used by two calls
+ *             that may run concurrently.
+ *   variant   0 = split: a partial-moments kernel whose last workgroup to
+ *                 finish a sample merges that sample's partials (LN page,
+ *                 turn 6; nothing waits, so any grid size works), then a
+ *                 normalize kernel;
  *             1 = single kernel: one cooperative launch in which every
  *                 workgroup keeps its share of each sample in registers
  *                 between the moments pass and the normalize pass (x is
@@ -90,7 +95,8 @@ const char* normfwd_last_error(void);
 size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
 
 /* Zero `workspace` (enqueued on `stream`, as a kernel: safe inside a
- * captured HIP graph).  Required once before a workspace's first use. */
+ * captured HIP graph).  Required before a workspace's first use with each
+ * (outer, inner). */
 normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 normfwd_status ln_forward(const float* x, const float* weight, const float* bias, float* y,
@@ -99,8 +105,9 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
                           float* mean_out, float* rstd_out, int variant, void* stream);
 
 /* The split variant's two halves, for callers that want the statistics
- * alone or want to time the phases: ln_forward_stats runs the moments and
- * merge kernels and leaves per-sample (mean hi, mean lo, rstd) in the workspace;
+ * alone or want to time the phases: ln_forward_stats runs the moments
+ * kernel (with its merge) and leaves per-sample (mean hi, mean lo, rstd) in
+ * the workspace;
  * ln_forward_apply runs the normalize kernel from them.  Calling stats then
  * apply on one stream equals ln_forward(..., variant 0, ...). */
 normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, float eps,

@@ -169,14 +169,20 @@ def _ln_shape(x, normalized_ndim):
     return outer, inner
 
 
-def _ln_workspace(device, nbytes):
-    """A cached workspace per device, zeroed once by ln_forward_workspace_init."""
-    hit = _LN_WS.get(device)
-    if hit is None or hit[1].numel() < nbytes:
-        buf, view = alloc_workspace(nbytes, device)
+def _ln_workspace(device, outer, inner):
+    """A cached workspace per (device, outer, inner), zeroed once by ln_forward_workspace_init.
+
+    A workspace is left ready for the next call of the same shape only (its
+    counters sit at offsets that depend on the shape), so shapes do not share
+    one; the cache keeps every workspace alive for the life of the process,
+    which prepared calls that captured its address rely on."""
+    key = (device, int(outer), int(inner))
+    hit = _LN_WS.get(key)
+    if hit is None:
+        buf, view = alloc_workspace(ln_forward_workspace_size(outer, inner), device)
         ln_forward_workspace_init(view)
         hit = (buf, view)
-        _LN_WS[device] = hit
+        _LN_WS[key] = hit
     return hit[1]
 
 
@@ -200,8 +206,7 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
     _need(y, "out", dev)
     if y.shape != x.shape:
         raise ValueError("out must have x's shape")
-    nbytes = ln_forward_workspace_size(outer, inner)
-    ws = _ln_workspace(dev, nbytes) if workspace is None else workspace
+    ws = _ln_workspace(dev, outer, inner) if workspace is None else workspace
     _invoke("ln_forward", _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, float(eps), _ptr(ws),
                             ws.numel() * ws.element_size(), _ptr(mean_out), _ptr(rstd_out), int(variant),
                             _stream(dev))
@@ -215,7 +220,7 @@ def ln_forward_stats(x, eps=1e-5, normalized_ndim=None, workspace=None, mean_out
     outer, inner = _ln_shape(x, normalized_ndim)
     _opt(mean_out, "mean_out", outer, dev)
     _opt(rstd_out, "rstd_out", outer, dev)
-    ws = _ln_workspace(dev, ln_forward_workspace_size(outer, inner)) if workspace is None else workspace
+    ws = _ln_workspace(dev, outer, inner) if workspace is None else workspace
     _invoke("ln_forward_stats", _ptr(x), outer, inner, float(eps), _ptr(ws), ws.numel() * ws.element_size(),
                                   _ptr(mean_out), _ptr(rstd_out), _stream(dev))
     return ws

@@ -20,6 +20,7 @@ struct LnLayout {
     size_t off_ctrl;  // control block: generation, completion counter, error word
     size_t off_counter;  // single kernel: ring of arrival counters
     size_t off_flag;
+    size_t off_split_counter;  // split schedule: per-sample arrival counters (128-byte lines)
     size_t off_stats;
     size_t off_part;
     size_t total;

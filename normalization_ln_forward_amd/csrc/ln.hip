@@ -92,6 +92,11 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 #ifndef NORMFWD_LN_XCD_MAP
 #define NORMFWD_LN_XCD_MAP 1
 #endif
+// Split schedule: 1 = the last moments workgroup of a sample to finish
+// merges its partials (no separate merge launch), 0 = ln_merge_kernel.
+#ifndef NORMFWD_LN_FUSED_MERGE
+#define NORMFWD_LN_FUSED_MERGE 1
+#endif
 
 
 // uint32 words of the single kernel's arrival-counter ring (4 slots x 128
@@ -112,6 +117,8 @@ LnLayout ln_layout(int64_t outer, int64_t inner)
     off += align256(4 * (size_t)kLnCounterWords);
     L.off_flag = off;
     off += align256(4 * (size_t)outer);
+    L.off_split_counter = off;
+    off += align256(4 * (size_t)kCounterStride * (size_t)outer);
     L.off_stats = off;
     off += align256(16 * (size_t)outer);
     L.off_part = off;
@@ -292,11 +299,50 @@ __device__ __forceinline__ int64_t rows_owned_units(int64_t nu, int64_t p, int64
     return owns_last ? (c - 1) * kLnThreads + last_units : c * kLnThreads;
 }
 
+// Merge of a sample's P partials by one wave: lane l folds partials l,
+// l + 64, ... in order, then a fixed butterfly over the 64 lanes (shuffles,
+// no LDS or barriers); every lane ends with the merged (n, mean, M2).
+// COHERENT: the partials were written by other workgroups of the running
+// launch and are read with device-coherent loads.
+template <bool COHERENT>
+__device__ __forceinline__ void wave_merge(const Partial* pb, int64_t P, double& n, double& m, double& m2)
+{
+    n = 0.0;
+    m = 0.0;
+    m2 = 0.0;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t j = lane; j < P; j += kWave) {
+        if constexpr (COHERENT)
+            chan_merge(n, m, m2, dev_load(&pb[j].n), dev_load(&pb[j].mean), dev_load(&pb[j].m2));
+        else
+            chan_merge(n, m, m2, pb[j].n, pb[j].mean, pb[j].m2);
+    }
+#pragma unroll
+    for (int mask = 1; mask < kWave; mask <<= 1) {
+        const double on = __shfl_xor(n, mask), om = __shfl_xor(m, mask), om2 = __shfl_xor(m2, mask);
+        chan_merge(n, m, m2, on, om, om2);
+    }
+}
+
+__device__ __forceinline__ void store_stats(int64_t b, const f4& st, f4* stats, float* mean_out, float* rstd_out)
+{
+    stats[b] = st;
+    if (mean_out) mean_out[b] = st.x;
+    if (rstd_out) rstd_out[b] = st.z;
+}
+
 // Moments of workgroup p's rows of sample b, stored as the sample's p-th
-// partial (n, mean, M2).
+// partial (n, mean, M2).  With counters (one per sample, on its own
+// 128-byte line, zero on entry) the partial is published with the
+// device-coherent protocol above and counted; the workgroup that arrives
+// last merges the sample's partials with one wave, writes its statistics
+// and puts the counter back to zero for the next launch.  Nothing waits, so
+// the launch needs no co-residency.  Without counters the merge is left to
+// ln_merge_kernel.
 template <int VEC>
 __global__ void __launch_bounds__(kLnThreads)
-ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Partial* parts)
+ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Partial* parts, uint32_t* counters,
+                  float eps, f4* stats, float* mean_out, float* rstd_out)
 {
     using V = typename LnVec<VEC>::T;
     constexpr int U = NORMFWD_LN_PARTIAL_UNROLL;
@@ -334,31 +380,35 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
     }
     double s1 = 0.0, s2 = 0.0;
     block_moments(a1f, a2f, red, s1, s2);
-    if (threadIdx.x == 0) parts[b * P_cap + p] = make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2);
+    Partial* pb = parts + b * P_cap;
+    if (counters == nullptr) {
+        if (threadIdx.x == 0) pb[p] = make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2);
+        return;
+    }
+    __shared__ int last;
+    uint32_t* counter = counters + b * kCounterStride;
+    if (threadIdx.x == 0)
+        last = deliver_partial(&pb[p], make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2), counter, P);
+    __syncthreads();
+    if (!last || threadIdx.x >= kWave) return;
+    double n, m, m2;
+    wave_merge<true>(pb, P, n, m, m2);
+    if (threadIdx.x == 0) {
+        store_stats(b, finish_stats(n, m, m2, eps), stats, mean_out, rstd_out);
+        dev_store(counter, 0u);
+    }
 }
 
-// One wave per sample: lane l folds partials l, l + 64, ... in order, then a
-// fixed butterfly over the 64 lanes (shuffles, no LDS or barriers) merges
-// the lanes' results; lane 0 writes (mean hi, mean lo, rstd).
+// One wave per sample merges its partials (wave_merge); lane 0 writes
+// (mean hi, mean lo, rstd).
 __global__ void __launch_bounds__(kWave)
 ln_merge_kernel(const Partial* parts, int64_t P, int64_t P_cap, float eps, f4* stats, float* mean_out,
                 float* rstd_out)
 {
     const int64_t b = blockIdx.x;
-    const Partial* pb = parts + b * P_cap;
-    double n = 0.0, m = 0.0, m2 = 0.0;
-    for (int64_t j = threadIdx.x; j < P; j += kWave) chan_merge(n, m, m2, pb[j].n, pb[j].mean, pb[j].m2);
-#pragma unroll
-    for (int mask = 1; mask < kWave; mask <<= 1) {
-        const double on = __shfl_xor(n, mask), om = __shfl_xor(m, mask), om2 = __shfl_xor(m2, mask);
-        chan_merge(n, m, m2, on, om, om2);
-    }
-    if (threadIdx.x == 0) {
-        const f4 st = finish_stats(n, m, m2, eps);
-        stats[b] = st;
-        if (mean_out) mean_out[b] = st.x;
-        if (rstd_out) rstd_out[b] = st.z;
-    }
+    double n, m, m2;
+    wave_merge<false>(parts + b * P_cap, P, n, m, m2);
+    if (threadIdx.x == 0) store_stats(b, finish_stats(n, m, m2, eps), stats, mean_out, rstd_out);
 }
 
 // One row of 256 units per workgroup.  With xcd_map the workgroups one XCD
@@ -716,14 +766,17 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
     char* base = static_cast<char*>(ws);
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
+    uint32_t* counters = NORMFWD_LN_FUSED_MERGE ? reinterpret_cast<uint32_t*>(base + lay.off_split_counter) : nullptr;
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x);
     const dim3 grid((unsigned)(outer * lay.P));
     if (vec4)
-        hipLaunchKernelGGL(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts);
+        hipLaunchKernelGGL(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
+                           counters, eps, stats, mean_out, rstd_out);
     else
-        hipLaunchKernelGGL(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts);
+        hipLaunchKernelGGL(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
+                           counters, eps, stats, mean_out, rstd_out);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || counters) return e;
     hipLaunchKernelGGL(ln_merge_kernel, dim3((unsigned)outer), dim3(kWave), 0, st, parts, lay.P, lay.P_cap, eps,
                        stats, mean_out, rstd_out);
     return hipGetLastError();

@@ -9,3 +9,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library through its C ABI")
+
+
+def pytest_collection_modifyitems(session, config, items):
+    """Tests that drive the GPU from a child process run first.  The single-kernel LayerNorm uses a
+    cooperative launch; after the test process had made one, the child's cooperative launch on the same
+    GPU was refused (hipErrorIllegalState) on MI355X, so the child runs before any such launch here."""
+    child = [it for it in items if "test_c_abi.py" in it.nodeid]
+    rest = [it for it in items if "test_c_abi.py" not in it.nodeid]
+    items[:] = child + rest

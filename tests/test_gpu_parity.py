@@ -384,3 +384,27 @@ def test_modules_match_the_functions():
     xf = synth.make("fc_gn_1024x8192x8192", device="cuda", shape=(16, 64), hidden=128, seed=43)["x"]
     ref = oracle.fc_gn_lrelu_x2(_np(xf), _np(fc.fc_weight), _np(fc.fc_bias), None, None, 8)
     _assert_close(_np(fc(xf)), ref, rtol=RTOL_FC, what="module fc_gn")
+
+
+def test_ln_alternating_shapes_and_workspace_reinit():
+    """Calls of different shapes in turn (the binding keeps one workspace per shape) stay correct, and a
+    caller's workspace re-zeroed between shapes serves each of them."""
+    _say("ln alternating shapes")
+    shapes = [(6, 4097), (2, 40001), (16, 20000), (6, 4097), (3, 70000), (16, 20000), (2, 40001)]
+    data = {s: synth.make("ln_16x64x256x256", device="cuda", shape=s, normalized_ndim=1, seed=s[0] + s[1])
+            for s in set(shapes)}
+    refs = {s: oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"])) for s, d in data.items()}
+    for variant in (0, 1):
+        for s in shapes:
+            d = data[s]
+            _assert_close(_np(nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant)), refs[s],
+                          what=f"ln {s} variant {variant}")
+    big = max(nf.ln_forward_workspace_size(*s) for s in shapes)
+    _, ws = nf.alloc_workspace(big, "cuda")
+    for variant in (0, 1):
+        for s in shapes:
+            d = data[s]
+            nf.ln_forward_workspace_init(ws)
+            for _ in range(2):
+                y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
+                _assert_close(_np(y), refs[s], what=f"ln {s} variant {variant}, own workspace")
