@@ -50,6 +50,19 @@ const char* normfwd_status_string(normfwd_status status);
 /* Message describing the last non-OK return on this thread ("" if none). */
 const char* normfwd_last_error(void);
 
+/* Measurement hook.  Arms two hipEvent_t handles (created by the caller with
+ * timing enabled; either may be NULL) for the next kernel this library
+ * launches from the calling thread: that launch records its own start and
+ * end time into them (hipExtLaunchKernel), so hipEventElapsedTime gives the
+ * kernel's duration with no marker packets between kernels.  For an entry
+ * point that launches several kernels, the first one is timed (ln_forward
+ * variant 0: the moments kernel; use ln_forward_apply to time the normalize
+ * kernel).  The cooperative launch of ln_forward variant 1 cannot carry
+ * events; there they are recorded as markers just before and after it.  The
+ * events stay armed until a launch takes them or this is called again
+ * (NULL, NULL disarms).  Always NORMFWD_OK. */
+normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
+
 /* ------------------------------------------------------------------------
  * LayerNorm (LN page, turn 1: per sample, mean and population variance over
  * all elements of normalized_shape; y = (x - mean) / sqrt(var + eps) * weight

@@ -21,5 +21,6 @@ from ._lib import (  # noqa: F401
     ln_forward_workspace_size,
     prepare,
     rmsnorm_ch_forward,
+    time_next_kernel,
 )
 from . import modules  # noqa: F401,E402

@@ -31,6 +31,7 @@ _ST = ctypes.c_int
 SIGNATURES = {
     "normfwd_status_string": (ctypes.c_char_p, [_ST]),
     "normfwd_last_error": (ctypes.c_char_p, []),
+    "normfwd_time_next_kernel": (_ST, [_P, _P]),
     "ln_forward_workspace_size": (_SZ, [_I64, _I64]),
     "ln_forward_workspace_init": (_ST, [_P, _SZ, _P]),
     "ln_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P, _P, ctypes.c_int, _P]),
@@ -106,6 +107,22 @@ def prepare(fn, *args, **kwargs):
         return out
 
     return run
+
+
+def _event_handle(ev):
+    if ev is None:
+        return None
+    h = int(getattr(ev, "cuda_event", 0) or 0)
+    if h == 0:
+        raise ValueError("event has no HIP event yet: record it once (torch creates events lazily)")
+    return ctypes.c_void_p(h)
+
+
+def time_next_kernel(start, stop):
+    """Arm two torch.cuda.Event objects (timing enabled, each recorded once so that it exists) for the next
+    kernel the library launches from this thread; see normfwd_time_next_kernel in include/normfwd.h.
+    Inside prepare() the arming is recorded like any other call, so the prepared closure re-arms it."""
+    _invoke("normfwd_time_next_kernel", _event_handle(start), _event_handle(stop))
 
 
 def _ptr(t):

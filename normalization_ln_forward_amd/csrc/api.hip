@@ -64,7 +64,26 @@ normfwd_status check_ws(const void* ws, size_t bytes, size_t need, const char* w
 
 }  // namespace
 
+namespace normfwd {
+
+thread_local LaunchEvents g_armed{nullptr, nullptr};
+
+LaunchEvents take_launch_events()
+{
+    const LaunchEvents e = g_armed;
+    g_armed = LaunchEvents{nullptr, nullptr};
+    return e;
+}
+
+}  // namespace normfwd
+
 extern "C" {
+
+normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event)
+{
+    normfwd::g_armed = normfwd::LaunchEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+    return ok();
+}
 
 const char* normfwd_status_string(normfwd_status s)
 {

@@ -224,10 +224,10 @@ static hipError_t launch_gemm(bool vec, const float* x, const float* W, const fl
     using T = Tile<WM>;
     const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, T::kBM));
     if (vec)
-        hipLaunchKernelGGL((fc_mfma_kernel<true, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
+        launch_kernel((fc_mfma_kernel<true, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
                            (int)N, (int)C, (int)K, eps, slope);
     else
-        hipLaunchKernelGGL((fc_mfma_kernel<false, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
+        launch_kernel((fc_mfma_kernel<false, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
                            (int)N, (int)C, (int)K, eps, slope);
     return hipGetLastError();
 }

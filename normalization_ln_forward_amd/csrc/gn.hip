@@ -160,7 +160,7 @@ static hipError_t launch_fast(const float* x, const float* gamma, const float* b
     const int64_t tiles_per_row = ceil_div(C4, (int64_t)ITEMS * kWave);
     const int64_t n_tiles = N * tiles_per_row;
     const int64_t blocks = ceil_div(n_tiles, 4);
-    hipLaunchKernelGGL((gn_fast_kernel<L, ITEMS>), dim3((unsigned)blocks), dim3(256), 0, st, x, gamma, beta,
+    launch_kernel((gn_fast_kernel<L, ITEMS>), dim3((unsigned)blocks), dim3(256), 0, st, x, gamma, beta,
                        y, n_tiles, tiles_per_row, C4, (int)M, eps, slope);
     return hipGetLastError();
 }
@@ -208,10 +208,10 @@ hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* b
     }
     const int64_t total = N * G;
     if (M <= 32) {
-        hipLaunchKernelGGL(gn_lane_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, x, gamma,
+        launch_kernel(gn_lane_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, x, gamma,
                            beta, y, total, G, C, (int)M, eps, slope);
     } else {
-        hipLaunchKernelGGL(gn_wave_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, st, x, gamma,
+        launch_kernel(gn_wave_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, st, x, gamma,
                            beta, y, total, G, C, M, eps, slope);
     }
     return hipGetLastError();

@@ -1,11 +1,31 @@
 // Host-side launchers behind the C ABI (one translation unit per operation).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace normfwd {
+
+// Events armed by normfwd_time_next_kernel on the calling thread; taking
+// them disarms them.
+struct LaunchEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+LaunchEvents take_launch_events();
+
+// Every kernel launch of the library goes through here, so an armed pair of
+// events is recorded by the first launch after arming (hipExtLaunchKernel
+// stamps the kernel's own start and end; no marker packets are added).
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t st,
+                          Args... args)
+{
+    const LaunchEvents ev = take_launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev.start, ev.stop, 0u, args...);
+}
 
 hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
                          hipStream_t st);

@@ -770,14 +770,14 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x);
     const dim3 grid((unsigned)(outer * lay.P));
     if (vec4)
-        hipLaunchKernelGGL(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
+        launch_kernel(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
                            counters, eps, stats, mean_out, rstd_out);
     else
-        hipLaunchKernelGGL(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
+        launch_kernel(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
                            counters, eps, stats, mean_out, rstd_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || counters) return e;
-    hipLaunchKernelGGL(ln_merge_kernel, dim3((unsigned)outer), dim3(kWave), 0, st, parts, lay.P, lay.P_cap, eps,
+    launch_kernel(ln_merge_kernel, dim3((unsigned)outer), dim3(kWave), 0, st, parts, lay.P, lay.P_cap, eps,
                        stats, mean_out, rstd_out);
     return hipGetLastError();
 }
@@ -802,17 +802,17 @@ hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float
     if (NORMFWD_LN_NORM_MODE == 1 && ceil_div(nu, (int64_t)kLnThreads) >= 1024) {
         const dim3 g((unsigned)ceil_div(nu, (int64_t)kLnThreads));
         if (vec4)
-            hipLaunchKernelGGL(ln_normalize_rows_kernel<4>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
+            launch_kernel(ln_normalize_rows_kernel<4>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
         else
-            hipLaunchKernelGGL(ln_normalize_rows_kernel<1>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
+            launch_kernel(ln_normalize_rows_kernel<1>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)(outer * bps));
     if (vec4)
-        hipLaunchKernelGGL(ln_normalize_kernel<4>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
+        launch_kernel(ln_normalize_kernel<4>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
                            xcd_map, stats);
     else
-        hipLaunchKernelGGL(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
+        launch_kernel(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
                            xcd_map, stats);
     return hipGetLastError();
 }
@@ -825,7 +825,7 @@ bool launch_ln_rows(const float* x, const float* w, const float* b, float* y, in
     const dim3 grid((unsigned)outer);
 #define NORMFWD_ROWS(VEC, U)                                                                                    \
     if (nu <= (int64_t)kLnThreads * (U)) {                                                                      \
-        hipLaunchKernelGGL((ln_row_kernel<VEC, U>), grid, dim3(kLnThreads), 0, st, x, w, b, y, inner, eps, mean_out, \
+        launch_kernel((ln_row_kernel<VEC, U>), grid, dim3(kLnThreads), 0, st, x, w, b, y, inner, eps, mean_out, \
                            rstd_out);                                                                           \
         err = hipGetLastError();                                                                                \
         return true;                                                                                            \
@@ -921,8 +921,12 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     void* args[] = {(void*)&x, (void*)&w, (void*)&b, (void*)&y, (void*)&outer, (void*)&inner, (void*)&pcap,
                     (void*)&eps, (void*)&ctrl, (void*)&counters, (void*)&flag, (void*)&stats, (void*)&parts,
                     (void*)&mean_out, (void*)&rstd_out};
+    // a cooperative launch cannot carry events: armed ones bracket it as markers
+    const LaunchEvents ev = take_launch_events();
+    if (ev.start) (void)hipEventRecord(ev.start, st);
     err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(kLnThreads), args, lds, st);
     if (err == hipSuccess) err = hipGetLastError();
+    if (err == hipSuccess && ev.stop) err = hipEventRecord(ev.stop, st);
     return true;
 }
 

@@ -196,7 +196,7 @@ static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, in
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
         const int64_t off = b0 * C * S;
-        hipLaunchKernelGGL((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
+        launch_kernel((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
                            dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -213,7 +213,7 @@ static hipError_t launch_stream(const float* x, float* y, int64_t B, int64_t C, 
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
         const int64_t off = b0 * C * S;
-        hipLaunchKernelGGL((rms_ch_stream_kernel<VEC>), dim3((unsigned)(nb * tiles)), dim3(256), 0, st,
+        launch_kernel((rms_ch_stream_kernel<VEC>), dim3((unsigned)(nb * tiles)), dim3(256), 0, st,
                            x + off, y + off, (int)C, S, tiles, eps);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -408,3 +408,30 @@ def test_ln_alternating_shapes_and_workspace_reinit():
             for _ in range(2):
                 y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
                 _assert_close(_np(y), refs[s], what=f"ln {s} variant {variant}, own workspace")
+
+
+def test_time_next_kernel_stamps_one_launch():
+    """normfwd_time_next_kernel: the next launch (ordinary or cooperative) stamps the armed events, later
+    launches leave them alone, and the results are unchanged."""
+    _say("time_next_kernel")
+    g = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(256, 8192), seed=51)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    nf.time_next_kernel(a, b)
+    y = nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    assert 0.0 < ms < 100.0, ms
+    y2 = nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512)
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == ms, "a later launch re-stamped the events"
+    assert torch.equal(y, y2)
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=(4, 1 << 18), normalized_ndim=1, seed=52)
+    for variant in (0, 1):
+        nf.time_next_kernel(a, b)
+        out = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant)
+        torch.cuda.synchronize()
+        assert 0.0 < a.elapsed_time(b) < 100.0
+        _assert_close(_np(out), oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"])), what=f"ln {variant}")
