@@ -12,6 +12,7 @@ stream handles and device pointers are valid inside the library).
 """
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -73,13 +74,14 @@ def _check(status):
         raise NormFwdError(status, lib().normfwd_last_error().decode())
 
 
-_capture = None
+_tls = threading.local()  # .capture: list of recorded calls while prepare() runs on this thread
 
 
 def _invoke(name, *args):
-    """Call C entry point `name`, or record the marshalled call while prepare() runs."""
-    if _capture is not None:
-        _capture.append((name, args))
+    """Call C entry point `name`, or record the marshalled call while prepare() runs on this thread."""
+    capture = getattr(_tls, "capture", None)
+    if capture is not None:
+        capture.append((name, args))
         return
     _check(getattr(lib(), name)(*args))
 
@@ -90,12 +92,13 @@ def prepare(fn, *args, **kwargs):
     same stream) with no Python-side checks.  For tight launch loops, where
     per-call argument checking would otherwise cost more host time than the
     kernels take on the GPU."""
-    global _capture
-    _capture = []
+    if getattr(_tls, "capture", None) is not None:
+        raise RuntimeError("prepare() calls do not nest")
+    _tls.capture = []
     try:
         out = fn(*args, **kwargs)
     finally:
-        calls, _capture = _capture, None
+        calls, _tls.capture = _tls.capture, None
     handle = lib()
     bound = [(getattr(handle, name), a) for name, a in calls]
 

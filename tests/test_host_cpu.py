@@ -63,3 +63,29 @@ def test_oracle_does_not_depend_on_the_thread_count():
         env = dict(os.environ, OMP_NUM_THREADS=threads)
         outs.append(subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, check=True).stdout)
     assert outs[0] == outs[1] and len(outs[0]) > 0
+
+
+def test_prepare_records_only_its_own_thread_and_does_not_nest():
+    """prepare() records the C calls its function makes on the calling thread (other threads' calls go
+    straight to the library), re-issues them when run, and refuses to nest."""
+    import threading
+
+    from normalization_ln_forward_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    seen = []
+
+    def fn():
+        _lib._invoke("normfwd_time_next_kernel", None, None)
+        t = threading.Thread(target=lambda: seen.append(getattr(_lib._tls, "capture", None)))
+        t.start()
+        t.join()
+        return 7
+
+    run = _lib.prepare(fn)
+    assert seen == [None]
+    assert run() == 7 and run() == 7
+    with pytest.raises(RuntimeError):
+        _lib.prepare(lambda: _lib.prepare(fn))
+    assert getattr(_lib._tls, "capture", None) is None
