@@ -22,6 +22,12 @@
  *     lane writes it.  Partial overlap of inputs and outputs is undefined.
  *   - Results are run-to-run bitwise deterministic: no floating-point
  *     atomics, every reduction has a fixed order.
+ *   - Size limits (beyond them NORMFWD_ERR_UNSUPPORTED): at most 2^40
+ *     elements per tensor; LayerNorm outer <= 2^22 and inner <= 2^31;
+ *     GroupNorm C <= 2^30; RMSNorm C < 2^31 and S <= 2^26; fc N <= 2^23 and
+ *     C <= 2^24.  Problems whose grid would exceed the 32-bit work-item
+ *     count of one launch are enqueued as several launches of whole samples
+ *     (rows), in order, on the same stream.
  *   - Errors are returned, never thrown: arguments are validated before
  *     anything is enqueued, so a non-OK return from validation means nothing
  *     was launched.  normfwd_last_error() then describes the failure

@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <limits>
 
 #include "internal.hpp"
@@ -49,6 +50,7 @@ normfwd_status check_ln(const float* x, const float* y, int64_t outer, int64_t i
                                                (long long)outer, (long long)inner);
     if (outer > kMaxElems / inner) return fail(NORMFWD_ERR_UNSUPPORTED, "ln: outer*inner too large");
     if (outer > ((int64_t)1 << 22)) return fail(NORMFWD_ERR_UNSUPPORTED, "ln: outer > 2^22 samples");
+    if (inner > ((int64_t)1 << 31)) return fail(NORMFWD_ERR_UNSUPPORTED, "ln: inner > 2^31 elements per sample");
     if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "ln: eps must be >= 0");
     return ok();
 }
@@ -67,6 +69,19 @@ normfwd_status check_ws(const void* ws, size_t bytes, size_t need, const char* w
 namespace normfwd {
 
 thread_local LaunchEvents g_armed{nullptr, nullptr};
+
+int64_t max_grid_items()
+{
+    static const int64_t limit = [] {
+        int64_t lim = (int64_t)1 << 31;
+        if (const char* e = std::getenv("NORMFWD_MAX_GRID_ITEMS")) {
+            const long long v = std::atoll(e);
+            if (v >= 4096 && v < lim) lim = v;
+        }
+        return lim;
+    }();
+    return limit;
+}
 
 LaunchEvents take_launch_events()
 {
@@ -176,7 +191,8 @@ normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const flo
     if (C % num_groups != 0)
         return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: C (%lld) must be a multiple of num_groups (%lld)",
                     (long long)C, (long long)num_groups);
-    if (N > kMaxElems / C) return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: N*C too large");
+    if (N > kMaxElems / C || C > ((int64_t)1 << 30))
+        return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: N*C too large or C > 2^30");
     if (N * num_groups > ((int64_t)1 << 38))
         return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: too many groups");
     if (C / num_groups > std::numeric_limits<int>::max())

@@ -224,12 +224,10 @@ static hipError_t launch_gemm(bool vec, const float* x, const float* W, const fl
     using T = Tile<WM>;
     const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, T::kBM));
     if (vec)
-        launch_kernel((fc_mfma_kernel<true, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
-                           (int)N, (int)C, (int)K, eps, slope);
-    else
-        launch_kernel((fc_mfma_kernel<false, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
-                           (int)N, (int)C, (int)K, eps, slope);
-    return hipGetLastError();
+        return launch_kernel((fc_mfma_kernel<true, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta,
+                             out, (int)N, (int)C, (int)K, eps, slope);
+    return launch_kernel((fc_mfma_kernel<false, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
+                         (int)N, (int)C, (int)K, eps, slope);
 }
 
 hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const float* gamma, const float* beta,

@@ -158,11 +158,16 @@ static hipError_t launch_fast(const float* x, const float* gamma, const float* b
 {
     const int64_t C4 = C / 4;
     const int64_t tiles_per_row = ceil_div(C4, (int64_t)ITEMS * kWave);
-    const int64_t n_tiles = N * tiles_per_row;
-    const int64_t blocks = ceil_div(n_tiles, 4);
-    launch_kernel((gn_fast_kernel<L, ITEMS>), dim3((unsigned)blocks), dim3(256), 0, st, x, gamma, beta,
-                       y, n_tiles, tiles_per_row, C4, (int)M, eps, slope);
-    return hipGetLastError();
+    const int64_t per = samples_per_launch(tiles_per_row * kWave);
+    for (int64_t r0 = 0; r0 < N; r0 += per) {
+        const int64_t nr = std::min(per, N - r0);
+        const int64_t n_tiles = nr * tiles_per_row;
+        const hipError_t e = launch_kernel((gn_fast_kernel<L, ITEMS>), dim3((unsigned)ceil_div(n_tiles, 4)), dim3(256),
+                                           0, st, x + r0 * C, gamma, beta, y + r0 * C, n_tiles, tiles_per_row, C4,
+                                           (int)M, eps, slope);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int L>
@@ -206,15 +211,18 @@ hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* b
             default: break;
         }
     }
-    const int64_t total = N * G;
-    if (M <= 32) {
-        launch_kernel(gn_lane_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, x, gamma,
-                           beta, y, total, G, C, (int)M, eps, slope);
-    } else {
-        launch_kernel(gn_wave_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, st, x, gamma,
-                           beta, y, total, G, C, M, eps, slope);
+    // one lane (M <= 32) or one wave per (row, group)
+    const int64_t per = samples_per_launch(M <= 32 ? G : G * kWave);
+    for (int64_t r0 = 0; r0 < N; r0 += per) {
+        const int64_t total = std::min(per, N - r0) * G;
+        const hipError_t e =
+            M <= 32 ? launch_kernel(gn_lane_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, x + r0 * C,
+                                    gamma, beta, y + r0 * C, total, G, C, (int)M, eps, slope)
+                    : launch_kernel(gn_wave_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, st, x + r0 * C,
+                                    gamma, beta, y + r0 * C, total, G, C, M, eps, slope);
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace normfwd

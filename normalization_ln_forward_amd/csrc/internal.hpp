@@ -16,15 +16,36 @@ struct LaunchEvents {
 };
 LaunchEvents take_launch_events();
 
-// Every kernel launch of the library goes through here, so an armed pair of
-// events is recorded by the first launch after arming (hipExtLaunchKernel
-// stamps the kernel's own start and end; no marker packets are added).
+// Work-items per grid dimension of one launch are a 32-bit count, so every
+// launcher splits larger problems into batches of whole samples / rows of at
+// most max_grid_items() work-items (2^31; the environment variable
+// NORMFWD_MAX_GRID_ITEMS, read once, can lower it so that tests exercise the
+// batching on small tensors).
+int64_t max_grid_items();
+
+// Every kernel launch of the library goes through here: it refuses a grid
+// whose work-item count does not fit 32 bits (instead of letting it wrap),
+// and an armed pair of events is recorded by the first launch after arming
+// (hipExtLaunchKernel stamps the kernel's own start and end; no marker
+// packets are added).
 template <typename F, typename... Args>
-inline void launch_kernel(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t st,
-                          Args... args)
+inline hipError_t launch_kernel(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t st,
+                                Args... args)
 {
+    constexpr uint64_t kMax = 0xFFFFFFFFull;
+    if ((uint64_t)grid.x * block.x > kMax || (uint64_t)grid.y * block.y > kMax || (uint64_t)grid.z * block.z > kMax ||
+        grid.x == 0 || grid.y == 0 || grid.z == 0)
+        return hipErrorInvalidConfiguration;
     const LaunchEvents ev = take_launch_events();
     hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev.start, ev.stop, 0u, args...);
+    return hipGetLastError();
+}
+
+// Samples (rows) per launch when one sample needs `items_per_sample`
+// work-items: at least 1, at most what keeps a launch under max_grid_items().
+inline int64_t samples_per_launch(int64_t items_per_sample)
+{
+    return items_per_sample >= max_grid_items() ? 1 : max_grid_items() / items_per_sample;
 }
 
 hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,

@@ -768,18 +768,27 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
     uint32_t* counters = NORMFWD_LN_FUSED_MERGE ? reinterpret_cast<uint32_t*>(base + lay.off_split_counter) : nullptr;
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x);
-    const dim3 grid((unsigned)(outer * lay.P));
-    if (vec4)
-        launch_kernel(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
-                           counters, eps, stats, mean_out, rstd_out);
-    else
-        launch_kernel(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, x, inner, lay.P, lay.P_cap, parts,
-                           counters, eps, stats, mean_out, rstd_out);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || counters) return e;
-    launch_kernel(ln_merge_kernel, dim3((unsigned)outer), dim3(kWave), 0, st, parts, lay.P, lay.P_cap, eps,
-                       stats, mean_out, rstd_out);
-    return hipGetLastError();
+    const int64_t per = samples_per_launch(lay.P * kLnThreads);
+    for (int64_t b0 = 0; b0 < outer; b0 += per) {
+        const int64_t nb = std::min(per, outer - b0);
+        const float* xb = x + b0 * inner;
+        Partial* pb = parts + b0 * lay.P_cap;
+        uint32_t* cb = counters ? counters + b0 * kCounterStride : nullptr;
+        float* mb = mean_out ? mean_out + b0 : nullptr;
+        float* rb = rstd_out ? rstd_out + b0 : nullptr;
+        const dim3 grid((unsigned)(nb * lay.P));
+        hipError_t e = vec4 ? launch_kernel(ln_partial_kernel<4>, grid, dim3(kLnThreads), 0, st, xb, inner, lay.P,
+                                            lay.P_cap, pb, cb, eps, stats + b0, mb, rb)
+                            : launch_kernel(ln_partial_kernel<1>, grid, dim3(kLnThreads), 0, st, xb, inner, lay.P,
+                                            lay.P_cap, pb, cb, eps, stats + b0, mb, rb);
+        if (e != hipSuccess) return e;
+        if (!counters) {
+            e = launch_kernel(ln_merge_kernel, dim3((unsigned)nb), dim3(kWave), 0, st, pb, lay.P, lay.P_cap, eps,
+                              stats + b0, mb, rb);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float* y, int64_t outer,
@@ -799,22 +808,28 @@ hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float
     // The sample loop needs enough rows per sample to fill the GPU (each of
     // its workgroups walks all `outer` samples); short samples use one row
     // per workgroup.
-    if (NORMFWD_LN_NORM_MODE == 1 && ceil_div(nu, (int64_t)kLnThreads) >= 1024) {
-        const dim3 g((unsigned)ceil_div(nu, (int64_t)kLnThreads));
-        if (vec4)
-            launch_kernel(ln_normalize_rows_kernel<4>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
-        else
-            launch_kernel(ln_normalize_rows_kernel<1>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, stats);
-        return hipGetLastError();
+    const int64_t rows = ceil_div(nu, (int64_t)kLnThreads);
+    if (NORMFWD_LN_NORM_MODE == 1 && rows >= 1024 && rows * kLnThreads <= max_grid_items()) {
+        const dim3 g((unsigned)rows);
+        return vec4 ? launch_kernel(ln_normalize_rows_kernel<4>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer,
+                                    inner, stats)
+                    : launch_kernel(ln_normalize_rows_kernel<1>, g, dim3(kLnThreads), 0, st, x, w, b, y, outer,
+                                    inner, stats);
     }
-    const dim3 grid((unsigned)(outer * bps));
-    if (vec4)
-        launch_kernel(ln_normalize_kernel<4>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
-                           xcd_map, stats);
-    else
-        launch_kernel(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, x, w, b, y, outer, inner, bps,
-                           xcd_map, stats);
-    return hipGetLastError();
+    const int64_t per = samples_per_launch(bps * kLnThreads);
+    for (int64_t b0 = 0; b0 < outer; b0 += per) {
+        const int64_t nb = std::min(per, outer - b0);
+        const float* xb = x + b0 * inner;
+        float* yb = y + b0 * inner;
+        const int xm = nb > 1 ? xcd_map : 0;
+        const dim3 grid((unsigned)(nb * bps));
+        const hipError_t e = vec4 ? launch_kernel(ln_normalize_kernel<4>, grid, dim3(kLnThreads), 0, st, xb, w, b, yb,
+                                                  nb, inner, bps, xm, stats + b0)
+                                  : launch_kernel(ln_normalize_kernel<1>, grid, dim3(kLnThreads), 0, st, xb, w, b, yb,
+                                                  nb, inner, bps, xm, stats + b0);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 bool launch_ln_rows(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner, float eps,
@@ -822,13 +837,17 @@ bool launch_ln_rows(const float* x, const float* w, const float* b, float* y, in
 {
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
     const int64_t nu = vec4 ? inner / 4 : inner;
-    const dim3 grid((unsigned)outer);
-#define NORMFWD_ROWS(VEC, U)                                                                                    \
-    if (nu <= (int64_t)kLnThreads * (U)) {                                                                      \
-        launch_kernel((ln_row_kernel<VEC, U>), grid, dim3(kLnThreads), 0, st, x, w, b, y, inner, eps, mean_out, \
-                           rstd_out);                                                                           \
-        err = hipGetLastError();                                                                                \
-        return true;                                                                                            \
+    const int64_t per = samples_per_launch(kLnThreads);
+#define NORMFWD_ROWS(VEC, U)                                                                                     \
+    if (nu <= (int64_t)kLnThreads * (U)) {                                                                       \
+        for (int64_t b0 = 0; b0 < outer; b0 += per) {                                                            \
+            const int64_t nb = std::min(per, outer - b0);                                                        \
+            err = launch_kernel((ln_row_kernel<VEC, U>), dim3((unsigned)nb), dim3(kLnThreads), 0, st,            \
+                                x + b0 * inner, w, b, y + b0 * inner, inner, eps,                                \
+                                mean_out ? mean_out + b0 : nullptr, rstd_out ? rstd_out + b0 : nullptr);         \
+            if (err != hipSuccess) break;                                                                        \
+        }                                                                                                        \
+        return true;                                                                                             \
     }
     if (vec4) {
         NORMFWD_ROWS(4, 1)

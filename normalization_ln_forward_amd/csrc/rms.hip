@@ -181,9 +181,7 @@ rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, 
     }
 }
 
-// Blocks per launch stay below the 2^32 work-item limit of one grid dimension;
-// larger tensors are launched in batches of whole samples.
-constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
+// Larger tensors are launched in batches of whole samples (samples_per_launch).
 
 template <int CPW, int PPL, int VEC>
 static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
@@ -192,13 +190,12 @@ static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, in
     const int nwaves = (int)ceil_div(C, CPW);
     const int64_t tiles = ceil_div(S, (int64_t)kWave * PPL * VEC);
     const size_t lds = (size_t)nwaves * PPL * kWave * sizeof(typename VecOf<VEC>::T);
-    const int64_t per_launch = std::max<int64_t>(1, kMaxGridItems / (tiles * nwaves * kWave));
+    const int64_t per_launch = samples_per_launch(tiles * nwaves * kWave);
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
         const int64_t off = b0 * C * S;
-        launch_kernel((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
-                           dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = launch_kernel((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
+                                           dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -209,13 +206,12 @@ static hipError_t launch_stream(const float* x, float* y, int64_t B, int64_t C, 
                                 hipStream_t st)
 {
     const int64_t tiles = ceil_div(S, (int64_t)kWave * VEC);
-    const int64_t per_launch = std::max<int64_t>(1, kMaxGridItems / (tiles * 256));
+    const int64_t per_launch = samples_per_launch(tiles * 256);
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
         const int64_t off = b0 * C * S;
-        launch_kernel((rms_ch_stream_kernel<VEC>), dim3((unsigned)(nb * tiles)), dim3(256), 0, st,
-                           x + off, y + off, (int)C, S, tiles, eps);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = launch_kernel((rms_ch_stream_kernel<VEC>), dim3((unsigned)(nb * tiles)), dim3(256), 0,
+                                           st, x + off, y + off, (int)C, S, tiles, eps);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
