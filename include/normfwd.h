@@ -93,10 +93,12 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *             per-sample statistics and the arrival counters the kernels
  *             synchronize on.  One workspace must not be used by two calls
  *             that may run concurrently.
- *   variant   0 = split: a partial-moments kernel whose last workgroup to
- *                 finish a sample merges that sample's partials (LN page,
- *                 turn 6; nothing waits, so any grid size works), then a
- *                 normalize kernel;
+ *   variant   0 = split: a partial-moments kernel, a per-sample merge of
+ *                 the partials, then a normalize kernel.  With fewer than
+ *                 1024 moments workgroups the merge is done by the last
+ *                 workgroup of each sample to finish (LN page, turn 6;
+ *                 nothing waits, so any grid size works), otherwise by a
+ *                 merge kernel;
  *             1 = single kernel: one cooperative launch in which every
  *                 workgroup keeps its share of each sample in registers
  *                 between the moments pass and the normalize pass (x is
@@ -125,7 +127,7 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
 
 /* The split variant's two halves, for callers that want the statistics
  * alone or want to time the phases: ln_forward_stats runs the moments
- * kernel (with its merge) and leaves per-sample (mean hi, mean lo, rstd) in
+ * kernel and the merge and leaves per-sample (mean hi, mean lo, rstd) in
  * the workspace;
  * ln_forward_apply runs the normalize kernel from them.  Calling stats then
  * apply on one stream equals ln_forward(..., variant 0, ...). */

@@ -92,10 +92,15 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 #ifndef NORMFWD_LN_XCD_MAP
 #define NORMFWD_LN_XCD_MAP 1
 #endif
-// Split schedule: 1 = the last moments workgroup of a sample to finish
-// merges its partials (no separate merge launch), 0 = ln_merge_kernel.
-#ifndef NORMFWD_LN_FUSED_MERGE
-#define NORMFWD_LN_FUSED_MERGE 1
+// Split schedule: below NORMFWD_LN_FUSE_BELOW moments workgroups in all,
+// the last workgroup of a sample to finish merges its partials (no separate
+// merge launch); from there on ln_merge_kernel does (0 = always the kernel).
+// Measured on MI355X: fusing saves 0.6-1.2 us at 64-512 workgroups
+// ([16, 65536], [8, 2^20]), is even at 1024 and costs 0.6-1.5 us at 1024-4096
+// ([4, 2^22], [16, 2^22]), where the atomics of thousands of workgroups
+// outweigh the saved launch.
+#ifndef NORMFWD_LN_FUSE_BELOW
+#define NORMFWD_LN_FUSE_BELOW 1024
 #endif
 
 
@@ -311,11 +316,30 @@ __device__ __forceinline__ void wave_merge(const Partial* pb, int64_t P, double&
     m = 0.0;
     m2 = 0.0;
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t j = lane; j < P; j += kWave) {
-        if constexpr (COHERENT)
-            chan_merge(n, m, m2, dev_load(&pb[j].n), dev_load(&pb[j].mean), dev_load(&pb[j].m2));
-        else
-            chan_merge(n, m, m2, pb[j].n, pb[j].mean, pb[j].m2);
+    // kBatch partials per lane are loaded before any is merged, so their
+    // loads are in flight together (the merge order is unchanged: lane l
+    // folds l, l + 64, l + 128, ...).  Out-of-range slots read slot l and
+    // count as empty.
+    constexpr int kBatch = 4;
+    for (int64_t j0 = lane; j0 < P; j0 += kBatch * kWave) {
+        double bn[kBatch], bm[kBatch], bm2[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t j = j0 + (int64_t)u * kWave;
+            const Partial* q = pb + (j < P ? j : j0);
+            if constexpr (COHERENT) {
+                bn[u] = dev_load(&q->n);
+                bm[u] = dev_load(&q->mean);
+                bm2[u] = dev_load(&q->m2);
+            } else {
+                bn[u] = q->n;
+                bm[u] = q->mean;
+                bm2[u] = q->m2;
+            }
+            if (j >= P) bn[u] = 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) chan_merge(n, m, m2, bn[u], bm[u], bm2[u]);
     }
 #pragma unroll
     for (int mask = 1; mask < kWave; mask <<= 1) {
@@ -766,7 +790,8 @@ hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float e
     char* base = static_cast<char*>(ws);
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
-    uint32_t* counters = NORMFWD_LN_FUSED_MERGE ? reinterpret_cast<uint32_t*>(base + lay.off_split_counter) : nullptr;
+    uint32_t* counters =
+        outer * lay.P < NORMFWD_LN_FUSE_BELOW ? reinterpret_cast<uint32_t*>(base + lay.off_split_counter) : nullptr;
     const bool vec4 = (inner % 4 == 0) && is_aligned16(x);
     const int64_t per = samples_per_launch(lay.P * kLnThreads);
     for (int64_t b0 = 0; b0 < outer; b0 += per) {
