@@ -72,8 +72,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--variant", type=int, default=0, choices=[0, 1],
-                    help="LN schedule for the headline: 0 = split (default, fastest measured), 1 = single kernel")
+    ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
+                    help="LN schedule for the headline: 0 = split (default, fastest measured), 1 = single kernel "
+                         "(control wave, tagged exchange), 2 = single kernel, last workgroup merges")
     ap.add_argument("--rotate", type=int, default=4, help="LN buffer sets rotated through (>=1)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,12 +119,13 @@ def main():
     nf.ln_forward_workspace_init(ws)
     stream = torch.cuda.current_stream(dev)
     # argument checking and marshalling happen once per buffer set, outside the timed region
-    if variant == 1:
-        steps = [nf.prepare(nf.ln_forward, xs[r], w, b, variant=1, out=ys[r], workspace=ws) for r in range(R)]
+    if variant != 0:
+        steps = [nf.prepare(nf.ln_forward, xs[r], w, b, variant=variant, out=ys[r], workspace=ws) for r in range(R)]
         t = time_launches(torch, stream, lambda i: steps[i % R](), args.steps, args.warmup)
         ms_per_step = t["wall_ms"]
         # the single-read kernel moves x once: its own algorithmic bytes are the normalize pass's
-        dom_kernel, dom_bytes, avg_ms = "ln_single_hold_kernel", LN_NORMALIZE_BYTES, t["avg_ms"]
+        dom_kernel = "ln_single_ctl_kernel" if variant == 1 else "ln_single_hold_kernel"
+        dom_bytes, avg_ms = LN_NORMALIZE_BYTES, t["avg_ms"]
     else:
         # the step is the two halves of the split schedule
         stats = [nf.prepare(nf.ln_forward_stats, xs[r], workspace=ws) for r in range(R)]
@@ -182,7 +184,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "config": {"workload": "ln_16x64x256x256", "shape": list(LN_SHAPE), "normalized_shape": [64, 256, 256],
-                   "variant": ["split", "single"][variant], "rotate_buffer_sets": R,
+                   "variant": ["split", "single", "single_last_block"][variant], "rotate_buffer_sets": R,
                    "algorithmic_bytes": LN_BYTES, "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -267,12 +269,12 @@ def per_kernel_table(torch, nf, synth, dev, stream, args, log):
         y = torch.empty_like(d["x"])
         x2 = synth.make(name, device=dev, seed=4000)["x"]
         y2 = torch.empty_like(d["x"])
-        for variant in (0, 1):
+        for variant in (0, 1, 2):
             log(f"[bench] {name} variant={variant}")
             calls = [nf.prepare(nf.ln_forward, xx, d["weight"], d["bias"], variant=variant, out=yy)
                      for xx, yy in ((d["x"], y), (x2, y2))]
             t = time_launches(torch, stream, lambda i: calls[i % 2](), steps, warm)
-            out[f"{name}/{['split', 'single'][variant]}"] = _entry(t, LN_BYTES)
+            out[f"{name}/{['split', 'single', 'single_last_block'][variant]}"] = _entry(t, LN_BYTES)
         del d, y, x2, y2
         torch.cuda.empty_cache()
 

@@ -102,16 +102,24 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *             1 = single kernel: one cooperative launch in which every
  *                 workgroup keeps its share of each sample in registers
  *                 between the moments pass and the normalize pass (x is
- *                 read from HBM once) and waits for the sample's merged
- *                 statistics; shapes it cannot hold (inner % 4 != 0,
- *                 unaligned pointers, more rows than co-resident
- *                 workgroups can keep) run the split schedule instead.
+ *                 read from HBM once).  A control wave per workgroup
+ *                 exchanges the workgroups' moments of each sample through
+ *                 generation-tagged words (no atomics) while the data waves
+ *                 stream the next samples;
+ *             2 = single kernel in which the last workgroup to deliver a
+ *                 sample's partial merges it and announces the statistics
+ *                 with a flag (LN page, turn 6: last-block-done), the others
+ *                 waiting for that flag.
+ *             Shapes a single kernel cannot hold (inner % 4 != 0, unaligned
+ *             pointers, more rows than co-resident workgroups can keep) run
+ *             the split schedule instead.
  *
  * Statistics are exact to about 1e-7 relative even when |mean| >> std: the
  * partial moments are accumulated around a per-sample shift (the sample's
- * first element), handed between workgroups in fp64, merged with Chan's
- * pairwise update in a fixed order, and the mean is applied as an fp32
- * hi + lo pair.
+ * first element), handed between workgroups in fp64, merged in a fixed
+ * order (Chan's pairwise update; variant 1 adds the workgroups' shifted
+ * sums, the same merge when every part has the same shift), and the mean is
+ * applied as an fp32 hi + lo pair.
  * ---------------------------------------------------------------------- */
 size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
 

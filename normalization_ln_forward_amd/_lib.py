@@ -211,7 +211,8 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
     """LayerNorm over the trailing ``normalized_ndim`` dims (default: all but dim 0).
 
     ``variant`` 0 = split (moments kernel + normalize kernel), 1 = single
-    cooperative kernel.  A caller-provided ``workspace`` must have been passed
+    cooperative kernel (control wave, tagged exchange), 2 = single cooperative
+    kernel in which the last workgroup of each sample merges it.  A caller-provided ``workspace`` must have been passed
     through ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if
     None).
     """

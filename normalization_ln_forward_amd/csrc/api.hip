@@ -163,7 +163,7 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
 {
     normfwd_status s = check_ln(x, y, outer, inner, eps);
     if (s != NORMFWD_OK) return s;
-    if (variant != 0 && variant != 1) return fail(NORMFWD_ERR_INVALID, "ln_forward: variant must be 0 or 1");
+    if (variant < 0 || variant > 2) return fail(NORMFWD_ERR_INVALID, "ln_forward: variant must be 0, 1 or 2");
     const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
     s = check_ws(workspace, workspace_bytes, lay.total, "ln_forward");
     if (s != NORMFWD_OK) return s;
@@ -172,9 +172,9 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
     hipError_t re = hipSuccess;
     if (normfwd::launch_ln_rows(x, weight, bias, y, outer, inner, eps, mean_out, rstd_out, st, re))
         return hip_status(re, "ln_forward (one workgroup per sample) launch");
-    if (variant == 1)
+    if (variant != 0)
         return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
-                                                    rstd_out, st),
+                                                    rstd_out, variant, st),
                           "ln_forward (single kernel) launch");
     hipError_t e = normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out, st);
     if (e != hipSuccess) return hip_status(e, "ln_forward stats launch");

@@ -309,7 +309,7 @@ __device__ __forceinline__ int64_t rows_owned_units(int64_t nu, int64_t p, int64
 // no LDS or barriers); every lane ends with the merged (n, mean, M2).
 // COHERENT: the partials were written by other workgroups of the running
 // launch and are read with device-coherent loads.
-template <bool COHERENT>
+template <bool COHERENT, int kBatch = 4>
 __device__ __forceinline__ void wave_merge(const Partial* pb, int64_t P, double& n, double& m, double& m2)
 {
     n = 0.0;
@@ -320,7 +320,6 @@ __device__ __forceinline__ void wave_merge(const Partial* pb, int64_t P, double&
     // loads are in flight together (the merge order is unchanged: lane l
     // folds l, l + 64, l + 128, ...).  Out-of-range slots read slot l and
     // count as empty.
-    constexpr int kBatch = 4;
     for (int64_t j0 = lane; j0 < P; j0 += kBatch * kWave) {
         double bn[kBatch], bm[kBatch], bm2[kBatch];
 #pragma unroll
@@ -766,6 +765,240 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
     }
 }
 
+// Generation-tagged fp64 words: the low 8 bits of the mantissa carry the
+// launch generation, so a reader can tell this launch's value from the one a
+// previous launch left in the same slot without a separate flag (an aligned
+// 8-byte store is seen whole or not at all).  The reader clears the tag
+// before use; the 2^-44 relative change is the same in every launch.
+__device__ __forceinline__ double tag_word(double v, uint32_t tag)
+{
+    return __longlong_as_double((long long)(((uint64_t)__double_as_longlong(v) & ~0xFFull) | (tag & 0xFFu)));
+}
+__device__ __forceinline__ bool has_tag(double v, uint32_t tag)
+{
+    return ((uint64_t)__double_as_longlong(v) & 0xFFull) == (tag & 0xFFu);
+}
+__device__ __forceinline__ double untag(double v)
+{
+    return __longlong_as_double((long long)((uint64_t)__double_as_longlong(v) & ~0xFFull));
+}
+
+// Single-read schedule with a control wave.  DW data waves hold the
+// workgroup's rows as above (rows are DW * 64 float4 wide here); one more
+// wave holds no data and runs the cross-workgroup exchange, so that the
+// data waves never wait on another workgroup and their loads stay in
+// flight (a wave's memory counter retires in issue order, so a wave that
+// polled memory would also wait for its own prefetch).  One workgroup
+// barrier per sample:
+//   data waves, iteration t:  issue the loads of sample t+1; moments of
+//       sample t -> per-wave sums in LDS; barrier t; normalize and store
+//       sample t-1 with the statistics the control wave left in LDS.
+//   control wave, after barrier t:  publish this workgroup's sums of
+//       d = x - K and d^2 (K the sample's first element, shared by every
+//       workgroup) as two generation-tagged words; read all P workgroups'
+//       sums until every tag is current, add them in a fixed order (every
+//       workgroup computes the same statistics: mean = K + S1/N, sum of
+//       squared deviations = S2 - S1^2/N, the shifted form of the pairwise
+//       merge when all parts share one shift) and leave the statistics in
+//       LDS before barrier t+1.
+// No atomics, counters or flags: the exchange for sample t overlaps the
+// data waves' normalize of t-1 and their loads and moments of t+1.  (The
+// last-workgroup-merges protocol of ln_single_hold_kernel measured slower
+// here: its chain of arrival atomic, merge and flag is longer than one
+// sample's streaming time.)
+template <int F4PT, int DW>
+__global__ void __launch_bounds__((DW + 1) * kWave)
+ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
+                     int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats, Partial* parts, float* mean_out,
+                     float* rstd_out)
+{
+    constexpr int RW = DW * kWave;  // row width in float4 = data threads
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    __shared__ double red[2][2 * DW];  // [sample parity][wave]: sum d, sum d^2
+    __shared__ f4 s_stats[2];          // [sample parity]: mean hi, mean lo, rstd
+    f4* w_s = reinterpret_cast<f4*>(smem_raw);
+    f4* b_s = w_s + (w ? F4PT * RW : 0);
+    const int64_t P = gridDim.x;
+    const int64_t p = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int64_t nv = inner / 4;
+
+    if (tid >= RW) {
+        // ---- control wave
+        const uint32_t target = dev_load(&ctrl->gen) + 1u;
+        float K = x[0];
+        __syncthreads();  // prologue: w/b in LDS
+        for (int64_t t = 0; t <= outer; ++t) {
+            __syncthreads();  // barrier t: the wave sums of sample t are in LDS
+            if (t == outer) break;
+            const float K_next = x[(t + 1 < outer ? t + 1 : t) * inner];
+            // this workgroup's sums of d = x - K and d^2 over its elements of sample t
+            Partial* pb = parts + t * P_cap;
+            if (lane == 0) {
+                const double* rd = red[t & 1];
+                double s1 = rd[0], s2 = rd[1];
+                for (int wv = 1; wv < DW; ++wv) {
+                    s1 += rd[2 * wv];
+                    s2 += rd[2 * wv + 1];
+                }
+                dev_store(&pb[p].n, tag_word(s1, target));
+                dev_store(&pb[p].mean, tag_word(s2, target));
+            }
+            // gather every workgroup's sums (lane l: workgroups l, l + 64, ...),
+            // retrying until every tag is current, then a fixed-order sum
+            double S1 = 0.0, S2 = 0.0;
+            for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
+                double a[4], b2[4];
+                uint32_t spins = 0;
+                for (;;) {
+                    bool ok = true;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int64_t j = j0 + lane + (int64_t)u * kWave;
+                        const Partial* q = pb + (j < P ? j : p);
+                        a[u] = dev_load(&q->n);
+                        b2[u] = dev_load(&q->mean);
+                        ok = ok && has_tag(a[u], target) && has_tag(b2[u], target);
+                    }
+                    if (__all(ok)) break;
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > kSpinLimit) {
+                        if (lane == 0) dev_store(&ctrl->error, 1u);
+                        break;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (j0 + lane + (int64_t)u * kWave < P) {
+                        S1 += untag(a[u]);
+                        S2 += untag(b2[u]);
+                    }
+                }
+            }
+            S1 = wave_sum(S1);
+            S2 = wave_sum(S2);
+            if (lane == 0) {
+                // mean = K + S1/N; sum of squared deviations = S2 - S1^2/N
+                const double N = (double)inner;
+                const double md = S1 / N;
+                const f4 st = finish_stats(N, (double)K + md, fmax(S2 - S1 * md, 0.0), eps);
+                s_stats[t & 1] = st;
+                if (p == 0) {
+                    stats[t] = st;
+                    if (mean_out) mean_out[t] = st.x;
+                    if (rstd_out) rstd_out[t] = st.z;
+                }
+            }
+            K = K_next;
+        }
+        // completion: the last workgroup out advances the generation
+        if (lane == 0) {
+            vmem_drain();
+            if (__hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(P - 1)) {
+                dev_store(&ctrl->done, 0u);
+                vmem_drain();
+                dev_store(&ctrl->gen, target);
+            }
+        }
+        return;
+    }
+
+    // ---- data waves.  Element k of this thread is float4 index(k) of row
+    // p + k P (< 2^32), present iff index(k) < nv.  Loads are issued
+    // unconditionally, clamped to a valid address and masked where used: the
+    // memory counter retires in issue order, so with a fixed number of loads
+    // per iteration a wave can wait for one tile while the next is in flight.
+    uint32_t off0 = (uint32_t)p * RW + (uint32_t)tid;
+    const uint32_t stride = (uint32_t)P * RW;
+    auto index = [&](int k) -> uint32_t { return off0 + (uint32_t)k * stride; };
+    auto valid = [&](int k) -> bool { return (int64_t)index(k) < nv; };
+    const uint32_t last_unit = (uint32_t)(nv - 1);
+    auto addr = [&](int k) -> uint32_t { return std::min(index(k), last_unit); };
+    f4 ta[F4PT], tb[F4PT], tc[F4PT];  // three x tiles whose roles rotate
+    float ka, kb, kc;                  // the matching per-sample shifts
+    for (int which = 0; which < 2; ++which) {
+        // weight / bias rows -> LDS: all loads in flight first, then the LDS stores
+        const float* src = which == 0 ? w : bias;
+        f4* dst = which == 0 ? w_s : b_s;
+        if (!src) continue;
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) ta[k] = reinterpret_cast<const f4*>(src)[addr(k)];
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) dst[k * RW + tid] = ta[k];
+    }
+    // samples 0 and 1 in flight (sample 0 again if there is no sample 1)
+    {
+        const int64_t t1 = outer > 1 ? 1 : 0;
+        const f4* x0 = reinterpret_cast<const f4*>(x);
+        const f4* x1 = reinterpret_cast<const f4*>(x + t1 * inner);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) tb[k] = x0[addr(k)];
+        kb = x[0];
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) tc[k] = x1[addr(k)];
+        kc = x[t1 * inner];
+        ka = kb;
+    }
+    __syncthreads();  // prologue: w/b in LDS
+
+    // One iteration: Cv holds sample t (shift Kc, loaded two iterations ago),
+    // the third tile sample t+1 (in flight), Pv sample t-1; once Pv is
+    // normalized it receives sample t+2 (shift Kp; past the last sample it
+    // re-reads the last one).  So two samples' loads are in flight while a
+    // third is reduced.  The loop unrolls three iterations with the tiles'
+    // roles rotated, so no tile is ever copied: a copy would wait for the
+    // loads that fill it.
+    auto step = [&](int64_t t, f4 (&Pv)[F4PT], f4 (&Cv)[F4PT], float& Kp, float Kc)
+                    __attribute__((always_inline)) {
+        // the per-row offsets are recomputed in every iteration instead of
+        // being kept live across the loop (registers hold three x tiles)
+        asm volatile("" : "+v"(off0));
+        if (t < outer) {
+            f4 a1 = f4(0.0f), a2 = f4(0.0f);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) {
+                const f4 d = valid(k) ? Cv[k] - Kc : f4(0.0f);
+                a1 += d;
+                a2 += d * d;
+            }
+            const double t1 = wave_sum(((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w));
+            const double t2 = wave_sum(((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w));
+            if (lane == 0) {
+                red[t & 1][2 * (tid / kWave)] = t1;
+                red[t & 1][2 * (tid / kWave) + 1] = t2;
+            }
+        }
+        __syncthreads();  // barrier t: sample t-1's statistics are in LDS
+        if (t >= 1) {
+            const f4 st = s_stats[(t - 1) & 1];
+            f4* y4 = reinterpret_cast<f4*>(y + (t - 1) * inner);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) {
+                if (valid(k)) {
+                    const f4 tt = ((Pv[k] - st.x) - st.y) * st.z;
+                    const f4 wv = w ? w_s[k * RW + tid] : f4(1.0f);
+                    const f4 bv = bias ? b_s[k * RW + tid] : f4(0.0f);
+                    st_nt(tt * wv + bv, y4 + index(k));
+                }
+            }
+        }
+        const int64_t tn = t + 2 < outer ? t + 2 : outer - 1;
+        const f4* xn = reinterpret_cast<const f4*>(x + tn * inner);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) Pv[k] = xn[addr(k)];
+        Kp = x[tn * inner];
+    };
+    for (int64_t t = 0; t <= outer; t += 3) {
+        step(t, ta, tb, ka, kb);
+        if (t + 1 > outer) break;
+        step(t + 1, tb, tc, kb, kc);
+        if (t + 2 > outer) break;
+        step(t + 2, tc, ta, kc, ka);
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 
 __global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int64_t n)
@@ -914,12 +1147,13 @@ static bool device_info(DeviceInfo& out)
 
 // Co-resident workgroups of `fn` with `lds` bytes of dynamic LDS on this
 // device (queried once per device, kernel and LDS size).
-static int coresident(const void* fn, size_t lds)
+static int coresident(const void* fn, size_t lds, int threads)
 {
     struct Entry {
         int dev;
         const void* fn;
         size_t lds;
+        int threads;
         int cap;
     };
     static std::mutex mu;
@@ -931,15 +1165,16 @@ static int coresident(const void* fn, size_t lds)
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < n_cache; ++i)
-        if (cache[i].dev == dev && cache[i].fn == fn && cache[i].lds == lds) return cache[i].cap;
+        if (cache[i].dev == dev && cache[i].fn == fn && cache[i].lds == lds && cache[i].threads == threads)
+            return cache[i].cap;
     int cap = 0;
     if (lds == 0 || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess) {
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kLnThreads, lds) == hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) == hipSuccess)
             cap = d.cus * per_cu;
     }
     (void)hipGetLastError();
-    if (n_cache < 64) cache[n_cache++] = Entry{dev, fn, lds, cap};
+    if (n_cache < 64) cache[n_cache++] = Entry{dev, fn, lds, threads, cap};
     return cap;
 }
 
@@ -947,28 +1182,38 @@ static int coresident(const void* fn, size_t lds)
 #define NORMFWD_LN_HOLD_F4PT 16
 #endif
 
-template <int F4PT>
+
+template <int F4PT, int DW>
 static bool try_launch_hold(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner,
                             float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats, Partial* parts,
                             int64_t P_cap, float* mean_out, float* rstd_out, hipStream_t st, hipError_t& err)
 {
     DeviceInfo d;
     if (!device_info(d)) return false;
-    const int64_t rows = ceil_div(inner / 4, (int64_t)kLnThreads);
+    // DW == 0: ln_single_hold_kernel (rows of kLnThreads float4, every wave
+    // does both jobs); DW > 0: ln_single_ctl_kernel with DW data waves
+    const int64_t rw = DW == 0 ? kLnThreads : DW * kWave;
+    const int64_t rows = ceil_div(inner / 4, rw);
     const int64_t P = ceil_div(rows, (int64_t)F4PT);
     if (P > P_cap) return false;
-    const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * kLnThreads * sizeof(f4);
+    const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * rw * sizeof(f4);
     if (lds + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
-    const void* fn = reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>);
-    if (coresident(fn, lds) < P) return false;
+    const void* fn = DW == 0 ? reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>)
+                             : reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW == 0 ? 1 : DW>);
+    const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
+    if (coresident(fn, lds, threads) < P) return false;
     int64_t pcap = P_cap;
-    void* args[] = {(void*)&x, (void*)&w, (void*)&b, (void*)&y, (void*)&outer, (void*)&inner, (void*)&pcap,
-                    (void*)&eps, (void*)&ctrl, (void*)&counters, (void*)&flag, (void*)&stats, (void*)&parts,
-                    (void*)&mean_out, (void*)&rstd_out};
+    void* args_hold[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
+                         (void*)&inner, (void*)&pcap,    (void*)&eps,  (void*)&ctrl,  (void*)&counters,
+                         (void*)&flag,  (void*)&stats,   (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
+    void* args_ctl[] = {(void*)&x,    (void*)&w,     (void*)&b,     (void*)&y,        (void*)&outer,   (void*)&inner,
+                        (void*)&pcap, (void*)&eps,   (void*)&ctrl,  (void*)&stats,    (void*)&parts,
+                        (void*)&mean_out, (void*)&rstd_out};
+    void** args = DW == 0 ? args_hold : args_ctl;
     // a cooperative launch cannot carry events: armed ones bracket it as markers
     const LaunchEvents ev = take_launch_events();
     if (ev.start) (void)hipEventRecord(ev.start, st);
-    err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(kLnThreads), args, lds, st);
+    err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
     if (err == hipSuccess) err = hipGetLastError();
     if (err == hipSuccess && ev.stop) err = hipEventRecord(ev.stop, st);
     return true;
@@ -981,7 +1226,7 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
 
 hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                             int64_t inner, float eps, void* ws, const LnLayout& lay, float* mean_out,
-                            float* rstd_out, hipStream_t st)
+                            float* rstd_out, int protocol, hipStream_t st)
 {
     char* base = static_cast<char*>(ws);
     LnCtrl* ctrl = reinterpret_cast<LnCtrl*>(base + lay.off_ctrl);
@@ -990,21 +1235,27 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
 
-    // The single-read kernel, when a co-resident grid can hold every
-    // sample's chunks (tuned register tile first, then the others).
+    // A single-read kernel, when a co-resident grid can hold every sample's
+    // rows (tuned tile first, then the others).
     if (ln_single_supported(inner, x, w, b, y)) {
         hipError_t err = hipSuccess;
-#define NORMFWD_TRY_HOLD(F)                                                                                      \
-    if (try_launch_hold<F>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, lay.P_cap, mean_out, \
-                           rstd_out, st, err))                                                                   \
+#define NORMFWD_TRY_HOLD(F, DW)                                                                                \
+    if (try_launch_hold<F, DW>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, lay.P_cap,      \
+                               mean_out, rstd_out, st, err))                                                      \
         return err;
-        NORMFWD_TRY_HOLD(NORMFWD_LN_HOLD_F4PT)
-        NORMFWD_TRY_HOLD(4)
-        NORMFWD_TRY_HOLD(8)
-        NORMFWD_TRY_HOLD(16)
+        if (protocol == 1) {  // control wave, tagged gather
+            NORMFWD_TRY_HOLD(8, 8)
+            NORMFWD_TRY_HOLD(4, 8)
+            NORMFWD_TRY_HOLD(8, 4)
+        }
+        // last workgroup merges (protocol 2, or shapes the above cannot hold)
+        NORMFWD_TRY_HOLD(NORMFWD_LN_HOLD_F4PT, 0)
+        NORMFWD_TRY_HOLD(4, 0)
+        NORMFWD_TRY_HOLD(8, 0)
+        NORMFWD_TRY_HOLD(16, 0)
 #undef NORMFWD_TRY_HOLD
     }
-    // Shapes the single-read kernel cannot hold run the split schedule.
+    // Shapes no single-read kernel can hold run the split schedule.
     hipError_t e = launch_ln_stats(x, outer, inner, eps, ws, lay, mean_out, rstd_out, st);
     if (e != hipSuccess) return e;
     return launch_ln_apply(x, w, b, y, outer, inner, ws, lay, st);

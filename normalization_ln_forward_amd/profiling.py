@@ -33,6 +33,7 @@ KERNEL_SOURCES = {
     "ln_normalize_rows_kernel": ["ln.hip", "common.hpp"],
     "ln_normalize_kernel": ["ln.hip", "common.hpp"],
     "ln_single_hold_kernel": ["ln.hip", "common.hpp"],
+    "ln_single_ctl_kernel": ["ln.hip", "common.hpp"],
     "gn_fast_kernel": ["gn.hip", "common.hpp"],
     "rms_ch_hold_kernel": ["rms.hip", "common.hpp"],
     "fc_mfma_kernel": ["fc.hip", "common.hpp"],

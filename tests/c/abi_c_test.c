@@ -102,7 +102,7 @@ static int run(void)
         void* dws = NULL;
         if (!dx || !dw || !db || !dy || hipMalloc(&dws, wsb) != hipSuccess) return 2;
         if (ln_forward_workspace_init(dws, wsb, st) != NORMFWD_OK) return 3;
-        for (int variant = 0; variant < 2; ++variant) {
+        for (int variant = 0; variant < 3; ++variant) {
             if (ln_forward(dx, dw, db, dy, outer, inner, 1e-5f, dws, wsb, NULL, NULL, variant, st) != NORMFWD_OK) {
                 printf("ln_forward: %s\n", normfwd_last_error());
                 return 3;
@@ -112,7 +112,8 @@ static int run(void)
             double *xd = promote(x, n), *wd = promote(w, (size_t)inner), *bd = promote(b, (size_t)inner);
             double* o = (double*)malloc(n * sizeof(double));
             oracle_ln(xd, wd, bd, outer, inner, (double)1e-5f, o, NULL, NULL);
-            fails += compare(variant ? "ln_forward single" : "ln_forward split", y, o, n);
+            fails += compare(variant == 0 ? "ln_forward split" : variant == 1 ? "ln_forward single" : "ln_forward single lbd",
+                             y, o, n);
             free(xd); free(wd); free(bd); free(o);
         }
         hipFree(dx); hipFree(dw); hipFree(db); hipFree(dy); hipFree(dws);

@@ -45,7 +45,7 @@ for _ in range(8):
 
 
 @pytest.mark.parametrize("outer,inner", LN_SHAPES)
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_ln_random_shapes(outer, inner, variant):
     print(f"ln fuzz outer={outer} inner={inner} variant={variant}", flush=True)
     d = synth.make("ln_16x64x256x256", device="cuda", shape=(outer, inner), seed=outer + 3 * inner,

@@ -176,6 +176,10 @@ LN_CASES = [
     (3, 300000, False, 0),           # no affine
     (3, 300000, False, 1),
     (1, 1 << 20, True, 1),           # one sample, many workgroups
+    (2, 40000, True, 2),             # single kernel, last workgroup merges
+    (4, 40001, True, 2),
+    (3, 300000, False, 2),
+    (1, 1 << 20, True, 2),
 ]
 
 
@@ -227,7 +231,7 @@ def test_ln_many_short_samples(outer, inner, dist):
 
 
 @pytest.mark.parametrize("name", ["ln_16x64x256x256", "ln_stress_16x64x256x256"])
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_ln_full_size(name, variant):
     """Full [16, 64, 256, 256] workloads, N(0,1) and the N(100, 0.01) cancellation stress."""
     _say(f"ln full {name} variant={variant}")
@@ -240,23 +244,24 @@ def test_ln_full_size(name, variant):
     assert torch.equal(y, y2), "not bitwise deterministic"
 
 
-def test_ln_single_kernel_repeated_and_split_halves():
+@pytest.mark.parametrize("variant", [1, 2])
+def test_ln_single_kernel_repeated_and_split_halves(variant):
     """Many back-to-back single-kernel launches on one workspace stay bitwise equal and
     leave the control block clean; stats + apply equals the split variant."""
-    _say("ln single repeated")
+    _say(f"ln single repeated variant={variant}")
     d = synth.make("ln_16x64x256x256", device="cuda", shape=(4, 1 << 19), normalized_ndim=1, seed=3)
     outer, inner = 4, 1 << 19
     nbytes = nf.ln_forward_workspace_size(outer, inner)
     _, ws = nf.alloc_workspace(nbytes, "cuda")
     nf.ln_forward_workspace_init(ws)
-    first = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws)
-    for _ in range(50):
-        again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws)
+    first = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
+    for _ in range(300):  # the generation tag wraps at 256
+        again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
         assert torch.equal(first, again)
     torch.cuda.synchronize()
     ctrl = ws[:16].view(torch.int32).cpu().tolist()  # gen, done, error, pad
     assert ctrl[1] == 0 and ctrl[2] == 0, ctrl
-    assert ctrl[0] == 51, ctrl
+    assert ctrl[0] == 301, ctrl
     ws0 = nf.ln_forward_stats(d["x"])
     halves = nf.ln_forward_apply(d["x"], d["weight"], d["bias"], ws0)
     split = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=0)
@@ -265,7 +270,7 @@ def test_ln_single_kernel_repeated_and_split_halves():
     _assert_close(_np(first), ref, what="ln single")
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_ln_in_place(variant):
     _say(f"ln in place variant={variant}")
     d = synth.make("ln_16x64x256x256", device="cuda", shape=(3, 100000), normalized_ndim=1, seed=9)
@@ -318,7 +323,7 @@ def test_prepared_calls_match_direct_calls():
     call()
     assert torch.equal(y1, y2)
     l = synth.make("ln_16x64x256x256", device="cuda", shape=(2, 64, 64, 64), seed=22)
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         z1 = nf.ln_forward(l["x"], l["weight"], l["bias"], variant=variant)
         z2 = torch.zeros_like(z1)
         run = nf.prepare(nf.ln_forward, l["x"], l["weight"], l["bias"], variant=variant, out=z2)
@@ -394,14 +399,14 @@ def test_ln_alternating_shapes_and_workspace_reinit():
     data = {s: synth.make("ln_16x64x256x256", device="cuda", shape=s, normalized_ndim=1, seed=s[0] + s[1])
             for s in set(shapes)}
     refs = {s: oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"])) for s, d in data.items()}
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         for s in shapes:
             d = data[s]
             _assert_close(_np(nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant)), refs[s],
                           what=f"ln {s} variant {variant}")
     big = max(nf.ln_forward_workspace_size(*s) for s in shapes)
     _, ws = nf.alloc_workspace(big, "cuda")
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         for s in shapes:
             d = data[s]
             nf.ln_forward_workspace_init(ws)
@@ -429,7 +434,7 @@ def test_time_next_kernel_stamps_one_launch():
     assert a.elapsed_time(b) == ms, "a later launch re-stamped the events"
     assert torch.equal(y, y2)
     d = synth.make("ln_16x64x256x256", device="cuda", shape=(4, 1 << 18), normalized_ndim=1, seed=52)
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         nf.time_next_kernel(a, b)
         out = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant)
         torch.cuda.synchronize()
