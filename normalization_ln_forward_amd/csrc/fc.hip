@@ -109,6 +109,51 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
+// Epilogue of a wave's 64 x 64 block of h (rows m0w.., columns n0w..).
+// D layout of a 32 x 32 tile: lane holds column (lane % 32); register r holds
+// row (r / 4) * 8 + (lane / 32) * 4 + r % 4.
+template <int GM>
+__device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __restrict__ bias,
+                                            const float* __restrict__ gamma, const float* __restrict__ beta,
+                                            float* __restrict__ out, int M, int N, int m0w, int n0w, int li, int lh,
+                                            float eps, float slope)
+{
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0w + j * 32 + li;
+            const bool col_ok = col < N;
+            const float bb = (bias && col_ok) ? bias[col] : 0.0f;
+            if constexpr (GM == 0) {
+                if (!col_ok) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                    if (row < M) out[(int64_t)row * N + col] = acc[i][j][r] + bb;
+                }
+            } else {
+                const float g = (gamma && col_ok) ? gamma[col] : 1.0f;
+                const float be = (beta && col_ok) ? beta[col] : 0.0f;
+                constexpr float inv_m = 1.0f / GM;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float hv = acc[i][j][r] + bb;
+                    float s1 = row16_sum(hv);
+                    if constexpr (GM == 32) s1 += __shfl_xor(s1, 16);
+                    const float d = hv - s1 * inv_m;
+                    float s2 = row16_sum(d * d);
+                    if constexpr (GM == 32) s2 += __shfl_xor(s2, 16);
+                    const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
+                    const float z = d * rstd * g + be;
+                    const float a = z > 0.0f ? z : slope * z;
+                    const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                    if (row < M && col_ok) out[(int64_t)row * N + col] = a + a;
+                }
+            }
+        }
+}
+
 // GM = 0: write h = x W^T + b to `out`.  GM = 16 or 32 (channels per group):
 // the GroupNorm -> LeakyReLU -> x + x epilogue runs on the accumulators and
 // `out` receives y; h never goes to memory.  In a 32 x 32 MFMA tile a lane
@@ -177,42 +222,118 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
         __syncthreads();
     }
 
-    // D layout of a 32 x 32 tile: lane holds column (lane % 32); register r
-    // holds row (r / 4) * 8 + (lane / 32) * 4 + r % 4.
+    fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope);
+}
+
+// Direct-to-LDS variant (K a multiple of 32, 16-byte aligned rows): the
+// K slices of x and W are copied from global memory straight into LDS with
+// gfx950's global_load_lds_dwordx4 (lane l of a wave fills bytes
+// [16 l, 16 l + 16) of the wave's 1 KiB destination), so no VGPRs stage
+// them and no ds_write is issued.  Three LDS stages (3 x 48 KiB): slice
+// it+2 is in flight while slice it is multiplied.  LDS rows are 128 bytes
+// (32 floats, eight 16-byte chunks) without padding; chunk c of row r is
+// stored at position c ^ (r & 7), so the eight rows a group of lanes reads
+// at one k land in eight different bank groups.  Rows beyond M or N read a
+// clamped (valid) row; their results are never stored.
+#ifndef NORMFWD_FC_DMA
+#define NORMFWD_FC_DMA 1
+#endif
+constexpr int kDmaStages = 3;
+constexpr int kDmaBM = 256, kDmaThreads = 512;
+constexpr int kDmaStageFloats = (kDmaBM + kBN) * 32;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int GM>
+__global__ void __launch_bounds__(kDmaThreads)
+fc_dma_kernel(const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
+              const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ out, int M, int N,
+              int K, float eps, float slope)
+{
+    __shared__ __attribute__((aligned(16))) float lds[kDmaStages * kDmaStageFloats];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * kDmaBM;
+    const int n0 = blockIdx.x * kBN;
+    const int li = lane & 31;  // row / column inside a 32 x 32 tile
+    const int lh = lane >> 5;  // which half of the k pair
+    const int nk = K / 32;
+
+    // This wave's share of one slice: A chunks q = (i * 8 + wave) * 64 + lane
+    // for i < 4 (256 rows x 8 chunks), B chunks likewise for i < 2.
+    auto issue = [&](int slice, int stage) __attribute__((always_inline)) {
+        float* base = lds + stage * kDmaStageFloats;
+        const int k0 = slice * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = (i * 8 + wave) * 64 + lane;
+            const int row = q >> 3, chunk = (q & 7) ^ (row & 7);
+            const int grow = min(m0 + row, M - 1);
+            __builtin_amdgcn_global_load_lds(x + (int64_t)grow * K + k0 + chunk * 4,
+                                             (lds_void_t*)(base + (i * 8 + wave) * 256), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = (i * 8 + wave) * 64 + lane;
+            const int row = q >> 3, chunk = (q & 7) ^ (row & 7);
+            const int grow = min(n0 + row, N - 1);
+            __builtin_amdgcn_global_load_lds(W + (int64_t)grow * K + k0 + chunk * 4,
+                                             (lds_void_t*)(base + kDmaBM * 32 + (i * 8 + wave) * 256), 16, 0, 0);
+        }
+    };
+
+    f16v acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + li;
-            const bool col_ok = col < N;
-            const float bb = (bias && col_ok) ? bias[col] : 0.0f;
-            if constexpr (GM == 0) {
-                if (!col_ok) continue;
+        for (int j = 0; j < 2; ++j) acc[i][j] = f16v(0.0f);
+
+    issue(0, 0);
+    issue(nk > 1 ? 1 : 0, 1);
+    // byte offset of this lane's 16 bytes for logical chunk c of its rows: rows
+    // r = w*64 + t*32 + li have r & 7 == li & 7
+    const int swz = li & 7;
+    for (int it = 0; it < nk; ++it) {
+        // This wave's copies of slice it are done (those of slice it+1 may
+        // still be in flight: 6 per slice, retired in issue order); after the
+        // barrier every wave's are, and every wave has consumed its reads of
+        // the stage read in iteration it-1.  (A plain __syncthreads() would
+        // first wait for all copies, slice it+1's included.)
+        asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+        issue(it + 2 < nk ? it + 2 : nk - 1, (it + 2) % kDmaStages);
+        const float* A = lds + (it % kDmaStages) * kDmaStageFloats;
+        const float* B = A + kDmaBM * 32;
+        // operands of k step kq+1 are read while the MFMAs of step kq run
+        f4 av[2][2], bv[2][2];
+        auto read = [&](int kq, int buf) __attribute__((always_inline)) {
+            const int chunk = ((kq * 2 + lh) ^ swz) * 4;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                    if (row < M) out[(int64_t)row * N + col] = acc[i][j][r] + bb;
-                }
-            } else {
-                const float g = (gamma && col_ok) ? gamma[col] : 1.0f;
-                const float be = (beta && col_ok) ? beta[col] : 0.0f;
-                constexpr float inv_m = 1.0f / GM;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float hv = acc[i][j][r] + bb;
-                    float s1 = row16_sum(hv);
-                    if constexpr (GM == 32) s1 += __shfl_xor(s1, 16);
-                    const float d = hv - s1 * inv_m;
-                    float s2 = row16_sum(d * d);
-                    if constexpr (GM == 32) s2 += __shfl_xor(s2, 16);
-                    const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
-                    const float z = d * rstd * g + be;
-                    const float a = z > 0.0f ? z : slope * z;
-                    const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                    if (row < M && col_ok) out[(int64_t)row * N + col] = a + a;
-                }
+            for (int t = 0; t < 2; ++t) {
+                av[buf][t] = *reinterpret_cast<const f4*>(A + (wm * 64 + t * 32 + li) * 32 + chunk);
+                bv[buf][t] = *reinterpret_cast<const f4*>(B + (wn * 64 + t * 32 + li) * 32 + chunk);
             }
+        };
+        read(0, 0);
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            if (kq < 3) read(kq + 1, (kq + 1) & 1);
+            // keep those reads ahead of this step's MFMAs (the scheduler would
+            // otherwise sink them to reuse the registers)
+            __builtin_amdgcn_sched_barrier(0);
+            const int cb = kq & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] =
+                            __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb][i][e], bv[cb][j][e], acc[i][j], 0, 0, 0);
         }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the workgroup's LDS
+    fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope);
 }
 
 template <int GM>
@@ -220,6 +341,11 @@ static hipError_t launch_gemm(bool vec, const float* x, const float* W, const fl
                               const float* beta, float* out, int64_t N, int64_t K, int64_t C, float eps, float slope,
                               hipStream_t st)
 {
+    if (NORMFWD_FC_DMA && vec && K % 32 == 0) {
+        const dim3 g((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, kDmaBM));
+        return launch_kernel((fc_dma_kernel<GM>), g, dim3(kDmaThreads), 0, st, x, W, b, gamma, beta, out, (int)N,
+                             (int)C, (int)K, eps, slope);
+    }
     constexpr int WM = NORMFWD_FC_WM;
     using T = Tile<WM>;
     const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, T::kBM));

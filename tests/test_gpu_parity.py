@@ -290,6 +290,9 @@ FC_CASES = [
     (96, 128, 256, 8),      # M = 32 fused
     (70, 64, 256, 32),      # M = 8: GEMM writes h, then the GroupNorm kernel
     (40, 36, 512, 8),       # M = 64: GEMM writes h, then the GroupNorm kernel
+    # K % 32 == 0 runs the direct-to-LDS GEMM (256-row tiles); the others above with K % 32 == 0 do too
+    (300, 32, 200, 25),     # M = 8; two row tiles, the second ragged; ragged column tile
+    (513, 256, 128, 8),     # M = 16 fused; three row tiles, one row in the last
 ]
 
 
