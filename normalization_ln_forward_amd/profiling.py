@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "gn_fast_kernel": ["gn.hip", "common.hpp"],
     "rms_ch_hold_kernel": ["rms.hip", "common.hpp"],
     "fc_mfma_kernel": ["fc.hip", "common.hpp"],
+    "fc_dma_kernel": ["fc.hip", "common.hpp"],
 }
 
 
