@@ -156,7 +156,7 @@ void oracle_rms_ch(const double* x, int64_t B, int64_t C, int64_t S, double eps,
 void oracle_fc(const double* x, const double* W, const double* bias,
                int64_t N, int64_t K, int64_t Cout, double* h)
 {
-    if (N <= 0 || K <= 0 || Cout <= 0) return;
+    if (N <= 0 || K < 0 || Cout <= 0) return;  /* K == 0: the empty sum, h = bias */
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t c = 0; c < Cout; ++c) {

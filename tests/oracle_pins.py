@@ -80,7 +80,7 @@ def pin_rms_bruteforce(orc, seed=2):
 def pin_fc_numpy(orc, seed=3):
     """fc == numpy's float64 matmul (an independent library routine), non-square W."""
     rng = np.random.default_rng(seed)
-    for N, K, Cout in [(3, 5, 7), (4, 33, 6), (1, 64, 2)]:
+    for N, K, Cout in [(3, 5, 7), (4, 33, 6), (1, 64, 2), (3, 0, 5)]:  # K = 0: the empty sum, h = b
         x = rng.standard_normal((N, K)).astype(np.float32)
         W = rng.uniform(-1, 1, (Cout, K)).astype(np.float32)
         b = rng.uniform(-1, 1, Cout).astype(np.float32)
