@@ -28,6 +28,9 @@
  *     C <= 2^24.  Problems whose grid would exceed the 32-bit work-item
  *     count of one launch are enqueued as several launches of whole samples
  *     (rows), in order, on the same stream.
+ *   - Empty work is a no-op that returns NORMFWD_OK without inspecting the
+ *     pointers: ln with outer == 0, gn with N == 0, rms with B == 0 or
+ *     S == 0, fc with N == 0 (fc with K == 0 computes h = b).
  *   - Errors are returned, never thrown: arguments are validated before
  *     anything is enqueued, so a non-OK return from validation means nothing
  *     was launched.  normfwd_last_error() then describes the failure

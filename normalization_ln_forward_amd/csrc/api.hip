@@ -133,6 +133,7 @@ normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes
 normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, float eps, void* workspace,
                                 size_t workspace_bytes, float* mean_out, float* rstd_out, void* stream)
 {
+    if (outer == 0 && inner >= 0) return ok();  // empty batch: nothing to do
     normfwd_status s = check_ln(x, x, outer, inner, eps);
     if (s != NORMFWD_OK) return s;
     const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
@@ -147,6 +148,7 @@ normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, fl
 normfwd_status ln_forward_apply(const float* x, const float* weight, const float* bias, float* y, int64_t outer,
                                 int64_t inner, const void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (outer == 0 && inner >= 0) return ok();  // empty batch: nothing to do
     normfwd_status s = check_ln(x, y, outer, inner, 0.0f);
     if (s != NORMFWD_OK) return s;
     const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
@@ -161,6 +163,7 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
                           int64_t inner, float eps, void* workspace, size_t workspace_bytes, float* mean_out,
                           float* rstd_out, int variant, void* stream)
 {
+    if (outer == 0 && inner >= 0 && variant >= 0 && variant <= 2) return ok();  // empty batch: nothing to do
     normfwd_status s = check_ln(x, y, outer, inner, eps);
     if (s != NORMFWD_OK) return s;
     if (variant < 0 || variant > 2) return fail(NORMFWD_ERR_INVALID, "ln_forward: variant must be 0, 1 or 2");
@@ -185,6 +188,7 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
 normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
                                    int64_t C, int64_t num_groups, float eps, float negative_slope, void* stream)
 {
+    if (N == 0 && C > 0 && num_groups > 0 && C % num_groups == 0) return ok();  // no rows: nothing to do
     if (!x || !y) return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: x and y must not be NULL");
     if (N <= 0 || C <= 0 || num_groups <= 0)
         return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: N, C and num_groups must be > 0");
@@ -206,6 +210,7 @@ normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const flo
 
 normfwd_status rmsnorm_ch_forward(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps, void* stream)
 {
+    if ((B == 0 || S == 0) && B >= 0 && S >= 0 && C > 0) return ok();  // no positions: nothing to do
     if (!x || !y) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward: x and y must not be NULL");
     if (B <= 0 || C <= 0 || S <= 0) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward: B, C and S must be > 0");
     if (C > std::numeric_limits<int>::max() || S > ((int64_t)1 << 26) || B > kMaxElems / (C * S))
@@ -226,13 +231,16 @@ normfwd_status fc_gn_forward(const float* x, const float* W, const float* b, con
                              float* y, int64_t N, int64_t K, int64_t C, int64_t num_groups, float eps,
                              float negative_slope, void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!x || !W || !y) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: x, W and y must not be NULL");
-    if (N <= 0 || K <= 0 || C <= 0 || num_groups <= 0)
-        return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: N, K, C and num_groups must be > 0");
+    if (N == 0 && K >= 0 && C > 0 && num_groups > 0 && C % num_groups == 0) return ok();  // no rows: nothing to do
+    if (!x && K > 0) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: x must not be NULL");
+    if ((!W && K > 0) || !y) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: W and y must not be NULL");
+    if (N <= 0 || K < 0 || C <= 0 || num_groups <= 0)
+        return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: N, C and num_groups must be > 0 and K >= 0");
     if (C % num_groups != 0)
         return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: C (%lld) must be a multiple of num_groups (%lld)",
                     (long long)C, (long long)num_groups);
-    if (N > kMaxElems / C || C > kMaxElems / K || N > kMaxElems / K || N > (1 << 23) || C > (1 << 24))
+    const int64_t K1 = K > 0 ? K : 1;
+    if (N > kMaxElems / C || C > kMaxElems / K1 || N > kMaxElems / K1 || N > (1 << 23) || C > (1 << 24))
         return fail(NORMFWD_ERR_UNSUPPORTED, "fc_gn_forward: shape too large");
     if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: eps must be >= 0");
     normfwd_status s = check_ws(workspace, workspace_bytes, fc_gn_forward_workspace_size(N, K, C), "fc_gn_forward");

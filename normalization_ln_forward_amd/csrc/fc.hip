@@ -341,7 +341,7 @@ static hipError_t launch_gemm(bool vec, const float* x, const float* W, const fl
                               const float* beta, float* out, int64_t N, int64_t K, int64_t C, float eps, float slope,
                               hipStream_t st)
 {
-    if (NORMFWD_FC_DMA && vec && K % 32 == 0) {
+    if (NORMFWD_FC_DMA && vec && K >= 32 && K % 32 == 0) {
         const dim3 g((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, kDmaBM));
         return launch_kernel((fc_dma_kernel<GM>), g, dim3(kDmaThreads), 0, st, x, W, b, gamma, beta, out, (int)N,
                              (int)C, (int)K, eps, slope);

@@ -21,17 +21,24 @@
 //   * the mean is handed to the normalize pass as an fp32 pair hi + lo, so
 //     (x - hi) - lo keeps ~48 bits of the mean.
 //
-// Two schedules of the same arithmetic:
-//   split  (variant 0): ln_partial_kernel -> ln_merge_kernel ->
-//          ln_normalize_rows_kernel (or ln_normalize_kernel).
-//   single (variant 1): one cooperative launch, one workgroup per chunk
-//          index p; the last workgroup to deliver a sample's partial merges
-//          it and publishes the statistics with an agent-scope release (LN
-//          page, turn 6: last-block-done with a counter), the others wait
-//          for it with acquire loads.  Workgroups run phase 1 of sample t and
-//          phase 2 of sample t-1 back to back, so the second read of a
-//          chunk follows the first by one sample (16 MiB of chip-wide
-//          traffic) and is served from L2 / MALL instead of HBM.
+// Schedules of the same arithmetic:
+//   split (variant 0): ln_partial_kernel (-> ln_merge_kernel from 1024
+//          moments workgroups on; below that the last workgroup of each
+//          sample merges it) -> ln_normalize_rows_kernel (or
+//          ln_normalize_kernel for short samples); x is read twice.
+//   single kernels (variants 1 and 2): one cooperative launch; workgroup p
+//          keeps its rows of every sample in VGPRs from the moments pass to
+//          the normalize pass, so x is read once, and the workgroups
+//          exchange each sample's moments in the middle:
+//          ln_single_ctl_kernel (variant 1): a control wave per workgroup
+//          publishes generation-tagged sums and gathers everyone's, while
+//          the data waves stream the next samples;
+//          ln_single_hold_kernel (variant 2): the last workgroup to
+//          deliver a sample's partial merges it and announces the
+//          statistics with a flag (LN page, turn 6: last-block-done).
+//   short samples (inner <= 8192): ln_row_kernel, one workgroup per sample.
+// Cross-workgroup data is only ever accessed with device-coherent atomic
+// loads and stores (see the protocol notes below), never with fences.
 #include "common.hpp"
 #include "internal.hpp"
 

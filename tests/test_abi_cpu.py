@@ -50,8 +50,8 @@ def test_ln_validation():
     lib = _lib.lib()
     st, msg = _err(lib.ln_forward(None, None, None, FAKE, 2, 8, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
     assert st == 1 and "NULL" in msg
-    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 0, 8, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
-    assert st == 1
+    st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 2, 0, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
+    assert st == 1  # normalizing over no elements
     st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 2, -1, 1e-5, FAKE_WS, 1 << 20, None, None, 0, None))
     assert st == 1
     st, _ = _err(lib.ln_forward(FAKE, None, None, FAKE, 2, 8, 1e-5, FAKE_WS, 1 << 20, None, None, 7, None))
@@ -92,7 +92,7 @@ def test_gn_validation():
     assert st == 1 and "multiple" in msg
     st, _ = _err(lib.gn_lrelu_x2_forward(None, None, None, FAKE, 4, 12, 3, 1e-5, 0.01, None))
     assert st == 1
-    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 0, 12, 3, 1e-5, 0.01, None))
+    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, -1, 12, 3, 1e-5, 0.01, None))
     assert st == 1
     st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 12, 0, 1e-5, 0.01, None))
     assert st == 1
@@ -121,3 +121,20 @@ def test_fc_validation():
     st, _ = _err(lib.fc_gn_forward(FAKE, None, None, None, None, FAKE, 1024, 8192, 8192, 512, 1e-5, 0.01, FAKE_WS,
                                    need, None))
     assert st == 1
+
+
+def test_empty_work_is_a_no_op_that_touches_nothing():
+    """Empty batches return OK before any pointer is inspected or anything is launched (so this runs
+    without a GPU): NULL everywhere, no workspace."""
+    lib = _lib.lib()
+    for variant in (0, 1, 2):
+        assert lib.ln_forward(None, None, None, None, 0, 4096, 1e-5, None, 0, None, None, variant, None) == 0
+    assert lib.ln_forward_stats(None, 0, 4096, 1e-5, None, 0, None, None, None) == 0
+    assert lib.ln_forward_apply(None, None, None, None, 0, 4096, None, 0, None) == 0
+    assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 8192, 512, 1e-5, 0.01, None) == 0
+    assert lib.rmsnorm_ch_forward(None, None, 0, 64, 1024, 1e-5, None) == 0
+    assert lib.rmsnorm_ch_forward(None, None, 3, 64, 0, 1e-5, None) == 0
+    assert lib.fc_gn_forward(None, None, None, None, None, None, 0, 64, 128, 8, 1e-5, 0.01, None, 0, None) == 0
+    # still invalid: a bad group count or a negative size
+    assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 100, 7, 1e-5, 0.01, None) == 1
+    assert lib.rmsnorm_ch_forward(None, None, -1, 64, 1024, 1e-5, None) == 1

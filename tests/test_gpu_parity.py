@@ -443,3 +443,25 @@ def test_time_next_kernel_stamps_one_launch():
         torch.cuda.synchronize()
         assert 0.0 < a.elapsed_time(b) < 100.0
         _assert_close(_np(out), oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"])), what=f"ln {variant}")
+
+
+def test_empty_inputs_and_k_zero():
+    """Empty batches return empty outputs (the library launches nothing); fc with K = 0 gives
+    GroupNorm of the bias."""
+    _say("empty inputs")
+    e = torch.empty(0, 64, 8, 8, device="cuda")
+    assert nf.ln_forward(e).shape == e.shape
+    for variant in (1, 2):
+        assert nf.ln_forward(e, variant=variant).shape == e.shape
+    assert nf.gn_lrelu_x2_forward(torch.empty(0, 256, device="cuda"), None, None, 16).shape == (0, 256)
+    assert nf.rmsnorm_ch_forward(torch.empty(0, 64, 16, device="cuda")).shape == (0, 64, 16)
+    assert nf.rmsnorm_ch_forward(torch.empty(3, 64, 0, device="cuda")).shape == (3, 64, 0)
+    f = synth.make("fc_gn_1024x8192x8192", device="cuda", shape=(5, 64), hidden=128, seed=61)
+    y0 = nf.fc_gn_forward(f["x"][:0], f["W"], f["b"], f["gamma"], f["beta"], 8)
+    assert y0.shape == (0, 128)
+    x0 = torch.empty(5, 0, device="cuda")
+    w0 = torch.empty(128, 0, device="cuda")
+    y = nf.fc_gn_forward(x0, w0, f["b"], f["gamma"], f["beta"], 8)
+    ref = oracle.fc_gn_lrelu_x2(np.zeros((5, 0), np.float32), np.zeros((128, 0), np.float32), _np(f["b"]),
+                                _np(f["gamma"]), _np(f["beta"]), 8)
+    _assert_close(_np(y), ref, rtol=RTOL_FC, what="fc K=0")
