@@ -229,8 +229,10 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
 // K slices of x and W are copied from global memory straight into LDS with
 // gfx950's global_load_lds_dwordx4 (lane l of a wave fills bytes
 // [16 l, 16 l + 16) of the wave's 1 KiB destination), so no VGPRs stage
-// them and no ds_write is issued.  Three LDS stages (3 x 48 KiB): slice
-// it+2 is in flight while slice it is multiplied.  LDS rows are 128 bytes
+// them and no ds_write is issued.  Three LDS stages (3 x 48 KiB): slices
+// it+1 and it+2 are in flight while slice it is multiplied, and one barrier
+// per slice, placed before its last k step, hands slice it's stage to the
+// copies of slice it+3.  LDS rows are 128 bytes
 // (32 floats, eight 16-byte chunks) without padding; chunk c of row r is
 // stored at position c ^ (r & 7), so the eight rows a group of lanes reads
 // at one k land in eight different bank groups.  Rows beyond M or N read a
@@ -289,48 +291,53 @@ fc_dma_kernel(const float* __restrict__ x, const float* __restrict__ W, const fl
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f16v(0.0f);
 
-    issue(0, 0);
-    issue(nk > 1 ? 1 : 0, 1);
     // byte offset of this lane's 16 bytes for logical chunk c of its rows: rows
     // r = w*64 + t*32 + li have r & 7 == li & 7
     const int swz = li & 7;
-    for (int it = 0; it < nk; ++it) {
-        // This wave's copies of slice it are done (those of slice it+1 may
-        // still be in flight: 6 per slice, retired in issue order); after the
-        // barrier every wave's are, and every wave has consumed its reads of
-        // the stage read in iteration it-1.  (A plain __syncthreads() would
-        // first wait for all copies, slice it+1's included.)
-        asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-        issue(it + 2 < nk ? it + 2 : nk - 1, (it + 2) % kDmaStages);
-        const float* A = lds + (it % kDmaStages) * kDmaStageFloats;
+    // Slice it's last k step is multiplied after the barrier, so the first
+    // operand reads of slice it+1 (issued right after the barrier) land while
+    // those MFMAs run; slice it+3 goes into slice it's stage, whose reads
+    // have all completed (lgkmcnt(0) before the barrier).
+    f4 av[2][2], bv[2][2];
+    auto read = [&](const float* A, int kq, int buf) __attribute__((always_inline)) {
         const float* B = A + kDmaBM * 32;
-        // operands of k step kq+1 are read while the MFMAs of step kq run
-        f4 av[2][2], bv[2][2];
-        auto read = [&](int kq, int buf) __attribute__((always_inline)) {
-            const int chunk = ((kq * 2 + lh) ^ swz) * 4;
+        const int chunk = ((kq * 2 + lh) ^ swz) * 4;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                av[buf][t] = *reinterpret_cast<const f4*>(A + (wm * 64 + t * 32 + li) * 32 + chunk);
-                bv[buf][t] = *reinterpret_cast<const f4*>(B + (wn * 64 + t * 32 + li) * 32 + chunk);
-            }
-        };
-        read(0, 0);
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            if (kq < 3) read(kq + 1, (kq + 1) & 1);
-            // keep those reads ahead of this step's MFMAs (the scheduler would
-            // otherwise sink them to reuse the registers)
-            __builtin_amdgcn_sched_barrier(0);
-            const int cb = kq & 1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] =
-                            __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb][i][e], bv[cb][j][e], acc[i][j], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+            av[buf][t] = *reinterpret_cast<const f4*>(A + (wm * 64 + t * 32 + li) * 32 + chunk);
+            bv[buf][t] = *reinterpret_cast<const f4*>(B + (wn * 64 + t * 32 + li) * 32 + chunk);
         }
+    };
+    auto mfma_step = [&](int cb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb][i][e], bv[cb][j][e], acc[i][j], 0, 0, 0);
+    };
+    issue(0, 0);
+    issue(nk > 1 ? 1 : 0, 1);
+    issue(nk > 2 ? 2 : nk - 1, 2);
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");  // slice 0 is in LDS
+    read(lds, 0, 0);
+    for (int it = 0; it < nk; ++it) {
+        const float* A = lds + (it % kDmaStages) * kDmaStageFloats;
+#pragma unroll
+        for (int kq = 0; kq < 3; ++kq) {
+            read(A, kq + 1, (kq + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(kq & 1);
+        }
+        // this wave's copies of slice it+1 are done (slice it+2's, 6 more,
+        // may be in flight) and its reads of slice it have landed; after the
+        // barrier the same holds for every wave
+        asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(it + 3 < nk ? it + 3 : nk - 1, it % kDmaStages);
+        if (it + 1 < nk) read(lds + ((it + 1) % kDmaStages) * kDmaStageFloats, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the workgroup's LDS
     fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope);
