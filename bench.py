@@ -3,11 +3,15 @@
 
 Headline step: LayerNorm forward on x [16, 64, 256, 256] fp32 ~ N(0,1),
 normalized over (64, 256, 256), elementwise weight/bias (LN page "Kimi-K2.6
-l1_p40" problem).  One step = the whole LN path (partial moments, merge,
-normalize) over one batch; `value` = algorithmic bytes / wall time per step,
-with inputs resident in HBM.  Algorithmic bytes of the method = x read twice
-(moments pass + normalize pass) + weight + bias read once + y written once
-= 838,860,800 B.
+l1_p40" problem).  One step = the whole LN path (moments, merge, normalize)
+over one batch; `value` = algorithmic bytes / wall time per step, with inputs
+resident in HBM.  Algorithmic bytes of the method = x read twice (moments
+pass + normalize pass) + weight + bias read once + y written once
+= 838,860,800 B, whatever schedule runs it.  The headline schedule is the
+fastest measured, the single-read kernel (--variant 1: x crosses HBM once,
+570,425,344 B, which are the bytes its roofline entry is priced on); the
+split schedule (--variant 0) and the last-block-done kernel (--variant 2)
+are timed in the `kernels` object.
 
 Also measured (the `kernels` object): GroupNorm+LeakyReLU+x2 [1024, 8192],
 RMSNorm over dim 1 [112, 64, 512, 512], the LN N(100, 0.01) stress input,
@@ -72,9 +76,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--variant", type=int, default=0, choices=[0, 1, 2],
-                    help="LN schedule for the headline: 0 = split (default, fastest measured), 1 = single kernel "
-                         "(control wave, tagged exchange), 2 = single kernel, last workgroup merges")
+    ap.add_argument("--variant", type=int, default=1, choices=[0, 1, 2],
+                    help="LN schedule for the headline: 1 = single kernel, control wave and tagged exchange "
+                         "(default, fastest measured), 0 = split, 2 = single kernel, last workgroup merges")
     ap.add_argument("--rotate", type=int, default=4, help="LN buffer sets rotated through (>=1)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,11 +125,13 @@ def main():
     # argument checking and marshalling happen once per buffer set, outside the timed region
     if variant != 0:
         steps = [nf.prepare(nf.ln_forward, xs[r], w, b, variant=variant, out=ys[r], workspace=ws) for r in range(R)]
-        t = time_launches(torch, stream, lambda i: steps[i % R](), args.steps, args.warmup)
+        t = time_launches(torch, stream, lambda i: steps[i % R](), args.steps, args.warmup, nf=nf)
         ms_per_step = t["wall_ms"]
-        # the single-read kernel moves x once: its own algorithmic bytes are the normalize pass's
+        # The single-read kernel moves x once, so its roofline is priced on the bytes it must move
+        # (x + y + weight + bias).  A cooperative launch cannot stamp events itself: the armed events
+        # bracket each launch, so its duration here includes the cooperative launch's own cost.
         dom_kernel = "ln_single_ctl_kernel" if variant == 1 else "ln_single_hold_kernel"
-        dom_bytes, avg_ms = LN_NORMALIZE_BYTES, t["avg_ms"]
+        dom_bytes, avg_ms = LN_NORMALIZE_BYTES, t["kernel_ms"]
     else:
         # the step is the two halves of the split schedule
         stats = [nf.prepare(nf.ln_forward_stats, xs[r], workspace=ws) for r in range(R)]

@@ -43,6 +43,7 @@
 #include "internal.hpp"
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 
 namespace normfwd {
@@ -106,6 +107,11 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // ([16, 65536], [8, 2^20]), is even at 1024 and costs 0.6-1.5 us at 1024-4096
 // ([4, 2^22], [16, 2^22]), where the atomics of thousands of workgroups
 // outweigh the saved launch.
+// Single kernel with a control wave: iterations between a sample's moments
+// and its normalize (1 or 2).
+#ifndef NORMFWD_LN_CTL_LAG
+#define NORMFWD_LN_CTL_LAG 2
+#endif
 #ifndef NORMFWD_LN_FUSE_BELOW
 #define NORMFWD_LN_FUSE_BELOW 1024
 #endif
@@ -796,33 +802,64 @@ __device__ __forceinline__ double untag(double v)
 // data waves never wait on another workgroup and their loads stay in
 // flight (a wave's memory counter retires in issue order, so a wave that
 // polled memory would also wait for its own prefetch).  One workgroup
-// barrier per sample:
-//   data waves, iteration t:  issue the loads of sample t+1; moments of
-//       sample t -> per-wave sums in LDS; barrier t; normalize and store
-//       sample t-1 with the statistics the control wave left in LDS.
+// barrier per sample; sample s is normalized LAG iterations after its
+// moments:
+//   data waves, iteration t:  moments of sample t -> per-wave sums in LDS;
+//       barrier t; normalize and store sample t-LAG with the statistics the
+//       control wave left in LDS, then load sample t-LAG+NT into the freed
+//       registers (NT = LAG + 2 register tiles: sample t+1 is in flight
+//       while t is reduced, and t+2 is issued at the end of the iteration).
 //   control wave, after barrier t:  publish this workgroup's sums of
-//       d = x - K and d^2 (K the sample's first element, shared by every
-//       workgroup) as two generation-tagged words; read all P workgroups'
-//       sums until every tag is current, add them in a fixed order (every
-//       workgroup computes the same statistics: mean = K + S1/N, sum of
-//       squared deviations = S2 - S1^2/N, the shifted form of the pairwise
-//       merge when all parts share one shift) and leave the statistics in
-//       LDS before barrier t+1.
-// No atomics, counters or flags: the exchange for sample t overlaps the
-// data waves' normalize of t-1 and their loads and moments of t+1.  (The
-// last-workgroup-merges protocol of ln_single_hold_kernel measured slower
-// here: its chain of arrival atomic, merge and flag is longer than one
-// sample's streaming time.)
-template <int F4PT, int DW>
+//       d = x - K and d^2 for sample t (K the sample's first element, shared
+//       by every workgroup) as two generation-tagged words; then read all P
+//       workgroups' sums of sample t-LAG+1 until every tag is current, add
+//       them in a fixed order (every workgroup computes the same statistics:
+//       mean = K + S1/N, sum of squared deviations = S2 - S1^2/N, the shifted
+//       form of the pairwise merge when all parts share one shift) and leave
+//       the statistics in LDS before barrier t+1.
+// With LAG = 2 every workgroup has had a whole iteration to publish the
+// sums the control wave gathers, so the gather rarely waits and the data
+// waves do not wait for the slowest workgroup each iteration.  No atomics,
+// counters or flags.  (The last-workgroup-merges protocol of
+// ln_single_hold_kernel measured slower here: its chain of arrival atomic,
+// merge and flag is longer than one sample's streaming time.)
+// Iterations of ln_single_ctl_kernel with compile-time tile indices:
+// ctl_first_steps runs iterations 0 .. LAG-1 (moments only); ctl_steps runs
+// t0 + U, t0 + U + 1, ... for U < NT (iteration t uses tile (t0 + U) % NT,
+// t0 = LAG mod NT), stopping after the last of `steps` iterations, and
+// returns false once that one has run.
+template <int U, int LAG, typename F>
+__device__ __forceinline__ void ctl_first_steps(F& f)
+{
+    if constexpr (U < LAG) {
+        f((int64_t)U, std::integral_constant<int, U>{}, std::false_type{});
+        ctl_first_steps<U + 1, LAG>(f);
+    }
+}
+template <int U, int NT, int LAG, typename F>
+__device__ __forceinline__ bool ctl_steps(int64_t t0, int64_t steps, F& f)
+{
+    if constexpr (U == NT) {
+        return true;
+    } else {
+        f(t0 + U, std::integral_constant<int, (LAG + U) % NT>{}, std::true_type{});
+        if (t0 + U + 1 >= steps) return false;
+        return ctl_steps<U + 1, NT, LAG>(t0, steps, f);
+    }
+}
+
+template <int F4PT, int DW, int LAG>
 __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
                      int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats, Partial* parts, float* mean_out,
                      float* rstd_out)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
+    constexpr int NT = LAG + 2;     // register tiles per data thread
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     __shared__ double red[2][2 * DW];  // [sample parity][wave]: sum d, sum d^2
     __shared__ f4 s_stats[2];          // [sample parity]: mean hi, mean lo, rstd
+    __shared__ float s_K[4];           // [sample % 4]: the sample's shift K (its first element)
     f4* w_s = reinterpret_cast<f4*>(smem_raw);
     f4* b_s = w_s + (w ? F4PT * RW : 0);
     const int64_t P = gridDim.x;
@@ -830,30 +867,44 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int64_t nv = inner / 4;
+    const int64_t steps = outer + LAG;  // iterations = barriers after the prologue
 
     if (tid >= RW) {
-        // ---- control wave
+        // ---- control wave.  It also hands the data waves each sample's
+        // shift: K of sample t+2 is written during iteration t, so the data
+        // waves find it in LDS when they reduce that sample (after barrier
+        // t+1), and their memory counters see only x tiles and y stores.
         const uint32_t target = dev_load(&ctrl->gen) + 1u;
-        float K = x[0];
-        __syncthreads();  // prologue: w/b in LDS
-        for (int64_t t = 0; t <= outer; ++t) {
+        if (lane == 0) {
+            s_K[0] = x[0];
+            if (outer > 1) s_K[1] = x[inner];
+        }
+        __syncthreads();  // prologue: w/b and the first shifts in LDS
+        for (int64_t t = 0; t < steps; ++t) {
             __syncthreads();  // barrier t: the wave sums of sample t are in LDS
-            if (t == outer) break;
-            const float K_next = x[(t + 1 < outer ? t + 1 : t) * inner];
-            // this workgroup's sums of d = x - K and d^2 over its elements of sample t
-            Partial* pb = parts + t * P_cap;
-            if (lane == 0) {
+            const bool next_k = t + 2 < outer;
+            const float k_next = next_k ? x[(t + 2) * inner] : 0.0f;
+            if (t < outer && lane == 0) {
+                // this workgroup's sums of d = x - K and d^2 over its elements of sample t
                 const double* rd = red[t & 1];
                 double s1 = rd[0], s2 = rd[1];
                 for (int wv = 1; wv < DW; ++wv) {
                     s1 += rd[2 * wv];
                     s2 += rd[2 * wv + 1];
                 }
-                dev_store(&pb[p].n, tag_word(s1, target));
-                dev_store(&pb[p].mean, tag_word(s2, target));
+                Partial* q = parts + t * P_cap + p;
+                dev_store(&q->n, tag_word(s1, target));
+                dev_store(&q->mean, tag_word(s2, target));
             }
+            const int64_t g = t - (LAG - 1);  // the sample gathered now, normalized after barrier g + LAG
+            if (g < 0 || g >= outer) {
+                if (next_k && lane == 0) s_K[(t + 2) & 3] = k_next;
+                continue;
+            }
+            const float K = s_K[g & 3];
             // gather every workgroup's sums (lane l: workgroups l, l + 64, ...),
             // retrying until every tag is current, then a fixed-order sum
+            const Partial* pb = parts + g * P_cap;
             double S1 = 0.0, S2 = 0.0;
             for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
                 double a[4], b2[4];
@@ -869,7 +920,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                         ok = ok && has_tag(a[u], target) && has_tag(b2[u], target);
                     }
                     if (__all(ok)) break;
-                    __builtin_amdgcn_s_sleep(1);
+                    __builtin_amdgcn_s_sleep(2);
                     if (++spins > kSpinLimit) {
                         if (lane == 0) dev_store(&ctrl->error, 1u);
                         break;
@@ -890,14 +941,14 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                 const double N = (double)inner;
                 const double md = S1 / N;
                 const f4 st = finish_stats(N, (double)K + md, fmax(S2 - S1 * md, 0.0), eps);
-                s_stats[t & 1] = st;
+                s_stats[g & 1] = st;
                 if (p == 0) {
-                    stats[t] = st;
-                    if (mean_out) mean_out[t] = st.x;
-                    if (rstd_out) rstd_out[t] = st.z;
+                    stats[g] = st;
+                    if (mean_out) mean_out[g] = st.x;
+                    if (rstd_out) rstd_out[g] = st.z;
                 }
+                if (next_k) s_K[(t + 2) & 3] = k_next;
             }
-            K = K_next;
         }
         // completion: the last workgroup out advances the generation
         if (lane == 0) {
@@ -917,56 +968,53 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
     // unconditionally, clamped to a valid address and masked where used: the
     // memory counter retires in issue order, so with a fixed number of loads
     // per iteration a wave can wait for one tile while the next is in flight.
+    // A tile past the last sample reads one fixed address (no traffic).
     uint32_t off0 = (uint32_t)p * RW + (uint32_t)tid;
     const uint32_t stride = (uint32_t)P * RW;
     auto index = [&](int k) -> uint32_t { return off0 + (uint32_t)k * stride; };
     auto valid = [&](int k) -> bool { return (int64_t)index(k) < nv; };
     const uint32_t last_unit = (uint32_t)(nv - 1);
     auto addr = [&](int k) -> uint32_t { return std::min(index(k), last_unit); };
-    f4 ta[F4PT], tb[F4PT], tc[F4PT];  // three x tiles whose roles rotate
-    float ka, kb, kc;                  // the matching per-sample shifts
+    f4 T[NT][F4PT];  // register tiles; sample s lives in tile s % NT
+    auto load = [&](int r, int64_t s) __attribute__((always_inline)) {
+        // past the last sample every lane reads the last sample's first
+        // float4 (index masked to 0): same instruction count, no traffic
+        const int64_t sb = s < outer ? s : outer - 1;
+        const uint32_t m = s < outer ? 0xFFFFFFFFu : 0u;
+        const f4* xs = reinterpret_cast<const f4*>(x + sb * inner);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) T[r][k] = xs[addr(k) & m];
+    };
     for (int which = 0; which < 2; ++which) {
         // weight / bias rows -> LDS: all loads in flight first, then the LDS stores
         const float* src = which == 0 ? w : bias;
         f4* dst = which == 0 ? w_s : b_s;
         if (!src) continue;
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) ta[k] = reinterpret_cast<const f4*>(src)[addr(k)];
+        for (int k = 0; k < F4PT; ++k) T[0][k] = reinterpret_cast<const f4*>(src)[addr(k)];
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) dst[k * RW + tid] = ta[k];
+        for (int k = 0; k < F4PT; ++k) dst[k * RW + tid] = T[0][k];
     }
-    // samples 0 and 1 in flight (sample 0 again if there is no sample 1)
-    {
-        const int64_t t1 = outer > 1 ? 1 : 0;
-        const f4* x0 = reinterpret_cast<const f4*>(x);
-        const f4* x1 = reinterpret_cast<const f4*>(x + t1 * inner);
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) tb[k] = x0[addr(k)];
-        kb = x[0];
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) tc[k] = x1[addr(k)];
-        kc = x[t1 * inner];
-        ka = kb;
-    }
+    for (int r = 0; r < NT - LAG; ++r) load(r, r);
     __syncthreads();  // prologue: w/b in LDS
 
-    // One iteration: Cv holds sample t (shift Kc, loaded two iterations ago),
-    // the third tile sample t+1 (in flight), Pv sample t-1; once Pv is
-    // normalized it receives sample t+2 (shift Kp; past the last sample it
-    // re-reads the last one).  So two samples' loads are in flight while a
-    // third is reduced.  The loop unrolls three iterations with the tiles'
-    // roles rotated, so no tile is ever copied: a copy would wait for the
-    // loads that fill it.
-    auto step = [&](int64_t t, f4 (&Pv)[F4PT], f4 (&Cv)[F4PT], float& Kp, float Kc)
-                    __attribute__((always_inline)) {
+    // One iteration with its register tiles fixed at compile time: the loop
+    // below unrolls NT of them, so no tile is ever copied (a copy would wait
+    // for the loads that fill it).
+    auto step = [&](int64_t t, auto U, auto NORM) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;     // tile of sample t
+        constexpr int r = (u + NT - LAG) % NT;    // tile of sample t - LAG
+        constexpr bool norm = decltype(NORM)::value;  // t >= LAG
         // the per-row offsets are recomputed in every iteration instead of
-        // being kept live across the loop (registers hold three x tiles)
+        // being kept live across the loop (registers hold NT x tiles)
         asm volatile("" : "+v"(off0));
         if (t < outer) {
+            const float K = s_K[t & 3];
             f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) {
-                const f4 d = valid(k) ? Cv[k] - Kc : f4(0.0f);
+                const f4 d = valid(k) ? T[u][k] - K : f4(0.0f);
                 a1 += d;
                 a2 += d * d;
             }
@@ -977,32 +1025,30 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                 red[t & 1][2 * (tid / kWave) + 1] = t2;
             }
         }
-        __syncthreads();  // barrier t: sample t-1's statistics are in LDS
-        if (t >= 1) {
-            const f4 st = s_stats[(t - 1) & 1];
-            f4* y4 = reinterpret_cast<f4*>(y + (t - 1) * inner);
+        __syncthreads();  // barrier t: sample t-LAG's statistics are in LDS
+        if constexpr (norm) {
+            const int64_t s = t - LAG;
+            const f4 st = s_stats[s & 1];
+            f4* y4 = reinterpret_cast<f4*>(y + s * inner);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) {
                 if (valid(k)) {
-                    const f4 tt = ((Pv[k] - st.x) - st.y) * st.z;
+                    const f4 tt = ((T[r][k] - st.x) - st.y) * st.z;
                     const f4 wv = w ? w_s[k * RW + tid] : f4(1.0f);
                     const f4 bv = bias ? b_s[k * RW + tid] : f4(0.0f);
                     st_nt(tt * wv + bv, y4 + index(k));
                 }
             }
         }
-        const int64_t tn = t + 2 < outer ? t + 2 : outer - 1;
-        const f4* xn = reinterpret_cast<const f4*>(x + tn * inner);
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) Pv[k] = xn[addr(k)];
-        Kp = x[tn * inner];
+        // tile r now receives sample t-LAG+NT (in the first LAG iterations it
+        // is still empty); the load is unconditional so that every iteration
+        // issues the same memory operations
+        load(r, t - LAG + NT);
     };
-    for (int64_t t = 0; t <= outer; t += 3) {
-        step(t, ta, tb, ka, kb);
-        if (t + 1 > outer) break;
-        step(t + 1, tb, tc, kb, kc);
-        if (t + 2 > outer) break;
-        step(t + 2, tc, ta, kc, ka);
+    // the first LAG iterations have nothing to normalize yet; from then on
+    // every iteration does (t < steps = outer + LAG, and outer >= 1)
+    ctl_first_steps<0, LAG>(step);
+    for (int64_t t0 = LAG; ctl_steps<0, NT, LAG>(t0, steps, step); t0 += NT) {
     }
 }
 
@@ -1206,7 +1252,8 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * rw * sizeof(f4);
     if (lds + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
     const void* fn = DW == 0 ? reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>)
-                             : reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW == 0 ? 1 : DW>);
+                             : reinterpret_cast<const void*>(
+                                   &ln_single_ctl_kernel<F4PT, DW == 0 ? 1 : DW, NORMFWD_LN_CTL_LAG>);
     const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
     if (coresident(fn, lds, threads) < P) return false;
     int64_t pcap = P_cap;
