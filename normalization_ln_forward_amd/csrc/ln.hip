@@ -65,7 +65,11 @@ constexpr int kLnThreads = 256;
 // 128-byte line (atomics that meet on one line serialize).
 constexpr int kCounterStride = 32;  // uint32 words
 constexpr int kRing = 4;
-constexpr uint32_t kSpinLimit = 1u << 22;
+// Polls before a wait gives up (sets the control block's error word and
+// goes on): ~0.3-0.5 s, thousands of times the longest wait of a healthy
+// launch, so a launch whose workgroups are not all resident ends instead of
+// hanging.
+constexpr uint32_t kSpinLimit = 1u << 18;
 
 // Split schedule tuning: elements per partial-moment workgroup, rows in
 // flight per thread in the moments pass, XCD-aware row order in the
@@ -112,6 +116,7 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 #ifndef NORMFWD_LN_CTL_LAG
 #define NORMFWD_LN_CTL_LAG 2
 #endif
+
 #ifndef NORMFWD_LN_FUSE_BELOW
 #define NORMFWD_LN_FUSE_BELOW 1024
 #endif
@@ -1199,7 +1204,11 @@ static bool device_info(DeviceInfo& out)
 }
 
 // Co-resident workgroups of `fn` with `lds` bytes of dynamic LDS on this
-// device (queried once per device, kernel and LDS size).
+// device (queried once per device, kernel and LDS size).  A workgroup whose
+// wave count is not a multiple of the CU's 4 SIMDs is counted once per CU
+// whatever the occupancy query says: the query assumes its waves can be
+// spread over the SIMDs freely, and a tuning run of such a kernel at two
+// workgroups per CU (5 waves of 168 VGPRs each) did not finish.
 static int coresident(const void* fn, size_t lds, int threads)
 {
     struct Entry {
@@ -1223,8 +1232,10 @@ static int coresident(const void* fn, size_t lds, int threads)
     int cap = 0;
     if (lds == 0 || hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess) {
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) == hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) == hipSuccess) {
+            if ((threads / kWave) % 4 != 0) per_cu = std::min(per_cu, 1);
             cap = d.cus * per_cu;
+        }
     }
     (void)hipGetLastError();
     if (n_cache < 64) cache[n_cache++] = Entry{dev, fn, lds, threads, cap};
@@ -1300,7 +1311,6 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
         if (protocol == 1) {  // control wave, tagged gather
             NORMFWD_TRY_HOLD(8, 8)
             NORMFWD_TRY_HOLD(4, 8)
-            NORMFWD_TRY_HOLD(8, 4)
         }
         // last workgroup merges (protocol 2, or shapes the above cannot hold)
         NORMFWD_TRY_HOLD(NORMFWD_LN_HOLD_F4PT, 0)
