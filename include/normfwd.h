@@ -10,8 +10,7 @@
  *
  * Conventions shared by every entry point:
  *   - Tensors are fp32, contiguous, row-major, in device memory (HBM).  The
- *     caller owns every buffer; the library never allocates, frees or
- *     synchronizes.
+ *     caller owns every buffer; the library never allocates or frees.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued on it; calls return as soon as the work is
  *     enqueued.
@@ -31,6 +30,7 @@
  *   - Empty work is a no-op that returns NORMFWD_OK without inspecting the
  *     pointers: ln with outer == 0, gn with N == 0, rms with B == 0 or
  *     S == 0, fc with N == 0 (fc with K == 0 computes h = b).
+ *   - Only ln_forward_workspace_check synchronizes (it reads a result back).
  *   - Errors are returned, never thrown: arguments are validated before
  *     anything is enqueued, so a non-OK return from validation means nothing
  *     was launched.  normfwd_last_error() then describes the failure
@@ -52,6 +52,7 @@ typedef int normfwd_status;
 #define NORMFWD_ERR_UNSUPPORTED 2 /* valid arguments this build does not handle         */
 #define NORMFWD_ERR_WORKSPACE 3   /* workspace null or smaller than the size query says */
 #define NORMFWD_ERR_HIP 4         /* a HIP runtime call or kernel launch failed         */
+#define NORMFWD_ERR_INCOMPLETE 5  /* a single-kernel LayerNorm gave up waiting (below)  */
 
 /* Static string naming a status code ("unknown status" for other values). */
 const char* normfwd_status_string(normfwd_status status);
@@ -130,6 +131,19 @@ size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
  * captured HIP graph).  Required before a workspace's first use with each
  * (outer, inner). */
 normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Health check of the single-kernel variants (ln_forward variant 1 and 2).
+ * Their workgroups wait for one another; each wait gives up after a bounded
+ * number of polls (a fraction of a second), which can only happen if the
+ * workgroups of the cooperative launch were not all resident, and then
+ * records the failure in the workspace instead of hanging.  This call waits
+ * for the work queued on `stream` (it synchronizes, unlike every other entry
+ * point, so it cannot be captured in a graph), reads that record and clears
+ * it.  Returns NORMFWD_OK if no launch that used `workspace` since the last
+ * check (or since ln_forward_workspace_init) gave up, NORMFWD_ERR_INCOMPLETE
+ * if one did (its y and statistics are not valid), NORMFWD_ERR_WORKSPACE for
+ * a null, misaligned or short buffer, NORMFWD_ERR_HIP if the copy fails. */
+normfwd_status ln_forward_workspace_check(void* workspace, size_t workspace_bytes, void* stream);
 
 normfwd_status ln_forward(const float* x, const float* weight, const float* bias, float* y,
                           int64_t outer, int64_t inner, float eps,

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     ln_forward,
     ln_forward_apply,
     ln_forward_stats,
+    ln_forward_workspace_check,
     ln_forward_workspace_init,
     ln_forward_workspace_size,
     prepare,

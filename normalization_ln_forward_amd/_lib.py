@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libnormfwd.so")
 
 NORMFWD_OK = 0
 STATUS_NAMES = {0: "NORMFWD_OK", 1: "NORMFWD_ERR_INVALID", 2: "NORMFWD_ERR_UNSUPPORTED",
-                3: "NORMFWD_ERR_WORKSPACE", 4: "NORMFWD_ERR_HIP"}
+                3: "NORMFWD_ERR_WORKSPACE", 4: "NORMFWD_ERR_HIP", 5: "NORMFWD_ERR_INCOMPLETE"}
 
 # Every symbol include/normfwd.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -35,6 +35,7 @@ SIGNATURES = {
     "normfwd_time_next_kernel": (_ST, [_P, _P]),
     "ln_forward_workspace_size": (_SZ, [_I64, _I64]),
     "ln_forward_workspace_init": (_ST, [_P, _SZ, _P]),
+    "ln_forward_workspace_check": (_ST, [_P, _SZ, _P]),
     "ln_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P, _P, ctypes.c_int, _P]),
     "ln_forward_stats": (_ST, [_P, _I64, _I64, _F, _P, _SZ, _P, _P, _P]),
     "ln_forward_apply": (_ST, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
@@ -176,6 +177,12 @@ def ln_forward_workspace_size(outer, inner):
 
 def ln_forward_workspace_init(workspace):
     _check(lib().ln_forward_workspace_init(_ptr(workspace), workspace.numel(), _stream(workspace.device)))
+
+
+def ln_forward_workspace_check(workspace):
+    """Raise NormFwdError (NORMFWD_ERR_INCOMPLETE) if a single-kernel call that used ``workspace``
+    since the last check gave up waiting; waits for the current stream, then clears the record."""
+    _check(lib().ln_forward_workspace_check(_ptr(workspace), workspace.numel(), _stream(workspace.device)))
 
 
 def _ln_shape(x, normalized_ndim):

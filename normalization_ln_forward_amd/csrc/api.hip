@@ -108,6 +108,7 @@ const char* normfwd_status_string(normfwd_status s)
         case NORMFWD_ERR_UNSUPPORTED: return "NORMFWD_ERR_UNSUPPORTED: arguments valid but not supported";
         case NORMFWD_ERR_WORKSPACE: return "NORMFWD_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case NORMFWD_ERR_HIP: return "NORMFWD_ERR_HIP: HIP runtime error";
+        case NORMFWD_ERR_INCOMPLETE: return "NORMFWD_ERR_INCOMPLETE: a single-kernel launch gave up waiting";
         default: return "unknown status";
     }
 }
@@ -128,6 +129,27 @@ normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes
     (void)hipGetLastError();
     return hip_status(normfwd::launch_zero_words(workspace, workspace_bytes, (hipStream_t)stream),
                       "ln_forward_workspace_init launch");
+}
+
+normfwd_status ln_forward_workspace_check(void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!workspace || workspace_bytes < 256 || !aligned256(workspace))
+        return fail(NORMFWD_ERR_WORKSPACE, "ln_forward_workspace_check: need a 256-byte aligned workspace of >= 256 bytes");
+    (void)hipGetLastError();
+    hipStream_t st = (hipStream_t)stream;
+    char* word_ptr = static_cast<char*>(workspace) + normfwd::kLnErrorWordOffset;
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, word_ptr, sizeof(word), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_status(e, "ln_forward_workspace_check: reading the error word");
+    if (word == 0) return ok();
+    const uint32_t zero = 0;
+    e = hipMemcpyAsync(word_ptr, &zero, sizeof(zero), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_status(e, "ln_forward_workspace_check: clearing the error word");
+    return fail(NORMFWD_ERR_INCOMPLETE,
+                "a single-kernel ln_forward on this workspace gave up waiting for another workgroup; "
+                "its output is not valid");
 }
 
 normfwd_status ln_forward_stats(const float* x, int64_t outer, int64_t inner, float eps, void* workspace,

@@ -66,6 +66,9 @@ struct LnLayout {
     size_t off_part;
     size_t total;
 };
+// Byte offset, in an LN workspace, of the word the single kernels set when
+// a wait gives up (the control block starts every LN workspace).
+constexpr size_t kLnErrorWordOffset = 8;
 LnLayout ln_layout(int64_t outer, int64_t inner);
 
 hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float eps, void* ws,

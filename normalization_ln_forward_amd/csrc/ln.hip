@@ -43,6 +43,7 @@
 #include "internal.hpp"
 
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 #include <mutex>
 
@@ -59,6 +60,7 @@ struct LnCtrl {
     uint32_t pad[61];
 };
 static_assert(sizeof(LnCtrl) == 256, "control block is 256 bytes");
+static_assert(offsetof(LnCtrl, error) == kLnErrorWordOffset, "error word where the API reads it");
 
 constexpr int kLnThreads = 256;
 // The single kernel's arrival counters: a ring of kRing, each on its own

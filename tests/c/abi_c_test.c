@@ -107,7 +107,10 @@ static int run(void)
                 printf("ln_forward: %s\n", normfwd_last_error());
                 return 3;
             }
-            hipStreamSynchronize(st);
+            if (ln_forward_workspace_check(dws, wsb, st) != NORMFWD_OK) {
+                printf("ln_forward_workspace_check: %s\n", normfwd_last_error());
+                return 3;
+            }
             hipMemcpy(y, dy, n * sizeof(float), hipMemcpyDeviceToHost);
             double *xd = promote(x, n), *wd = promote(w, (size_t)inner), *bd = promote(b, (size_t)inner);
             double* o = (double*)malloc(n * sizeof(double));

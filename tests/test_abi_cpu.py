@@ -75,6 +75,12 @@ def test_ln_validation():
     assert lib.ln_forward_workspace_size(0, 5) == 0
     st, _ = _err(lib.ln_forward_workspace_init(None, 1024, None))
     assert st == 3
+    st, _ = _err(lib.ln_forward_workspace_check(None, 1024, None))
+    assert st == 3
+    st, _ = _err(lib.ln_forward_workspace_check(ctypes.c_void_p(0x200010), 1024, None))
+    assert st == 3
+    st, _ = _err(lib.ln_forward_workspace_check(FAKE_WS, 255, None))
+    assert st == 3
 
 
 def test_ln_workspace_size_monotone():

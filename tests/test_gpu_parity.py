@@ -418,6 +418,29 @@ def test_ln_alternating_shapes_and_workspace_reinit():
                 _assert_close(_np(y), refs[s], what=f"ln {s} variant {variant}, own workspace")
 
 
+def test_workspace_check_reports_and_clears_a_failed_wait():
+    """ln_forward_workspace_check: OK after healthy single-kernel calls; a recorded give-up (planted from
+    the host in the workspace's error word, as a kernel whose wait ran out would leave it) is reported as
+    NORMFWD_ERR_INCOMPLETE once and then cleared."""
+    _say("ln workspace check")
+    s = (6, 40000)
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=s, normalized_ndim=1, seed=77)
+    ref = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]))
+    _, ws = nf.alloc_workspace(nf.ln_forward_workspace_size(*s), "cuda")
+    nf.ln_forward_workspace_init(ws)
+    for variant in (1, 2, 0):
+        y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
+        nf.ln_forward_workspace_check(ws)
+        _assert_close(_np(y), ref, what=f"ln {s} variant {variant} before the check")
+    word = ws.view(torch.int32)[2:3]
+    word.fill_(1)
+    with pytest.raises(nf.NormFwdError) as e:
+        nf.ln_forward_workspace_check(ws)
+    assert e.value.status == 5
+    assert int(word.item()) == 0
+    nf.ln_forward_workspace_check(ws)
+
+
 def test_time_next_kernel_stamps_one_launch():
     """normfwd_time_next_kernel: the next launch (ordinary or cooperative) stamps the armed events, later
     launches leave them alone, and the results are unchanged."""
