@@ -213,13 +213,14 @@ def _ln_workspace(device, outer, inner):
     return hit[1]
 
 
-def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, variant=0, out=None,
+def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, variant=3, out=None,
                workspace=None, mean_out=None, rstd_out=None):
     """LayerNorm over the trailing ``normalized_ndim`` dims (default: all but dim 0).
 
     ``variant`` 0 = split (moments kernel + normalize kernel), 1 = single
     cooperative kernel (control wave, tagged exchange), 2 = single cooperative
-    kernel in which the last workgroup of each sample merges it.  A caller-provided ``workspace`` must have been passed
+    kernel in which the last workgroup of each sample merges it, 3 (default) =
+    the library's choice by shape (1 where it measured fastest, else 0).  A caller-provided ``workspace`` must have been passed
     through ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if
     None).
     """

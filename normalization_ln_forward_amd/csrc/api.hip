@@ -185,10 +185,10 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
                           int64_t inner, float eps, void* workspace, size_t workspace_bytes, float* mean_out,
                           float* rstd_out, int variant, void* stream)
 {
-    if (outer == 0 && inner >= 0 && variant >= 0 && variant <= 2) return ok();  // empty batch: nothing to do
+    if (outer == 0 && inner >= 0 && variant >= 0 && variant <= 3) return ok();  // empty batch: nothing to do
     normfwd_status s = check_ln(x, y, outer, inner, eps);
     if (s != NORMFWD_OK) return s;
-    if (variant < 0 || variant > 2) return fail(NORMFWD_ERR_INVALID, "ln_forward: variant must be 0, 1 or 2");
+    if (variant < 0 || variant > 3) return fail(NORMFWD_ERR_INVALID, "ln_forward: variant must be 0, 1, 2 or 3");
     const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
     s = check_ws(workspace, workspace_bytes, lay.total, "ln_forward");
     if (s != NORMFWD_OK) return s;
@@ -197,6 +197,7 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
     hipError_t re = hipSuccess;
     if (normfwd::launch_ln_rows(x, weight, bias, y, outer, inner, eps, mean_out, rstd_out, st, re))
         return hip_status(re, "ln_forward (one workgroup per sample) launch");
+    if (variant == 3) variant = normfwd::ln_auto_variant(x, weight, bias, y, outer, inner);
     if (variant != 0)
         return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
                                                     rstd_out, variant, st),

@@ -86,6 +86,10 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
                             int64_t inner, float eps, void* ws, const LnLayout& lay, float* mean_out,
                             float* rstd_out, int protocol, hipStream_t st);
 
+// ln_forward variant 3: the schedule measured fastest for this shape on this
+// device (1 = the control-wave single kernel, else 0 = split).
+int ln_auto_variant(const float* x, const float* w, const float* b, const float* y, int64_t outer, int64_t inner);
+
 // Fill bytes/4 32-bit words with zero (a kernel, not a memset, so the call
 // can sit inside a captured HIP graph).
 hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t st);

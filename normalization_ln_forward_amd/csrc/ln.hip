@@ -1291,6 +1291,25 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
     return (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
 }
 
+// Measured on MI355X (split against the control-wave kernel, one call per
+// shape): [16, 4M] 135 vs 117 us, [8, 4M] 71 vs 71 us, [4, 4M] 41 vs 46 us,
+// [32, 1M] 68 vs 118 us, [64, 256K] 34 vs 164 us.  The single kernel pays a
+// cooperative launch (~17 us) and one workgroup barrier plus a cross-
+// workgroup exchange per sample, and saves one read of x; it wins only where
+// its tile of 8 float4 x 512 threads per sample puts a workgroup on every CU
+// and there are enough samples to amortize the launch.
+int ln_auto_variant(const float* x, const float* w, const float* b, const float* y, int64_t outer, int64_t inner)
+{
+    if (outer < 8 || !ln_single_supported(inner, x, w, b, y)) return 0;
+    DeviceInfo d;
+    if (!device_info(d)) return 0;
+    const int64_t P = ceil_div(ceil_div(inner / 4, (int64_t)8 * kWave), (int64_t)8);
+    if (P < d.cus) return 0;
+    const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * 8 * 8 * kWave * sizeof(f4);
+    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG>);
+    return coresident(fn, lds, 9 * kWave) >= P ? 1 : 0;
+}
+
 hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                             int64_t inner, float eps, void* ws, const LnLayout& lay, float* mean_out,
                             float* rstd_out, int protocol, hipStream_t st)

@@ -18,7 +18,7 @@ from . import _lib
 class LayerNorm(torch.nn.Module):
     """LayerNorm over the trailing ``normalized_shape`` dims (LN page, turn 1)."""
 
-    def __init__(self, normalized_shape, eps=1e-5, elementwise_affine=True, variant=0, device=None):
+    def __init__(self, normalized_shape, eps=1e-5, elementwise_affine=True, variant=3, device=None):
         super().__init__()
         if isinstance(normalized_shape, int):
             normalized_shape = (normalized_shape,)

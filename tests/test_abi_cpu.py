@@ -133,8 +133,9 @@ def test_empty_work_is_a_no_op_that_touches_nothing():
     """Empty batches return OK before any pointer is inspected or anything is launched (so this runs
     without a GPU): NULL everywhere, no workspace."""
     lib = _lib.lib()
-    for variant in (0, 1, 2):
+    for variant in (0, 1, 2, 3):
         assert lib.ln_forward(None, None, None, None, 0, 4096, 1e-5, None, 0, None, None, variant, None) == 0
+    assert lib.ln_forward(None, None, None, None, 0, 4096, 1e-5, None, 0, None, None, 4, None) != 0
     assert lib.ln_forward_stats(None, 0, 4096, 1e-5, None, 0, None, None, None) == 0
     assert lib.ln_forward_apply(None, None, None, None, 0, 4096, None, 0, None) == 0
     assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 8192, 512, 1e-5, 0.01, None) == 0

@@ -244,6 +244,19 @@ def test_ln_full_size(name, variant):
     assert torch.equal(y, y2), "not bitwise deterministic"
 
 
+def test_ln_auto_variant_picks_the_measured_fastest():
+    """variant 3 runs the single-read kernel on the benchmark shape and the split schedule where that
+    measured faster (few samples, or samples too small to put a workgroup on every CU): its output is
+    bitwise that of the variant it picks."""
+    for shape, pick in (((16, 4194304), 1), ((4, 4194304), 0), ((64, 262144), 0)):
+        _say(f"ln auto {shape}")
+        d = synth.make("ln_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=shape[0])
+        auto = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=3)
+        assert torch.equal(auto, nf.ln_forward(d["x"], d["weight"], d["bias"], variant=pick)), shape
+        del d, auto
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("variant", [1, 2])
 def test_ln_single_kernel_repeated_and_split_halves(variant):
     """Many back-to-back single-kernel launches on one workspace stay bitwise equal and
