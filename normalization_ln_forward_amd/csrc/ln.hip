@@ -4,10 +4,10 @@
 // weight and bias).
 //
 // One sample is 4,194,304 floats (16 MiB) in the LN page's problem, far
-// more than one workgroup should reduce, so each sample is split into P
-// contiguous chunks (LN page, turn 2: many blocks per sample write partial
-// moments to a workspace, a small step reduces them per sample, a third
-// pass normalizes).
+// more than one workgroup should reduce, so each sample is spread over P
+// workgroups (LN page, turn 2: many blocks per sample write partial moments
+// to a workspace, a small step reduces them per sample, a third pass
+// normalizes).
 //
 // Numerics (the page's own one-pass E[x^2] - mean^2 loses everything when
 // |mean| >> std, e.g. N(100, 0.01) data):
@@ -15,9 +15,10 @@
 //     (for data clustered around K the subtraction is exact), one sum and
 //     one sum of squares per float4 component;
 //   * lane sums are widened to fp64 and reduced over the workgroup in a fixed
-//     order; the chunk's moments (n, mean, M2) are stored in fp64;
-//   * chunk moments are merged with Chan's pairwise update (LN page, turn 2
-//     derives the same merge for Welford partials) in chunk order;
+//     order; a workgroup's moments (n, mean, M2) are stored in fp64;
+//   * the workgroups' moments are merged with Chan's pairwise update (LN
+//     page, turn 2 derives the same merge for Welford partials) in
+//     workgroup order;
 //   * the mean is handed to the normalize pass as an fp32 pair hi + lo, so
 //     (x - hi) - lo keeps ~48 bits of the mean.
 //
@@ -36,6 +37,8 @@
 //          ln_single_hold_kernel (variant 2): the last workgroup to
 //          deliver a sample's partial merges it and announces the
 //          statistics with a flag (LN page, turn 6: last-block-done).
+//   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
+//          shape, from measurements.
 //   short samples (inner <= 8192): ln_row_kernel, one workgroup per sample.
 // Cross-workgroup data is only ever accessed with device-coherent atomic
 // loads and stores (see the protocol notes below), never with fences.
@@ -830,6 +833,7 @@ __device__ __forceinline__ double untag(double v)
 // counters or flags.  (The last-workgroup-merges protocol of
 // ln_single_hold_kernel measured slower here: its chain of arrival atomic,
 // merge and flag is longer than one sample's streaming time.)
+//
 // Iterations of ln_single_ctl_kernel with compile-time tile indices:
 // ctl_first_steps runs iterations 0 .. LAG-1 (moments only); ctl_steps runs
 // t0 + U, t0 + U + 1, ... for U < NT (iteration t uses tile (t0 + U) % NT,
