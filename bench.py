@@ -128,8 +128,9 @@ def main():
         t = time_launches(torch, stream, lambda i: steps[i % R](), args.steps, args.warmup, nf=nf)
         ms_per_step = t["wall_ms"]
         # The single-read kernel moves x once, so its roofline is priced on the bytes it must move
-        # (x + y + weight + bias).  A cooperative launch cannot stamp events itself: the armed events
-        # bracket each launch, so its duration here includes the cooperative launch's own cost.
+        # (x + y + weight + bias).  Variant 1 is an ordinary launch that stamps the armed events itself
+        # (kernel start to end); variant 2's cooperative launch cannot, so there the events bracket each
+        # launch and its duration includes the cooperative launch's own cost.
         dom_kernel = "ln_single_ctl_kernel" if variant == 1 else "ln_single_hold_kernel"
         dom_bytes, avg_ms = LN_NORMALIZE_BYTES, t["kernel_ms"]
     else:

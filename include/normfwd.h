@@ -67,7 +67,7 @@ const char* normfwd_last_error(void);
  * kernel's duration with no marker packets between kernels.  For an entry
  * point that launches several kernels, the first one is timed (ln_forward
  * variant 0: the moments kernel; use ln_forward_apply to time the normalize
- * kernel).  The cooperative launch of ln_forward variant 1 cannot carry
+ * kernel).  The cooperative launch of ln_forward variant 2 cannot carry
  * events; there they are recorded as markers just before and after it.  The
  * events stay armed until a launch takes them or this is called again
  * (NULL, NULL disarms).  Always NORMFWD_OK. */
@@ -103,17 +103,24 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 workgroup of each sample to finish (LN page, turn 6;
  *                 nothing waits, so any grid size works), otherwise by a
  *                 merge kernel;
- *             1 = single kernel: one cooperative launch in which every
- *                 workgroup keeps its share of each sample in registers
- *                 between the moments pass and the normalize pass (x is
- *                 read from HBM once).  A control wave per workgroup
- *                 exchanges the workgroups' moments of each sample through
- *                 generation-tagged words (no atomics) while the data waves
- *                 stream the next samples;
+ *             1 = single kernel: one launch of at most one workgroup per
+ *                 CU in which every workgroup keeps its share of each
+ *                 sample in registers between the moments pass and the
+ *                 normalize pass (x is read from HBM once).  A control wave
+ *                 per workgroup exchanges the workgroups' moments of each
+ *                 sample through generation-tagged words (no atomics) while
+ *                 the data waves stream the next samples.  It is an
+ *                 ordinary launch: if a workgroup is not resident (another
+ *                 kernel holds its CU), the others stop waiting for its
+ *                 moments after a bounded number of polls and compute them
+ *                 from x themselves, bit for bit the same, so the result
+ *                 never depends on residency (a forced-recompute GPU test
+ *                 checks that bitwise);
  *             2 = single kernel in which the last workgroup to deliver a
  *                 sample's partial merges it and announces the statistics
  *                 with a flag (LN page, turn 6: last-block-done), the others
- *                 waiting for that flag.
+ *                 waiting for that flag.  A cooperative launch, since its
+ *                 waits need every workgroup resident.
  *             3 = automatic: variant 1 where it measured fastest (at least
  *                 8 samples, and a sample spread over one workgroup per CU,
  *                 e.g. [16, 4194304]), otherwise variant 0.  The choice
@@ -137,11 +144,13 @@ size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
  * (outer, inner). */
 normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
-/* Health check of the single-kernel variants (ln_forward variant 1 and 2).
- * Their workgroups wait for one another; each wait gives up after a bounded
+/* Health check of the last-workgroup-merges kernel (ln_forward variant 2).
+ * Its workgroups wait for one another; each wait gives up after a bounded
  * number of polls (a fraction of a second), which can only happen if the
  * workgroups of the cooperative launch were not all resident, and then
- * records the failure in the workspace instead of hanging.  This call waits
+ * records the failure in the workspace instead of hanging.  (Variant 1
+ * never records one: a workgroup whose moments do not arrive has them
+ * computed by the others.)  This call waits
  * for the work queued on `stream` (it synchronizes, unlike every other entry
  * point, so it cannot be captured in a graph), reads that record and clears
  * it.  Returns NORMFWD_OK if no launch that used `workspace` since the last

@@ -218,7 +218,7 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
     """LayerNorm over the trailing ``normalized_ndim`` dims (default: all but dim 0).
 
     ``variant`` 0 = split (moments kernel + normalize kernel), 1 = single
-    cooperative kernel (control wave, tagged exchange), 2 = single cooperative
+    kernel (control wave, tagged exchange; x read once), 2 = single cooperative
     kernel in which the last workgroup of each sample merges it, 3 (default) =
     the library's choice by shape (1 where it measured fastest, else 0).  A caller-provided ``workspace`` must have been passed
     through ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if

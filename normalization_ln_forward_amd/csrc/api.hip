@@ -83,6 +83,19 @@ int64_t max_grid_items()
     return limit;
 }
 
+uint32_t ln_force_recompute()
+{
+    static const uint32_t k = [] {
+        uint32_t v = 0;
+        if (const char* e = std::getenv("NORMFWD_LN_FORCE_RECOMPUTE")) {
+            const long long n = std::atoll(e);
+            if (n > 0 && n <= (1ll << 30) && (n & (n - 1)) == 0) v = (uint32_t)n;
+        }
+        return v;
+    }();
+    return k;
+}
+
 LaunchEvents take_launch_events()
 {
     const LaunchEvents e = g_armed;

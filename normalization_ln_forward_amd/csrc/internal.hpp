@@ -69,6 +69,14 @@ struct LnLayout {
 // Byte offset, in an LN workspace, of the word the single kernels set when
 // a wait gives up (the control block starts every LN workspace).
 constexpr size_t kLnErrorWordOffset = 8;
+// Byte offset of the control-wave kernel's count of workgroup sums that a
+// reader computed itself (after waiting past its spin limit, or forced).
+constexpr size_t kLnRecomputedWordOffset = 12;
+// Test knob, read once from NORMFWD_LN_FORCE_RECOMPUTE (0 = off): a power of
+// two k makes the control-wave kernel ignore the published sums of every
+// workgroup j with j % k == k - 1 and compute them from x instead, which
+// must give bitwise the same result (other values are ignored).
+uint32_t ln_force_recompute();
 LnLayout ln_layout(int64_t outer, int64_t inner);
 
 hipError_t launch_ln_stats(const float* x, int64_t outer, int64_t inner, float eps, void* ws,

@@ -27,16 +27,19 @@
 //          moments workgroups on; below that the last workgroup of each
 //          sample merges it) -> ln_normalize_rows_kernel (or
 //          ln_normalize_kernel for short samples); x is read twice.
-//   single kernels (variants 1 and 2): one cooperative launch; workgroup p
-//          keeps its rows of every sample in VGPRs from the moments pass to
-//          the normalize pass, so x is read once, and the workgroups
-//          exchange each sample's moments in the middle:
-//          ln_single_ctl_kernel (variant 1): a control wave per workgroup
-//          publishes generation-tagged sums and gathers everyone's, while
-//          the data waves stream the next samples;
-//          ln_single_hold_kernel (variant 2): the last workgroup to
-//          deliver a sample's partial merges it and announces the
-//          statistics with a flag (LN page, turn 6: last-block-done).
+//   single kernels (variants 1 and 2): one launch of at most one workgroup
+//          per CU; workgroup p keeps its rows of every sample in VGPRs from
+//          the moments pass to the normalize pass, so x is read once, and
+//          the workgroups exchange each sample's moments in the middle:
+//          ln_single_ctl_kernel (variant 1, an ordinary launch): a control
+//          wave per workgroup publishes generation-tagged sums and gathers
+//          everyone's, while the data waves stream the next samples; sums
+//          that do not arrive within a bounded wait (their workgroup is not
+//          resident) are computed by the reader from x, with the same bits;
+//          ln_single_hold_kernel (variant 2, a cooperative launch): the
+//          last workgroup to deliver a sample's partial merges it and
+//          announces the statistics with a flag (LN page, turn 6:
+//          last-block-done).
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
 //          shape, from measurements.
 //   short samples (inner <= 8192): ln_row_kernel, one workgroup per sample.
@@ -59,11 +62,13 @@ struct alignas(32) Partial {
 struct LnCtrl {
     uint32_t gen;    // generation: incremented by the last workgroup of each single-kernel launch
     uint32_t done;   // completion counter of the current launch (returns to 0)
-    uint32_t error;  // set to 1 if a wait ran past its spin limit
-    uint32_t pad[61];
+    uint32_t error;  // set to 1 if a wait ran past its spin limit (last-workgroup-merges kernel)
+    uint32_t recomputed;  // control-wave kernel: workgroup sums computed by a reader instead (diagnostic)
+    uint32_t pad[60];
 };
 static_assert(sizeof(LnCtrl) == 256, "control block is 256 bytes");
 static_assert(offsetof(LnCtrl, error) == kLnErrorWordOffset, "error word where the API reads it");
+static_assert(offsetof(LnCtrl, recomputed) == kLnRecomputedWordOffset, "recompute count where the tests read it");
 
 constexpr int kLnThreads = 256;
 // The single kernel's arrival counters: a ring of kRing, each on its own
@@ -75,6 +80,10 @@ constexpr int kRing = 4;
 // launch, so a launch whose workgroups are not all resident ends instead of
 // hanging.
 constexpr uint32_t kSpinLimit = 1u << 18;
+// The control-wave kernel, once one of its waits has run out: later waits
+// give up after this many polls (~1-2 ms), since the missing workgroup is
+// most likely still not resident.
+constexpr uint32_t kSpinLimitAfterMiss = 1u << 10;
 
 // Split schedule tuning: elements per partial-moment workgroup, rows in
 // flight per thread in the moments pass, XCD-aware row order in the
@@ -806,6 +815,70 @@ __device__ __forceinline__ double untag(double v)
     return __longlong_as_double((long long)((uint64_t)__double_as_longlong(v) & ~0xFFull));
 }
 
+// One float4 of d = x - K into a thread's running sums of d and d^2.  Every
+// place that must reproduce these sums bit for bit goes through here, so
+// they round the same way (the square and the add contract to one fused
+// multiply-add on gfx950).
+__device__ __forceinline__ void shifted_acc(f4& a1, f4& a2, const f4 d)
+{
+    a1 += d;
+    a2 += d * d;
+}
+
+// A wave's sums of its lanes' (a1, a2), widened to fp64 in a fixed order;
+// every lane ends with the same bits (each butterfly step adds the same two
+// values on both partners).
+__device__ __forceinline__ void wave_moments(const f4 a1, const f4 a2, double& t1, double& t2)
+{
+    t1 = wave_sum(((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w));
+    t2 = wave_sum(((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w));
+}
+
+// The sums workgroup j of ln_single_ctl_kernel publishes for one sample
+// (xs: the sample's float4s), computed by one whole wave from x: lane l
+// replays thread w * 64 + l of j's data waves for w = 0 .. DW-1 with the
+// same elements, the same order of additions and the same wave reduction,
+// and the wave totals are added in wave order, so the result has exactly
+// the bits j itself would publish.  Used when j's sums do not arrive.
+// Out of line: inlined, its registers pushed the data waves' loop into
+// spills.  The sums come back by value (in registers, not on the stack).
+struct CtlSums {
+    double s1, s2;
+};
+template <int F4PT, int DW>
+__device__ __noinline__ CtlSums ctl_recompute_sums(const f4* xs, float K, uint32_t j, uint32_t P, int64_t nv)
+{
+    double s1 = 0.0, s2 = 0.0;
+    constexpr int RW = DW * kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t stride = P * (uint32_t)RW;
+    for (int w = 0; w < DW; ++w) {
+        const uint32_t off0 = j * (uint32_t)RW + (uint32_t)(w * kWave + lane);
+        f4 v[F4PT];
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) {
+            const uint32_t idx = off0 + (uint32_t)k * stride;
+            v[k] = (int64_t)idx < nv ? ld_nt(xs + idx) : f4(0.0f);
+        }
+        f4 a1 = f4(0.0f), a2 = f4(0.0f);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) {
+            const uint32_t idx = off0 + (uint32_t)k * stride;
+            shifted_acc(a1, a2, (int64_t)idx < nv ? v[k] - K : f4(0.0f));
+        }
+        double t1, t2;
+        wave_moments(a1, a2, t1, t2);
+        if (w == 0) {
+            s1 = t1;
+            s2 = t2;
+        } else {
+            s1 += t1;
+            s2 += t2;
+        }
+    }
+    return CtlSums{s1, s2};
+}
+
 // Single-read schedule with a control wave.  DW data waves hold the
 // workgroup's rows as above (rows are DW * 64 float4 wide here); one more
 // wave holds no data and runs the cross-workgroup exchange, so that the
@@ -863,7 +936,7 @@ template <int F4PT, int DW, int LAG>
 __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
                      int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats, Partial* parts, float* mean_out,
-                     float* rstd_out)
+                     float* rstd_out, uint32_t spin_limit, uint32_t force_mask)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
@@ -886,6 +959,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         // waves find it in LDS when they reduce that sample (after barrier
         // t+1), and their memory counters see only x tiles and y stores.
         const uint32_t target = dev_load(&ctrl->gen) + 1u;
+        uint32_t limit = spin_limit;
         if (lane == 0) {
             s_K[0] = x[0];
             if (outer > 1) s_K[1] = x[inner];
@@ -914,11 +988,17 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             }
             const float K = s_K[g & 3];
             // gather every workgroup's sums (lane l: workgroups l, l + 64, ...),
-            // retrying until every tag is current, then a fixed-order sum
+            // retrying until every tag is current, then a fixed-order sum.
+            // Sums that have not arrived after `limit` polls (their workgroup
+            // is not resident: an ordinary launch does not promise that every
+            // workgroup runs at once) are computed here from x, with the same
+            // bits; x of sample g is still intact then, also in place, since a
+            // workgroup overwrites its rows of g only after publishing its sums.
             const Partial* pb = parts + g * P_cap;
             double S1 = 0.0, S2 = 0.0;
             for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
                 double a[4], b2[4];
+                bool miss[4];
                 uint32_t spins = 0;
                 for (;;) {
                     bool ok = true;
@@ -928,14 +1008,36 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                         const Partial* q = pb + (j < P ? j : p);
                         a[u] = dev_load(&q->n);
                         b2[u] = dev_load(&q->mean);
-                        ok = ok && has_tag(a[u], target) && has_tag(b2[u], target);
+                        const bool forced = ((uint32_t)j & force_mask) == force_mask;
+                        miss[u] = j < P && (forced || !(has_tag(a[u], target) && has_tag(b2[u], target)));
+                        ok = ok && (!miss[u] || forced);
                     }
                     if (__all(ok)) break;
                     __builtin_amdgcn_s_sleep(2);
-                    if (++spins > kSpinLimit) {
-                        if (lane == 0) dev_store(&ctrl->error, 1u);
+                    if (++spins > limit) {
+                        // from now on this workgroup waits only briefly
+                        limit = kSpinLimitAfterMiss;
                         break;
                     }
+                }
+                const f4* xg = reinterpret_cast<const f4*>(x + g * inner);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint64_t todo = __ballot(miss[u]);
+                    uint32_t n_done = 0;
+                    while (todo) {
+                        const int l = __builtin_ctzll(todo);
+                        todo &= todo - 1;
+                        const CtlSums r =
+                            ctl_recompute_sums<F4PT, DW>(xg, K, (uint32_t)(j0 + l + u * kWave), (uint32_t)P, nv);
+                        if (lane == l) {
+                            a[u] = tag_word(r.s1, target);
+                            b2[u] = tag_word(r.s2, target);
+                        }
+                        ++n_done;
+                    }
+                    if (n_done && lane == 0)
+                        __hip_atomic_fetch_add(&ctrl->recomputed, n_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -1025,16 +1127,14 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             const float K = s_K[t & 3];
             f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
-            for (int k = 0; k < F4PT; ++k) {
-                const f4 d = valid(k) ? T[u][k] - K : f4(0.0f);
-                a1 += d;
-                a2 += d * d;
-            }
-            const double t1 = wave_sum(((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w));
-            const double t2 = wave_sum(((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w));
+            for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? T[u][k] - K : f4(0.0f));
+            double t1, t2;
+            wave_moments(a1, a2, t1, t2);
             if (lane == 0) {
-                red[t & 1][2 * (tid / kWave)] = t1;
-                red[t & 1][2 * (tid / kWave) + 1] = t2;
+                // the wave's slot from a scalar register (no VGPR stays live for it)
+                const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+                red[t & 1][2 * wv] = t1;
+                red[t & 1][2 * wv + 1] = t2;
             }
         }
         __syncthreads();  // barrier t: sample t-LAG's statistics are in LDS
@@ -1269,19 +1369,33 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     if (P > P_cap) return false;
     const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * rw * sizeof(f4);
     if (lds + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
-    const void* fn = DW == 0 ? reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>)
-                             : reinterpret_cast<const void*>(
-                                   &ln_single_ctl_kernel<F4PT, DW == 0 ? 1 : DW, NORMFWD_LN_CTL_LAG>);
+    const void* fn;
+    if constexpr (DW == 0)
+        fn = reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>);
+    else
+        fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>);
     const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
     if (coresident(fn, lds, threads) < P) return false;
     int64_t pcap = P_cap;
-    void* args_hold[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
-                         (void*)&inner, (void*)&pcap,    (void*)&eps,  (void*)&ctrl,  (void*)&counters,
-                         (void*)&flag,  (void*)&stats,   (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
-    void* args_ctl[] = {(void*)&x,    (void*)&w,     (void*)&b,     (void*)&y,        (void*)&outer,   (void*)&inner,
-                        (void*)&pcap, (void*)&eps,   (void*)&ctrl,  (void*)&stats,    (void*)&parts,
-                        (void*)&mean_out, (void*)&rstd_out};
-    void** args = DW == 0 ? args_hold : args_ctl;
+    if constexpr (DW > 0) {
+        // An ordinary launch (a cooperative one costs ~17 us more per call on
+        // MI355X).  The grid fits the device, so normally every workgroup is
+        // resident at once; when one is not (another kernel holds its CU), the
+        // others compute its sums themselves after a bounded wait, so the
+        // launch completes with the same result either way.  Test knob: force
+        // that path for every k-th workgroup (not in place, where the forced
+        // workgroup may already have overwritten its rows of x).  Workgroup j
+        // is forced iff (j & mask) == mask; all ones forces none (P <= 1024).
+        const uint32_t k = x == y ? 0u : ln_force_recompute();
+        const uint32_t force = k ? k - 1u : 0xFFFFFFFFu;
+        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)P), dim3(threads),
+                            (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, parts, mean_out,
+                            rstd_out, kSpinLimit, force);
+        return true;
+    }
+    void* args[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
+                    (void*)&inner, (void*)&pcap,    (void*)&eps,  (void*)&ctrl,  (void*)&counters,
+                    (void*)&flag,  (void*)&stats,   (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
     // a cooperative launch cannot carry events: armed ones bracket it as markers
     const LaunchEvents ev = take_launch_events();
     if (ev.start) (void)hipEventRecord(ev.start, st);

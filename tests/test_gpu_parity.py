@@ -272,9 +272,10 @@ def test_ln_single_kernel_repeated_and_split_halves(variant):
         again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
         assert torch.equal(first, again)
     torch.cuda.synchronize()
-    ctrl = ws[:16].view(torch.int32).cpu().tolist()  # gen, done, error, pad
+    ctrl = ws[:16].view(torch.int32).cpu().tolist()  # gen, done, error, recomputed
     assert ctrl[1] == 0 and ctrl[2] == 0, ctrl
     assert ctrl[0] == 301, ctrl
+    assert ctrl[3] == 0, f"every workgroup was resident, none had its sums recomputed: {ctrl}"
     ws0 = nf.ln_forward_stats(d["x"])
     halves = nf.ln_forward_apply(d["x"], d["weight"], d["bias"], ws0)
     split = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=0)

@@ -1,0 +1,48 @@
+"""The control-wave LayerNorm kernel (ln_forward variant 1) runs as an ordinary launch: when a workgroup's
+published sums do not arrive (it is not resident), the others compute them from x with the same bits.  A
+child process forces that path for every k-th workgroup (NORMFWD_LN_FORCE_RECOMPUTE=k, read once by the
+library) and the results must equal this process's normal results bit for bit, and the oracle."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import normalization_ln_forward_amd as nf
+from normalization_ln_forward_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+import recompute_child  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("k", [4, 1])
+def test_forced_recompute_is_bitwise_equal(k, tmp_path):
+    path = str(tmp_path / f"forced_{k}.npz")
+    env = dict(os.environ, NORMFWD_LN_FORCE_RECOMPUTE=str(k))
+    print(f"forced recompute k={k}: child", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(HERE, "recompute_child.py"), path], capture_output=True,
+                       text=True, timeout=300, env=env)
+    print(r.stdout, flush=True)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    forced = np.load(path)
+    normal = recompute_child.run_cases()  # this process: no knob, nothing recomputed
+    # k = 4 forces workgroups 3, 7, ...: none in the 3-workgroup case
+    assert sum(int(forced[f"recomputed_{o}x{i}"]) > 0 for o, i, _, _ in recompute_child.CASES) >= (4 if k == 1 else 3)
+    for outer, inner, seed, name in recompute_child.CASES:
+        tag = f"{outer}x{inner}"
+        assert int(normal[f"recomputed_{tag}"]) == 0, f"{tag}: a healthy launch recomputed sums"
+        for key in ("y", "mean", "rstd"):
+            a, b = forced[f"{key}_{tag}"], normal[f"{key}_{tag}"]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{tag} {key}: forced != normal"
+        if k == 4:
+            d = synth.make(name, device="cuda", shape=(outer, inner), normalized_ndim=1, seed=seed)
+            ref = oracle.ln(*(d[t].cpu().numpy() for t in ("x", "weight", "bias")))
+            rep = oracle.allclose_report(forced[f"y_{tag}"], ref, 1e-4, 1e-4)
+            assert rep["ok"], f"{tag}: {rep}"
+        torch.cuda.empty_cache()
