@@ -121,11 +121,12 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 with a flag (LN page, turn 6: last-block-done), the others
  *                 waiting for that flag.  A cooperative launch, since its
  *                 waits need every workgroup resident.
- *             3 = automatic: variant 1 where it measured fastest (at least
- *                 8 samples, and a sample spread over one workgroup per CU,
- *                 e.g. [16, 4194304]), otherwise variant 0.  The choice
- *                 depends only on the shape, the pointers' alignment and the
- *                 device, so it is the same on every call.
+ *             3 = automatic: variant 1 where it measured fastest (each
+ *                 sample spread over at least half the CUs' worth of
+ *                 workgroups, e.g. inner >= 2097152 on MI355X),
+ *                 otherwise variant 0.  The choice depends only on the
+ *                 shape, the pointers' alignment and the device, so it is
+ *                 the same on every call.
  *             Shapes a single kernel cannot hold (inner % 4 != 0, unaligned
  *             pointers, more rows than co-resident workgroups can keep) run
  *             the split schedule instead.

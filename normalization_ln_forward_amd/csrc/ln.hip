@@ -840,13 +840,14 @@ __device__ __forceinline__ void wave_moments(const f4 a1, const f4 a2, double& t
 // same elements, the same order of additions and the same wave reduction,
 // and the wave totals are added in wave order, so the result has exactly
 // the bits j itself would publish.  Used when j's sums do not arrive.
-// Out of line: inlined, its registers pushed the data waves' loop into
-// spills.  The sums come back by value (in registers, not on the stack).
+// One load in flight at a time: few registers, so that this rarely taken
+// path does not raise the kernel's register count (the data waves' loop sits
+// at its limit), and no call.
 struct CtlSums {
     double s1, s2;
 };
 template <int F4PT, int DW>
-__device__ __noinline__ CtlSums ctl_recompute_sums(const f4* xs, float K, uint32_t j, uint32_t P, int64_t nv)
+__device__ __forceinline__ CtlSums ctl_recompute_sums(const f4* xs, float K, uint32_t j, uint32_t P, int64_t nv)
 {
     double s1 = 0.0, s2 = 0.0;
     constexpr int RW = DW * kWave;
@@ -854,17 +855,11 @@ __device__ __noinline__ CtlSums ctl_recompute_sums(const f4* xs, float K, uint32
     const uint32_t stride = P * (uint32_t)RW;
     for (int w = 0; w < DW; ++w) {
         const uint32_t off0 = j * (uint32_t)RW + (uint32_t)(w * kWave + lane);
-        f4 v[F4PT];
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) {
-            const uint32_t idx = off0 + (uint32_t)k * stride;
-            v[k] = (int64_t)idx < nv ? ld_nt(xs + idx) : f4(0.0f);
-        }
         f4 a1 = f4(0.0f), a2 = f4(0.0f);
-#pragma unroll
+#pragma unroll 1
         for (int k = 0; k < F4PT; ++k) {
             const uint32_t idx = off0 + (uint32_t)k * stride;
-            shifted_acc(a1, a2, (int64_t)idx < nv ? v[k] - K : f4(0.0f));
+            shifted_acc(a1, a2, (int64_t)idx < nv ? ld_nt(xs + idx) - K : f4(0.0f));
         }
         double t1, t2;
         wave_moments(a1, a2, t1, t2);
@@ -936,7 +931,7 @@ template <int F4PT, int DW, int LAG>
 __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
                      int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats, Partial* parts, float* mean_out,
-                     float* rstd_out, uint32_t spin_limit, uint32_t force_mask)
+                     float* rstd_out, uint32_t spin_limit, uint32_t silent_mask)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
@@ -960,6 +955,9 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         // t+1), and their memory counters see only x tiles and y stores.
         const uint32_t target = dev_load(&ctrl->gen) + 1u;
         uint32_t limit = spin_limit;
+        // test knob: a silent workgroup never publishes, so every reader
+        // (itself included) computes its sums from x
+        const bool silent = ((uint32_t)p & silent_mask) == silent_mask;
         if (lane == 0) {
             s_K[0] = x[0];
             if (outer > 1) s_K[1] = x[inner];
@@ -969,7 +967,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             __syncthreads();  // barrier t: the wave sums of sample t are in LDS
             const bool next_k = t + 2 < outer;
             const float k_next = next_k ? x[(t + 2) * inner] : 0.0f;
-            if (t < outer && lane == 0) {
+            if (t < outer && lane == 0 && !silent) {
                 // this workgroup's sums of d = x - K and d^2 over its elements of sample t
                 const double* rd = red[t & 1];
                 double s1 = rd[0], s2 = rd[1];
@@ -998,8 +996,8 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             double S1 = 0.0, S2 = 0.0;
             for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
                 double a[4], b2[4];
-                bool miss[4];
                 uint32_t spins = 0;
+                bool late = false;
                 for (;;) {
                     bool ok = true;
 #pragma unroll
@@ -1008,35 +1006,37 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                         const Partial* q = pb + (j < P ? j : p);
                         a[u] = dev_load(&q->n);
                         b2[u] = dev_load(&q->mean);
-                        const bool forced = ((uint32_t)j & force_mask) == force_mask;
-                        miss[u] = j < P && (forced || !(has_tag(a[u], target) && has_tag(b2[u], target)));
-                        ok = ok && (!miss[u] || forced);
+                        ok = ok && has_tag(a[u], target) && has_tag(b2[u], target);
                     }
                     if (__all(ok)) break;
                     __builtin_amdgcn_s_sleep(2);
                     if (++spins > limit) {
-                        // from now on this workgroup waits only briefly
-                        limit = kSpinLimitAfterMiss;
+                        late = true;
                         break;
                     }
                 }
-                const f4* xg = reinterpret_cast<const f4*>(x + g * inner);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    uint64_t todo = __ballot(miss[u]);
+                if (late) {
+                    // from now on this workgroup waits only briefly
+                    limit = std::min(limit, kSpinLimitAfterMiss);
+                    const f4* xg = reinterpret_cast<const f4*>(x + g * inner);
                     uint32_t n_done = 0;
-                    while (todo) {
-                        const int l = __builtin_ctzll(todo);
-                        todo &= todo - 1;
-                        const CtlSums r =
-                            ctl_recompute_sums<F4PT, DW>(xg, K, (uint32_t)(j0 + l + u * kWave), (uint32_t)P, nv);
-                        if (lane == l) {
-                            a[u] = tag_word(r.s1, target);
-                            b2[u] = tag_word(r.s2, target);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int64_t j = j0 + lane + (int64_t)u * kWave;
+                        uint64_t todo = __ballot(j < P && !(has_tag(a[u], target) && has_tag(b2[u], target)));
+                        while (todo) {
+                            const int l = __builtin_ctzll(todo);
+                            todo &= todo - 1;
+                            const CtlSums r =
+                                ctl_recompute_sums<F4PT, DW>(xg, K, (uint32_t)(j0 + l + u * kWave), (uint32_t)P, nv);
+                            if (lane == l) {
+                                a[u] = tag_word(r.s1, target);
+                                b2[u] = tag_word(r.s2, target);
+                            }
+                            ++n_done;
                         }
-                        ++n_done;
                     }
-                    if (n_done && lane == 0)
+                    if (lane == 0)
                         __hip_atomic_fetch_add(&ctrl->recomputed, n_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
 #pragma unroll
@@ -1131,10 +1131,8 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             double t1, t2;
             wave_moments(a1, a2, t1, t2);
             if (lane == 0) {
-                // the wave's slot from a scalar register (no VGPR stays live for it)
-                const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-                red[t & 1][2 * wv] = t1;
-                red[t & 1][2 * wv + 1] = t2;
+                red[t & 1][2 * (tid / kWave)] = t1;
+                red[t & 1][2 * (tid / kWave) + 1] = t2;
             }
         }
         __syncthreads();  // barrier t: sample t-LAG's statistics are in LDS
@@ -1386,11 +1384,13 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
         // that path for every k-th workgroup (not in place, where the forced
         // workgroup may already have overwritten its rows of x).  Workgroup j
         // is forced iff (j & mask) == mask; all ones forces none (P <= 1024).
+        // A forced workgroup never publishes its sums, so the wait for them
+        // is cut short (64 polls) in that mode.
         const uint32_t k = x == y ? 0u : ln_force_recompute();
         const uint32_t force = k ? k - 1u : 0xFFFFFFFFu;
         err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)P), dim3(threads),
                             (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, parts, mean_out,
-                            rstd_out, kSpinLimit, force);
+                            rstd_out, k ? 64u : kSpinLimit, force);
         return true;
     }
     void* args[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
@@ -1410,20 +1410,21 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
     return (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
 }
 
-// Measured on MI355X (split against the control-wave kernel, one call per
-// shape): [16, 4M] 135 vs 117 us, [8, 4M] 71 vs 71 us, [4, 4M] 41 vs 46 us,
-// [32, 1M] 68 vs 118 us, [64, 256K] 34 vs 164 us.  The single kernel pays a
-// cooperative launch (~17 us) and one workgroup barrier plus a cross-
-// workgroup exchange per sample, and saves one read of x; it wins only where
-// its tile of 8 float4 x 512 threads per sample puts a workgroup on every CU
-// and there are enough samples to amortize the launch.
+// Measured on MI355X (split against the control-wave kernel, 30 calls per
+// shape, one process): [16, 4M] 136 vs 99 us, [8, 4M] 72 vs 53, [4, 4M] 41
+// vs 26, [2, 4M] 29 vs 19, [1, 4M] 20 vs 14, [32, 2M] 134 vs 119, [8, 2M] 41
+// vs 34, [2, 2M] 14.4 vs 12.9, [32, 1M] 69 vs 101, [16, 1M] 39 vs 54, [4, 1M]
+// 12 vs 17, [64, 256K] 34 vs 170.  The single kernel saves one read of x and
+// pays one workgroup barrier plus a cross-workgroup exchange per sample;
+// with 8 float4 x 512 threads per workgroup it wins where a sample spreads
+// over at least half the CUs (inner >= 2M here), whatever the sample count.
 int ln_auto_variant(const float* x, const float* w, const float* b, const float* y, int64_t outer, int64_t inner)
 {
-    if (outer < 8 || !ln_single_supported(inner, x, w, b, y)) return 0;
+    if (!ln_single_supported(inner, x, w, b, y)) return 0;
     DeviceInfo d;
     if (!device_info(d)) return 0;
     const int64_t P = ceil_div(ceil_div(inner / 4, (int64_t)8 * kWave), (int64_t)8);
-    if (P < d.cus) return 0;
+    if (2 * P < d.cus) return 0;
     const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * 8 * 8 * kWave * sizeof(f4);
     const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG>);
     return coresident(fn, lds, 9 * kWave) >= P ? 1 : 0;

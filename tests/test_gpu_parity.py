@@ -245,10 +245,10 @@ def test_ln_full_size(name, variant):
 
 
 def test_ln_auto_variant_picks_the_measured_fastest():
-    """variant 3 runs the single-read kernel on the benchmark shape and the split schedule where that
-    measured faster (few samples, or samples too small to put a workgroup on every CU): its output is
-    bitwise that of the variant it picks."""
-    for shape, pick in (((16, 4194304), 1), ((4, 4194304), 0), ((64, 262144), 0)):
+    """variant 3 runs the single-read kernel where it measured faster (samples spread over at least half
+    the CUs) and the split schedule elsewhere: its output is bitwise that of the variant it picks."""
+    for shape, pick in (((16, 4194304), 1), ((4, 4194304), 1), ((8, 2097152), 1), ((1, 4194304), 1),
+                        ((16, 1048576), 0), ((64, 262144), 0)):
         _say(f"ln auto {shape}")
         d = synth.make("ln_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=shape[0])
         auto = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=3)
