@@ -350,10 +350,16 @@ def test_prepared_calls_match_direct_calls():
 
 
 def test_captured_graph_replays_match_eager():
-    """The split LayerNorm, GN, RMS and fc+GN calls captured in one HIP graph (via torch's graph API on the
-    capturing stream) replay correctly several times, with eager work and synchronizations in between."""
+    """The split LayerNorm, the single-read LayerNorm (an ordinary launch), GN, RMS and fc+GN calls
+    captured in one HIP graph (via torch's graph API on the capturing stream) replay correctly several
+    times, with eager work and synchronizations in between."""
     _say("graph capture")
     l = synth.make("ln_16x64x256x256", device="cuda", shape=(4, 70000), normalized_ndim=1, seed=31)
+    s1 = synth.make("ln_16x64x256x256", device="cuda", shape=(3, 1 << 20), normalized_ndim=1, seed=35)
+    single_eager = nf.ln_forward(s1["x"], s1["weight"], s1["bias"], variant=1)
+    single_out = torch.empty_like(single_eager)
+    _, ws1 = nf.alloc_workspace(nf.ln_forward_workspace_size(3, 1 << 20), "cuda")
+    nf.ln_forward_workspace_init(ws1)
     g = synth.make("gn_lrelu_x2_1024x8192", device="cuda", shape=(64, 8192), seed=32)
     r = synth.make("rms_ch_112x64x512x512", device="cuda", shape=(2, 64, 4096), seed=33)
     f = synth.make("fc_gn_1024x8192x8192", device="cuda", shape=(128, 256), hidden=512, seed=34)
@@ -374,15 +380,20 @@ def test_captured_graph_replays_match_eager():
             nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512, out=outs[1])
             nf.rmsnorm_ch_forward(r["x"], out=outs[2])
             nf.fc_gn_forward(f["x"], f["W"], f["b"], f["gamma"], f["beta"], 32, out=outs[3])
+            nf.ln_forward(s1["x"], s1["weight"], s1["bias"], variant=1, out=single_out, workspace=ws1)
     torch.cuda.synchronize()
+    outs.append(single_out)
     for rep in range(4):
         for o in outs:
             o.fill_(float("nan"))          # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for o, e, name in zip(outs, (ln_eager, gn_eager, rms_eager, fc_eager), ("ln", "gn", "rms", "fc")):
+        for o, e, name in zip(outs, (ln_eager, gn_eager, rms_eager, fc_eager, single_eager),
+                              ("ln", "gn", "rms", "fc", "ln single-read")):
             assert torch.equal(o, e), f"replay {rep}: {name} differs from eager"
+    ctrl = ws1[:16].view(torch.int32).cpu().tolist()  # gen, done, error, recomputed
+    assert ctrl[0] == 4 and ctrl[1] == 0 and ctrl[3] == 0, ctrl
 
 
 def test_modules_match_the_functions():
