@@ -955,9 +955,12 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         // t+1), and their memory counters see only x tiles and y stores.
         const uint32_t target = dev_load(&ctrl->gen) + 1u;
         uint32_t limit = spin_limit;
-        // test knob: a silent workgroup never publishes, so every reader
-        // (itself included) computes its sums from x
+        // test knob: a silent workgroup publishes its sums under a tag no
+        // reader of this launch accepts (the generation with its top bit
+        // flipped: never the next launch's either), so every reader (itself
+        // included) computes them from x
         const bool silent = ((uint32_t)p & silent_mask) == silent_mask;
+        const uint32_t pub_tag = silent ? target ^ 0x80u : target;
         if (lane == 0) {
             s_K[0] = x[0];
             if (outer > 1) s_K[1] = x[inner];
@@ -967,7 +970,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             __syncthreads();  // barrier t: the wave sums of sample t are in LDS
             const bool next_k = t + 2 < outer;
             const float k_next = next_k ? x[(t + 2) * inner] : 0.0f;
-            if (t < outer && lane == 0 && !silent) {
+            if (t < outer && lane == 0) {
                 // this workgroup's sums of d = x - K and d^2 over its elements of sample t
                 const double* rd = red[t & 1];
                 double s1 = rd[0], s2 = rd[1];
@@ -976,8 +979,8 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                     s2 += rd[2 * wv + 1];
                 }
                 Partial* q = parts + t * P_cap + p;
-                dev_store(&q->n, tag_word(s1, target));
-                dev_store(&q->mean, tag_word(s2, target));
+                dev_store(&q->n, tag_word(s1, pub_tag));
+                dev_store(&q->mean, tag_word(s2, pub_tag));
             }
             const int64_t g = t - (LAG - 1);  // the sample gathered now, normalized after barrier g + LAG
             if (g < 0 || g >= outer) {
@@ -1384,7 +1387,7 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
         // that path for every k-th workgroup (not in place, where the forced
         // workgroup may already have overwritten its rows of x).  Workgroup j
         // is forced iff (j & mask) == mask; all ones forces none (P <= 1024).
-        // A forced workgroup never publishes its sums, so the wait for them
+        // A forced workgroup's sums are never accepted, so the wait for them
         // is cut short (64 polls) in that mode.
         const uint32_t k = x == y ? 0u : ln_force_recompute();
         const uint32_t force = k ? k - 1u : 0xFFFFFFFFu;

@@ -29,6 +29,12 @@ def run_cases():
         mean = torch.empty(outer, device="cuda")
         rstd = torch.empty(outer, device="cuda")
         y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws, mean_out=mean, rstd_out=rstd)
+        if (outer, inner) == CASES[0][:2]:
+            # past the wrap of the 8-bit generation tag: a sum that is never accepted stays so
+            for _ in range(300):
+                again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws)
+                if not torch.equal(again, y):
+                    sys.exit("a repeated launch on one workspace changed the result")
         torch.cuda.synchronize()
         tag = f"{outer}x{inner}"
         out[f"y_{tag}"] = y.cpu().numpy()
