@@ -16,7 +16,8 @@ object.
 
 Also measured (the `kernels` object): GroupNorm+LeakyReLU+x2 [1024, 8192],
 RMSNorm over dim 1 [112, 64, 512, 512], the LN N(100, 0.01) stress input,
-both LN schedules, and fc+GN [1024 x 8192 x 8192] (TFLOP/s).
+both LN schedules, fc+GN [1024 x 8192 x 8192] (TFLOP/s), and, as context for
+the HBM fractions, torch's device copy of 256 MiB (what a plain copy reaches).
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by
 torch.cuda.synchronize(); average launch durations from a pair of HIP events
@@ -291,6 +292,17 @@ def per_kernel_table(torch, nf, synth, dev, stream, args, log):
             out[f"{name}/{['split', 'single', 'single_last_block'][variant]}"] = _entry(t, ln_step_bytes(variant))
         del d, y, x2, y2
         torch.cuda.empty_cache()
+
+    # Context for the HBM fractions: torch's own device copy of 256 MiB into 256 MiB (the size of the LN
+    # input), rotating over 4 pairs (2 GiB) like the LN step; a ceiling of sorts, not an optimal copy.
+    log("[bench] copy reference: 256 MiB")
+    n = (256 << 20) // 4
+    srcs = [torch.randn(n, device=dev) for _ in range(4)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    t = time_launches(torch, stream, lambda i: dsts[i % 4].copy_(srcs[i % 4]), steps, warm)
+    out["copy_reference_torch_256MiB"] = _entry(t, 2 * 4 * n)
+    del srcs, dsts
+    torch.cuda.empty_cache()
 
     # RMSNorm over dim 1: 7.5 GB in, 7.5 GB out (far beyond any cache)
     log("[bench] RMS [112, 64, 512, 512]")
