@@ -35,6 +35,13 @@
  *     anything is enqueued, so a non-OK return from validation means nothing
  *     was launched.  normfwd_last_error() then describes the failure
  *     (thread-local, valid until the next call on the same thread).
+ *   - Two environment variables, read once per process, exist for testing
+ *     and change no result: NORMFWD_MAX_GRID_ITEMS (>= 4096) lowers the
+ *     work-items per launch so that small problems also take the
+ *     several-launch path; NORMFWD_LN_FORCE_RECOMPUTE = k (a power of two)
+ *     makes every k-th workgroup of the single-read LayerNorm kernel
+ *     (ln_forward variant 1, not in place) have its moments computed by the
+ *     other workgroups, the path taken when a workgroup is not resident.
  */
 #ifndef NORMFWD_H
 #define NORMFWD_H
