@@ -122,7 +122,11 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 moments after a bounded number of polls and compute them
  *                 from x themselves, bit for bit the same, so the result
  *                 never depends on residency (a forced-recompute GPU test
- *                 checks that bitwise);
+ *                 checks that bitwise).  The grid takes one workgroup per
+ *                 CU, so two such launches running at once on different
+ *                 streams each finish correctly but slowly (their waits
+ *                 run out first, a fraction of a second); order them on
+ *                 one stream or with an event;
  *             2 = single kernel in which the last workgroup to deliver a
  *                 sample's partial merges it and announces the statistics
  *                 with a flag (LN page, turn 6: last-block-done), the others
