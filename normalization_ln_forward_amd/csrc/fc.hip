@@ -109,6 +109,30 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
+// Sum over the GM lanes (channels) of a group inside one 32-lane half:
+// GM <= 8 butterflies (group_sum), 16 one DPP row, 32 two DPP rows.  Fixed
+// order, every lane of the group gets the total.
+template <int GM>
+__device__ __forceinline__ float group_lanes_sum(float v)
+{
+    if constexpr (GM <= 8) {
+        return group_sum<GM>(v);
+    } else {
+        v = row16_sum(v);
+        if constexpr (GM == 32) v += __shfl_xor(v, 16);
+        return v;
+    }
+}
+
+// One output element of the epilogue: GroupNorm with the group's statistics
+// (mean m, rstd r), gamma g, beta be, then LeakyReLU and the doubling.
+__device__ __forceinline__ float gn_out(float d, float rstd, float g, float be, float slope)
+{
+    const float z = d * rstd * g + be;
+    const float a = z > 0.0f ? z : slope * z;
+    return a + a;
+}
+
 // Epilogue of a wave's 64 x 64 block of h (rows m0w.., columns n0w..).
 // D layout of a 32 x 32 tile: lane holds column (lane % 32); register r holds
 // row (r / 4) * 8 + (lane / 32) * 4 + r % 4.
@@ -132,34 +156,56 @@ __device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __re
                     const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
                     if (row < M) out[(int64_t)row * N + col] = acc[i][j][r] + bb;
                 }
-            } else {
+            } else if constexpr (GM <= 32) {
                 const float g = (gamma && col_ok) ? gamma[col] : 1.0f;
                 const float be = (beta && col_ok) ? beta[col] : 0.0f;
                 constexpr float inv_m = 1.0f / GM;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float hv = acc[i][j][r] + bb;
-                    float s1 = row16_sum(hv);
-                    if constexpr (GM == 32) s1 += __shfl_xor(s1, 16);
+                    const float s1 = group_lanes_sum<GM>(hv);
                     const float d = hv - s1 * inv_m;
-                    float s2 = row16_sum(d * d);
-                    if constexpr (GM == 32) s2 += __shfl_xor(s2, 16);
+                    const float s2 = group_lanes_sum<GM>(d * d);
                     const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
-                    const float z = d * rstd * g + be;
-                    const float a = z > 0.0f ? z : slope * z;
                     const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                    if (row < M && col_ok) out[(int64_t)row * N + col] = a + a;
+                    if (row < M && col_ok) out[(int64_t)row * N + col] = gn_out(d, rstd, g, be, slope);
                 }
             }
         }
+    if constexpr (GM == 64) {
+        // a 64-channel group is the wave's two 32-channel tiles: each row's
+        // sums are the two tiles' 32-lane sums, added in tile order
+        const int c0 = n0w + li, c1 = n0w + 32 + li;
+        const bool ok0 = c0 < N, ok1 = c1 < N;
+        const float bb0 = (bias && ok0) ? bias[c0] : 0.0f, bb1 = (bias && ok1) ? bias[c1] : 0.0f;
+        const float g0 = (gamma && ok0) ? gamma[c0] : 1.0f, g1 = (gamma && ok1) ? gamma[c1] : 1.0f;
+        const float be0 = (beta && ok0) ? beta[c0] : 0.0f, be1 = (beta && ok1) ? beta[c1] : 0.0f;
+        constexpr float inv_m = 1.0f / 64.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float h0 = acc[i][0][r] + bb0, h1 = acc[i][1][r] + bb1;
+                const float s1 = group_lanes_sum<32>(h0) + group_lanes_sum<32>(h1);
+                const float d0 = h0 - s1 * inv_m, d1 = h1 - s1 * inv_m;
+                const float s2 = group_lanes_sum<32>(d0 * d0) + group_lanes_sum<32>(d1 * d1);
+                const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
+                const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                if (row < M) {
+                    if (ok0) out[(int64_t)row * N + c0] = gn_out(d0, rstd, g0, be0, slope);
+                    if (ok1) out[(int64_t)row * N + c1] = gn_out(d1, rstd, g1, be1, slope);
+                }
+            }
+    }
 }
 
-// GM = 0: write h = x W^T + b to `out`.  GM = 16 or 32 (channels per group):
-// the GroupNorm -> LeakyReLU -> x + x epilogue runs on the accumulators and
-// `out` receives y; h never goes to memory.  In a 32 x 32 MFMA tile a lane
-// holds one column (channel) for 16 rows, so the 16 channels of a group
-// are the 16 lanes of one DPP row (GM = 32: two adjacent DPP rows), and
-// each row's group statistics are a 16-lane (32-lane) reduction per
+// GM = 0: write h = x W^T + b to `out`.  GM = 4, 8, 16, 32 or 64 (channels
+// per group): the GroupNorm -> LeakyReLU -> x + x epilogue runs on the
+// accumulators and `out` receives y; h never goes to memory.  In a 32 x 32
+// MFMA tile a lane holds one column (channel) for 16 rows, so the 16
+// channels of a group are the 16 lanes of one DPP row (GM = 32: two
+// adjacent DPP rows; GM = 4, 8: part of one; GM = 64: both of the wave's
+// tiles), and each row's group statistics are a lane reduction per
 // register, two-pass in registers.
 //
 // Software pipeline over K: while the waves multiply slice k out of one LDS
@@ -371,10 +417,19 @@ hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const fl
     auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const bool vec = K % 4 == 0 && al(x) && al(W);
     const int64_t M = C / G;
-    // Groups of 16 or 32 channels fit in the GEMM epilogue (tiles are 32
-    // channels wide and start at multiples of 32).
-    if (NORMFWD_FC_FUSE && M == 16) return launch_gemm<16>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
-    if (NORMFWD_FC_FUSE && M == 32) return launch_gemm<32>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+    // Groups of 4 to 64 channels (powers of two) fit in the GEMM epilogue: a
+    // wave's block is 64 channels wide in two 32-channel tiles and starts at
+    // a multiple of 64, so no group straddles waves.
+    if (NORMFWD_FC_FUSE) {
+        switch (M) {
+            case 4: return launch_gemm<4>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+            case 8: return launch_gemm<8>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+            case 16: return launch_gemm<16>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+            case 32: return launch_gemm<32>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+            case 64: return launch_gemm<64>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+            default: break;
+        }
+    }
     float* h = static_cast<float*>(ws);
     hipError_t e = launch_gemm<0>(vec, x, W, b, nullptr, nullptr, h, N, K, C, eps, slope, st);
     if (e != hipSuccess) return e;

@@ -297,15 +297,20 @@ def test_ln_in_place(variant):
 # ---------------------------------------------------------------- fc -> GroupNorm epilogue
 
 FC_CASES = [
-    # (N, K, C, G)                 16- and 32-channel groups use the fused GEMM epilogue
-    (100, 96, 384, 24),     # M = 16 fused; ragged row tile (100 < 128), 3 column tiles
-    (130, 70, 256, 16),     # M = 16 fused; K % 4 != 0 -> scalar tile loader, 2 row tiles
+    # (N, K, C, G)   groups of 4-64 channels use the fused GEMM epilogue, other sizes the GN kernel on h;
+    # K % 32 == 0 with 16-byte rows runs the direct-to-LDS GEMM (256-row tiles), else the staged one
+    (100, 96, 384, 24),     # M = 16 fused; ragged row tile (100 < 256), 3 column tiles
+    (130, 70, 256, 16),     # M = 16 fused; K % 4 != 0 -> staged GEMM, scalar tile loader
     (64, 512, 160, 10),     # M = 16 fused; ragged column tile
     (96, 128, 256, 8),      # M = 32 fused
-    (70, 64, 256, 32),      # M = 8: GEMM writes h, then the GroupNorm kernel
-    (40, 36, 512, 8),       # M = 64: GEMM writes h, then the GroupNorm kernel
-    # K % 32 == 0 runs the direct-to-LDS GEMM (256-row tiles); the others above with K % 32 == 0 do too
-    (300, 32, 200, 25),     # M = 8; two row tiles, the second ragged; ragged column tile
+    (70, 64, 256, 32),      # M = 8 fused
+    (300, 32, 200, 25),     # M = 8 fused; two row tiles, the second ragged; ragged column tile
+    (40, 36, 512, 8),       # M = 64 fused, staged GEMM
+    (90, 64, 320, 5),       # M = 64 fused, direct-to-LDS GEMM; 320 = 2.5 column tiles
+    (100, 40, 96, 24),      # M = 4 fused, staged GEMM
+    (66, 30, 12, 3),        # M = 4 fused; K % 4 != 0; one narrow column tile
+    (50, 64, 100, 5),       # M = 20: GEMM writes h, then the GroupNorm kernel
+    (40, 32, 96, 48),       # M = 2: GEMM writes h, then the GroupNorm kernel
     (513, 256, 128, 8),     # M = 16 fused; three row tiles, one row in the last
 ]
 
