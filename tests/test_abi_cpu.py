@@ -114,6 +114,40 @@ def test_rms_validation():
     assert st == 2
 
 
+def test_documented_size_limits_are_refused():
+    """Each limit the header states is enforced before anything is launched (NORMFWD_ERR_UNSUPPORTED)."""
+    lib = _lib.lib()
+    big_ws = 1 << 62
+
+    def ln(outer, inner):
+        return _err(lib.ln_forward(FAKE, None, None, FAKE, outer, inner, 1e-5, FAKE_WS, big_ws, None, None, 0,
+                                   None))[0]
+
+    assert ln((1 << 22) + 1, 1) == 2          # samples
+    assert ln(1, (1 << 31) + 4) == 2          # elements per sample
+    assert ln(1 << 12, 1 << 29) == 2          # elements per tensor (2^41 > 2^40)
+
+    def gn(N, C, G):
+        return _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, N, C, G, 1e-5, 0.01, None))[0]
+
+    assert gn(1, 1 << 31, 1) == 2             # channels
+    assert gn(1 << 12, 1 << 29, 1 << 20) == 2  # elements per tensor
+
+    def rms(B, C, S):
+        return _err(lib.rmsnorm_ch_forward(FAKE, FAKE, B, C, S, 1e-5, None))[0]
+
+    assert rms(1, 1 << 31, 4) == 2            # channels
+    assert rms(1, 3, (1 << 26) + 4) == 2      # positions per sample
+    assert rms(1 << 12, 1 << 10, 1 << 20) == 2  # elements per tensor
+
+    def fc(N, K, C, G):
+        return _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, N, K, C, G, 1e-5, 0.01, FAKE_WS, big_ws,
+                                      None))[0]
+
+    assert fc((1 << 23) + 1, 16, 64, 4) == 2  # rows
+    assert fc(64, 16, (1 << 24) + 16, 16) == 2  # output channels
+
+
 def test_fc_validation():
     lib = _lib.lib()
     need = lib.fc_gn_forward_workspace_size(1024, 8192, 8192)
