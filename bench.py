@@ -140,7 +140,7 @@ def main():
         # (kernel start to end); variant 2's cooperative launch cannot, so there the events bracket each
         # launch and its duration includes the cooperative launch's own cost.
         dom_kernel = "ln_single_ctl_kernel" if variant == 1 else "ln_single_hold_kernel"
-        dom_bytes, avg_ms = LN_NORMALIZE_BYTES, t["kernel_ms"]
+        dom_bytes, avg_ms, med_ms = LN_NORMALIZE_BYTES, t["kernel_ms"], t["kernel_ms_median"]
     else:
         # the step is the two halves of the split schedule
         stats = [nf.prepare(nf.ln_forward_stats, xs[r], workspace=ws) for r in range(R)]
@@ -162,13 +162,16 @@ def main():
         ms_per_step = t["wall_ms"]
         time_launches(torch, stream, step, args.steps, 0)
         dom_kernel, dom_bytes = "ln_normalize_rows_kernel", LN_NORMALIZE_BYTES
-        avg_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / len(evs)
+        durs = sorted(a.elapsed_time(b_) for a, b_ in evs)
+        avg_ms = sum(durs) / len(durs)
+        med_ms = durs[len(durs) // 2]
     value = ln_step_bytes(variant) / (ms_per_step / 1e3) / 1e9
     achieved = dom_bytes / (avg_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for(dom_kernel),
-                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": round(avg_ms, 5)}
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": round(avg_ms, 5),
+                "median_launch_ms": round(med_ms, 5)}
     log(f"[bench] LN: {ms_per_step:.4f} ms/step wall, {value:.1f} GB/s; {dom_kernel} {avg_ms:.4f} ms, "
         f"{achieved:.1f} GB/s")
     del xs, ys
@@ -225,7 +228,8 @@ def time_launches(torch, stream, fn, steps, warmup, nf=None):
     events on `stream`, bracketed by synchronize() for the wall clock.
     Returns the average per launch from the events and from the wall clock;
     with nf, a second loop of `steps` launches, each stamping its kernel's
-    own start and end into events, adds the average kernel duration."""
+    own start and end into events, adds the average and the median kernel
+    duration."""
     for i in range(warmup):
         fn(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -244,7 +248,9 @@ def time_launches(torch, stream, fn, steps, warmup, nf=None):
             arms[i]()
             fn(i)
         torch.cuda.synchronize()
-        res["kernel_ms"] = sum(a.elapsed_time(b) for a, b in evs) / steps
+        durs = sorted(a.elapsed_time(b) for a, b in evs)
+        res["kernel_ms"] = sum(durs) / steps
+        res["kernel_ms_median"] = durs[steps // 2] if steps % 2 else 0.5 * (durs[steps // 2 - 1] + durs[steps // 2])
     return res
 
 
