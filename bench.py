@@ -19,7 +19,10 @@ RMSNorm over dim 1 [112, 64, 512, 512], the LN N(100, 0.01) stress input,
 both LN schedules, fc+GN [1024 x 8192 x 8192] (TFLOP/s), and, as context for
 the HBM fractions, torch's device copy of 256 MiB (what a plain copy reaches).
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by
+Timing: an untimed settle phase (--settle-ms, default 200 ms of the same
+work: on MI355X kernel durations settle only after ~100 ms of sustained load;
+the LN step measured 104 us after 10 warm-up steps and 99 us after 100 ms), then
+W untimed warm-up steps, then K timed steps bracketed by
 torch.cuda.synchronize(); average launch durations from a pair of HIP events
 recorded around the K launches on the stream the library launches on
 (torch's current stream).  Kernel durations (the roofline's dominant kernel,
@@ -91,6 +94,9 @@ def parse():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed run of each measured workload before its warm-up steps, in ms of wall time "
+                         "(lets kernel durations reach their steady state; 0 = none)")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB a few times (reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -99,6 +105,8 @@ def parse():
 
 def main():
     args = parse()
+    global SETTLE_MS
+    SETTLE_MS = args.settle_ms
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -160,7 +168,7 @@ def main():
         # kernel inside each step with events stamped by its own launch
         t = time_launches(torch, stream, plain_step, args.steps, args.warmup)
         ms_per_step = t["wall_ms"]
-        time_launches(torch, stream, step, args.steps, 0)
+        time_launches(torch, stream, step, args.steps, 0, settle_ms=0)
         dom_kernel, dom_bytes = "ln_normalize_rows_kernel", LN_NORMALIZE_BYTES
         durs = sorted(a.elapsed_time(b_) for a, b_ in evs)
         avg_ms = sum(durs) / len(durs)
@@ -223,13 +231,32 @@ def kernel_events(torch, nf, stream, n):
     return evs, [nf.prepare(nf.time_next_kernel, a, b) for a, b in evs]
 
 
-def time_launches(torch, stream, fn, steps, warmup, nf=None):
-    """Run fn(i) for i < warmup untimed, then `steps` times between two HIP
+SETTLE_MS = 200.0  # set from --settle-ms in main()
+
+
+def settle(torch, fn, ms):
+    """Run fn untimed, in growing batches, for `ms` milliseconds of wall time.  MI355X needs ~100 ms of
+    sustained work before a kernel's duration settles (measured: the LN step at 104 us after 10 warm-up
+    steps, 99 us after 100 ms), so every timed loop starts from that steady state."""
+    if ms <= 0:
+        return
+    t0, n, i = time.perf_counter(), 1, 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(n):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        n = min(2 * n, 4096)
+
+
+def time_launches(torch, stream, fn, steps, warmup, nf=None, settle_ms=None):
+    """Settle (see settle()), run fn(i) for i < warmup untimed, then `steps` times between two HIP
     events on `stream`, bracketed by synchronize() for the wall clock.
     Returns the average per launch from the events and from the wall clock;
     with nf, a second loop of `steps` launches, each stamping its kernel's
     own start and end into events, adds the average and the median kernel
     duration."""
+    settle(torch, fn, SETTLE_MS if settle_ms is None else settle_ms)
     for i in range(warmup):
         fn(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
