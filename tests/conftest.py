@@ -12,10 +12,12 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(session, config, items):
-    """The plain-C program that drives the GPU from a child process runs first.  The last-workgroup-merges
-    LayerNorm kernel (variant 2) uses a cooperative launch; after the test process had made one, the
-    child's cooperative launch on the same GPU was refused (hipErrorIllegalState) on MI355X, so the child
-    runs before any such launch here.  (The recompute child makes no cooperative launch.)"""
-    child = [it for it in items if "test_c_abi.py" in it.nodeid]
-    rest = [it for it in items if "test_c_abi.py" not in it.nodeid]
+    """Tests that drive the GPU from a child process (the plain-C program, a short bench.py run) run
+    first.  The last-workgroup-merges LayerNorm kernel (variant 2) uses a cooperative launch; after the
+    test process had made one, a child's cooperative launch on the same GPU was refused
+    (hipErrorIllegalState) on MI355X, so these children run before any such launch here.  (The batching
+    and recompute children make no cooperative launch.)"""
+    first = ("test_c_abi.py", "test_bench_contract.py")
+    child = [it for it in items if any(f in it.nodeid for f in first)]
+    rest = [it for it in items if not any(f in it.nodeid for f in first)]
     items[:] = child + rest
