@@ -24,10 +24,11 @@
 #include <algorithm>
 
 // Channels per wave and 64-lane position segments per lane for the
-// register-held kernel (C = 64: 8 waves of 8 channels, 2 KiB per channel
-// row segment; the fastest of the shapes measured on MI355X).
+// register-held kernel (C = 64: 16 waves of 4 channels, 2 KiB per channel
+// row segment; the fastest of the shapes measured on MI355X in steady
+// state, 1.7% ahead of 8 waves of 8 channels).
 #ifndef NORMFWD_RMS_CPW
-#define NORMFWD_RMS_CPW 8
+#define NORMFWD_RMS_CPW 4
 #endif
 #ifndef NORMFWD_RMS_PPL
 #define NORMFWD_RMS_PPL 2
