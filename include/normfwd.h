@@ -113,7 +113,10 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *             1 = single kernel: one launch of at most one workgroup per
  *                 CU in which every workgroup keeps its share of each
  *                 sample in registers between the moments pass and the
- *                 normalize pass (x is read from HBM once).  A control wave
+ *                 normalize pass (x is read from HBM once).  When a sample
+ *                 spreads over fewer workgroups than fit on the GPU, the
+ *                 grid holds several groups of workgroups, each taking every
+ *                 groups-th sample.  A control wave
  *                 per workgroup exchanges the workgroups' moments of each
  *                 sample through generation-tagged words (no atomics) while
  *                 the data waves stream the next samples.  It is an
@@ -132,12 +135,11 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 with a flag (LN page, turn 6: last-block-done), the others
  *                 waiting for that flag.  A cooperative launch, since its
  *                 waits need every workgroup resident.
- *             3 = automatic: variant 1 where it measured fastest (each
- *                 sample spread over at least half the CUs' worth of
- *                 workgroups, e.g. inner >= 2097152 on MI355X),
- *                 otherwise variant 0.  The choice depends only on the
- *                 shape, the pointers' alignment and the device, so it is
- *                 the same on every call.
+ *             3 = automatic: variant 1 wherever it can run (it measured
+ *                 faster than the split, or within 1 us of it on calls of
+ *                 ~10 us, at every shape tried), otherwise variant 0.  The
+ *                 choice depends only on the shape, the pointers' alignment
+ *                 and the device, so it is the same on every call.
  *             Shapes a single kernel cannot hold (inner % 4 != 0, unaligned
  *             pointers, more rows than co-resident workgroups can keep) run
  *             the split schedule instead.

@@ -929,9 +929,9 @@ __device__ __forceinline__ bool ctl_steps(int64_t t0, int64_t steps, F& f)
 
 template <int F4PT, int DW, int LAG>
 __global__ void __launch_bounds__((DW + 1) * kWave)
-ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
-                     int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats, Partial* parts, float* mean_out,
-                     float* rstd_out, uint32_t spin_limit, uint32_t silent_mask)
+ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, float* y_all, int64_t outer_all,
+                     int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, Partial* parts_all,
+                     float* mean_all, float* rstd_all, int64_t groups, uint32_t spin_limit, uint32_t silent_mask)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
@@ -941,8 +941,23 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
     __shared__ float s_K[4];           // [sample % 4]: the sample's shift K (its first element)
     f4* w_s = reinterpret_cast<f4*>(smem_raw);
     f4* b_s = w_s + (w ? F4PT * RW : 0);
-    const int64_t P = gridDim.x;
-    const int64_t p = blockIdx.x;
+    // `groups` groups of P workgroups; group gr takes samples gr, gr + groups,
+    // ... as its own sequence (local sample i is sample gr + i * groups), so
+    // a grid of groups x P workgroups fills the GPU when one sample spreads
+    // over fewer.  Below, x, y, parts, stats, mean_out, rstd_out and outer
+    // are the group's view: local sample i at x + i * sstride, and so on.
+    const int64_t P = gridDim.x / groups;
+    const int64_t gr = blockIdx.x / P;
+    const int64_t p = blockIdx.x - gr * P;
+    const int64_t sstride = groups * inner;   // elements between the group's samples
+    const int64_t pstride = groups * P_cap;   // partial slots between the group's samples
+    const float* x = x_all + gr * inner;
+    float* y = y_all + gr * inner;
+    Partial* parts = parts_all + gr * P_cap;
+    f4* stats = stats_all + gr;
+    float* mean_out = mean_all ? mean_all + gr : nullptr;
+    float* rstd_out = rstd_all ? rstd_all + gr : nullptr;
+    const int64_t outer = (outer_all - gr + groups - 1) / groups;  // >= 1: groups <= outer_all
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int64_t nv = inner / 4;
@@ -963,13 +978,13 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         const uint32_t pub_tag = silent ? target ^ 0x80u : target;
         if (lane == 0) {
             s_K[0] = x[0];
-            if (outer > 1) s_K[1] = x[inner];
+            if (outer > 1) s_K[1] = x[sstride];
         }
         __syncthreads();  // prologue: w/b and the first shifts in LDS
         for (int64_t t = 0; t < steps; ++t) {
             __syncthreads();  // barrier t: the wave sums of sample t are in LDS
             const bool next_k = t + 2 < outer;
-            const float k_next = next_k ? x[(t + 2) * inner] : 0.0f;
+            const float k_next = next_k ? x[(t + 2) * sstride] : 0.0f;
             if (t < outer && lane == 0) {
                 // this workgroup's sums of d = x - K and d^2 over its elements of sample t
                 const double* rd = red[t & 1];
@@ -978,7 +993,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                     s1 += rd[2 * wv];
                     s2 += rd[2 * wv + 1];
                 }
-                Partial* q = parts + t * P_cap + p;
+                Partial* q = parts + t * pstride + p;
                 dev_store(&q->n, tag_word(s1, pub_tag));
                 dev_store(&q->mean, tag_word(s2, pub_tag));
             }
@@ -995,7 +1010,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
             // workgroup runs at once) are computed here from x, with the same
             // bits; x of sample g is still intact then, also in place, since a
             // workgroup overwrites its rows of g only after publishing its sums.
-            const Partial* pb = parts + g * P_cap;
+            const Partial* pb = parts + g * pstride;
             double S1 = 0.0, S2 = 0.0;
             for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
                 double a[4], b2[4];
@@ -1021,7 +1036,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                 if (late) {
                     // from now on this workgroup waits only briefly
                     limit = std::min(limit, kSpinLimitAfterMiss);
-                    const f4* xg = reinterpret_cast<const f4*>(x + g * inner);
+                    const f4* xg = reinterpret_cast<const f4*>(x + g * sstride);
                     uint32_t n_done = 0;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -1059,9 +1074,9 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
                 const f4 st = finish_stats(N, (double)K + md, fmax(S2 - S1 * md, 0.0), eps);
                 s_stats[g & 1] = st;
                 if (p == 0) {
-                    stats[g] = st;
-                    if (mean_out) mean_out[g] = st.x;
-                    if (rstd_out) rstd_out[g] = st.z;
+                    stats[g * groups] = st;
+                    if (mean_out) mean_out[g * groups] = st.x;
+                    if (rstd_out) rstd_out[g * groups] = st.z;
                 }
                 if (next_k) s_K[(t + 2) & 3] = k_next;
             }
@@ -1070,7 +1085,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         if (lane == 0) {
             vmem_drain();
             if (__hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)(P - 1)) {
+                gridDim.x - 1u) {
                 dev_store(&ctrl->done, 0u);
                 vmem_drain();
                 dev_store(&ctrl->gen, target);
@@ -1098,7 +1113,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         // Streaming loads: x is read once here (measured ~1% faster).
         const int64_t sb = s < outer ? s : outer - 1;
         const uint32_t m = s < outer ? 0xFFFFFFFFu : 0u;
-        const f4* xs = reinterpret_cast<const f4*>(x + sb * inner);
+        const f4* xs = reinterpret_cast<const f4*>(x + sb * sstride);
 #pragma unroll
         for (int k = 0; k < F4PT; ++k) T[r][k] = ld_nt(xs + (addr(k) & m));
     };
@@ -1142,7 +1157,7 @@ ln_single_ctl_kernel(const float* x, const float* w, const float* bias, float* y
         if constexpr (norm) {
             const int64_t s = t - LAG;
             const f4 st = s_stats[s & 1];
-            f4* y4 = reinterpret_cast<f4*>(y + s * inner);
+            f4* y4 = reinterpret_cast<f4*>(y + s * sstride);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) {
                 if (valid(k)) {
@@ -1376,7 +1391,8 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     else
         fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>);
     const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
-    if (coresident(fn, lds, threads) < P) return false;
+    const int cap = coresident(fn, lds, threads);
+    if (cap < P) return false;
     int64_t pcap = P_cap;
     if constexpr (DW > 0) {
         // An ordinary launch (a cooperative one costs ~17 us more per call on
@@ -1391,9 +1407,12 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
         // is cut short (64 polls) in that mode.
         const uint32_t k = x == y ? 0u : ln_force_recompute();
         const uint32_t force = k ? k - 1u : 0xFFFFFFFFu;
-        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)P), dim3(threads),
-                            (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, parts, mean_out,
-                            rstd_out, k ? 64u : kSpinLimit, force);
+        // as many groups of P workgroups (each taking every groups-th
+        // sample) as stay co-resident, at most one per sample
+        const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
+        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)(groups * P)),
+                            dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, parts,
+                            mean_out, rstd_out, groups, k ? 64u : kSpinLimit, force);
         return true;
     }
     void* args[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
@@ -1413,21 +1432,21 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
     return (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
 }
 
-// Measured on MI355X (split against the control-wave kernel, 30 calls per
-// shape, one process): [16, 4M] 136 vs 99 us, [8, 4M] 72 vs 53, [4, 4M] 41
-// vs 26, [2, 4M] 29 vs 19, [1, 4M] 20 vs 14, [32, 2M] 134 vs 119, [8, 2M] 41
-// vs 34, [2, 2M] 14.4 vs 12.9, [32, 1M] 69 vs 101, [16, 1M] 39 vs 54, [4, 1M]
-// 12 vs 17, [64, 256K] 34 vs 170.  The single kernel saves one read of x and
-// pays one workgroup barrier plus a cross-workgroup exchange per sample;
-// with 8 float4 x 512 threads per workgroup it wins where a sample spreads
-// over at least half the CUs (inner >= 2M here), whatever the sample count.
+// Measured on MI355X (split against the control-wave kernel with sample
+// groups, one call, 200 ms settle per shape): [16, 4M] 134.8 vs 99.1 us,
+// [4, 4M] 41.1 vs 26.6, [32, 2M] 137.3 vs 93.6, [16, 2M] 70.4 vs 50.1,
+// [32, 1M] 67.8 vs 49.3, [16, 1M] 39.1 vs 24.0, [8, 1M] 20.9 vs 15.7, [4, 1M]
+// 11.7 vs 12.1, [2, 1M] 10.5 vs 10.4, [64, 256K] 33.5 vs 23.7, [16, 256K]
+// 11.3 vs 11.9, [4, 256K] 9.5 vs 8.8, [128, 64K] 22.5 vs 14.9, [32, 64K]
+// 11.7 vs 10.0, [256, 16K] 14.8 vs 12.1.  With as many groups of workgroups
+// as stay co-resident, the single-read kernel fills the GPU whatever the
+// sample size and saves one read of x; the split is ahead only by < 1 us
+// on calls of ~10 us.  So it is taken wherever it can run.
 int ln_auto_variant(const float* x, const float* w, const float* b, const float* y, int64_t outer, int64_t inner)
 {
+    (void)outer;
     if (!ln_single_supported(inner, x, w, b, y)) return 0;
-    DeviceInfo d;
-    if (!device_info(d)) return 0;
     const int64_t P = ceil_div(ceil_div(inner / 4, (int64_t)8 * kWave), (int64_t)8);
-    if (2 * P < d.cus) return 0;
     const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * 8 * 8 * kWave * sizeof(f4);
     const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG>);
     return coresident(fn, lds, 9 * kWave) >= P ? 1 : 0;

@@ -245,10 +245,11 @@ def test_ln_full_size(name, variant):
 
 
 def test_ln_auto_variant_picks_the_measured_fastest():
-    """variant 3 runs the single-read kernel where it measured faster (samples spread over at least half
-    the CUs) and the split schedule elsewhere: its output is bitwise that of the variant it picks."""
+    """variant 3 runs the single-read kernel wherever it can run (float4 rows, 16-byte aligned tensors,
+    a co-resident grid) and the split schedule elsewhere: its output is bitwise that of the variant it
+    picks (with groups of workgroups for samples that spread over fewer than all CUs)."""
     for shape, pick in (((16, 4194304), 1), ((4, 4194304), 1), ((8, 2097152), 1), ((1, 4194304), 1),
-                        ((16, 1048576), 0), ((64, 262144), 0)):
+                        ((16, 1048576), 1), ((64, 262144), 1), ((100, 20000), 1), ((4, 1000001), 0)):
         _say(f"ln auto {shape}")
         d = synth.make("ln_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=shape[0])
         auto = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=3)
