@@ -220,7 +220,7 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
     ``variant`` 0 = split (moments kernel + normalize kernel), 1 = single
     kernel (control wave, tagged exchange; x read once), 2 = single cooperative
     kernel in which the last workgroup of each sample merges it, 3 (default) =
-    the library's choice by shape (1 where it measured fastest, else 0).  A caller-provided ``workspace`` must have been passed
+    the library's choice (1 wherever it can run: float4 rows, aligned tensors; else 0).  A caller-provided ``workspace`` must have been passed
     through ``ln_forward_workspace_init`` once.  Returns ``out`` (allocated if
     None).
     """
