@@ -24,14 +24,14 @@
 #include <algorithm>
 
 // Channels per wave and 64-lane position segments per lane for the
-// register-held kernel (C = 64: 16 waves of 4 channels, 2 KiB per channel
+// register-held kernel (C = 64: 16 waves of 4 channels, 1 KiB per channel
 // row segment; the fastest of the shapes measured on MI355X in steady
-// state, 1.7% ahead of 8 waves of 8 channels).
+// state: 3% ahead of 8 waves of 8 channels with 2 KiB segments).
 #ifndef NORMFWD_RMS_CPW
 #define NORMFWD_RMS_CPW 4
 #endif
 #ifndef NORMFWD_RMS_PPL
-#define NORMFWD_RMS_PPL 2
+#define NORMFWD_RMS_PPL 1
 #endif
 #ifndef NORMFWD_RMS_XCD
 #define NORMFWD_RMS_XCD 1
