@@ -28,9 +28,11 @@
 //          sample merges it) -> ln_normalize_rows_kernel (or
 //          ln_normalize_kernel for short samples); x is read twice.
 //   single kernels (variants 1 and 2): one launch of at most one workgroup
-//          per CU; workgroup p keeps its rows of every sample in VGPRs from
-//          the moments pass to the normalize pass, so x is read once, and
-//          the workgroups exchange each sample's moments in the middle:
+//          per CU; workgroup p keeps its rows of every sample (variant 1: of
+//          every sample of its group, when the grid holds several groups of
+//          workgroups that take every G-th sample) in VGPRs from the moments
+//          pass to the normalize pass, so x is read once, and the
+//          workgroups exchange each sample's moments in the middle:
 //          ln_single_ctl_kernel (variant 1, an ordinary launch): a control
 //          wave per workgroup publishes generation-tagged sums and gathers
 //          everyone's, while the data waves stream the next samples; sums
