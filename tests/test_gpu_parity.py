@@ -258,6 +258,25 @@ def test_ln_auto_variant_picks_the_measured_fastest():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("shape", [(64, 262144), (32, 1048576), (256, 16384)])
+def test_ln_sample_groups_against_the_oracle(shape):
+    """Samples that span fewer than all CUs: the default variant runs the single-read kernel with several
+    groups of workgroups (16, 4 and 256 groups here); y, the means and the rstds match the oracle."""
+    _say(f"ln sample groups {shape}")
+    outer, inner = shape
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=outer + 11)
+    mean = torch.empty(outer, device="cuda")
+    rstd = torch.empty(outer, device="cuda")
+    y = nf.ln_forward(d["x"], d["weight"], d["bias"], mean_out=mean, rstd_out=rstd)
+    assert torch.equal(y, nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1))
+    ref, om, ov = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]), eps=1e-5, return_stats=True)
+    _assert_close(_np(y), ref, what=f"ln {shape}")
+    np.testing.assert_allclose(_np(mean), om, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(_np(rstd), 1.0 / np.sqrt(ov + np.float32(1e-5)), rtol=1e-5)
+    del d, y
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("variant", [1, 2])
 def test_ln_single_kernel_repeated_and_split_halves(variant):
     """Many back-to-back single-kernel launches on one workspace stay bitwise equal and
