@@ -178,6 +178,31 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
                           void* workspace, size_t workspace_bytes,
                           float* mean_out, float* rstd_out, int variant, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ln_forward
+ * without a workspace argument.  The workspace is a static array inside the
+ * library, one per GPU, of 8 MiB (NORMFWD_LN_NOALLOC_SCRATCH_BYTES), which
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates and frees nothing and otherwise behaves exactly as ln_forward
+ * (same kernels, same results, bit for bit) with the same arguments.
+ *   - Shapes whose workspace (ln_forward_workspace_size(outer, inner)) is
+ *     larger than the scratch return NORMFWD_ERR_UNSUPPORTED before anything
+ *     is enqueued; samples of up to 8192 elements need no workspace at all.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents.  When a call's (outer, inner) differs from the last
+ *     call's on that GPU, the call first clears the part it uses, with a
+ *     kernel enqueued on `stream` ahead of its own work.
+ *   - Calls that may run concurrently on one GPU (different streams without
+ *     ordering between them, or different host threads) race on the scratch
+ *     and give wrong results: order them.
+ *   - The first call on each GPU looks up the scratch's device address
+ *     (hipGetSymbolAddress) with that GPU current; a failure there returns
+ *     NORMFWD_ERR_HIP. */
+#define NORMFWD_LN_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+normfwd_status ln_forward_noalloc(const float* x, const float* weight, const float* bias, float* y,
+                                  int64_t outer, int64_t inner, float eps,
+                                  float* mean_out, float* rstd_out, int variant, void* stream);
+
 /* The split variant's two halves, for callers that want the statistics
  * alone or want to time the phases: ln_forward_stats runs the moments
  * kernel and the merge and leaves per-sample (mean hi, mean lo, rstd) in

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     lib,
     ln_forward,
     ln_forward_apply,
+    ln_forward_noalloc,
     ln_forward_stats,
     ln_forward_workspace_check,
     ln_forward_workspace_init,

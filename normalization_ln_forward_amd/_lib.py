@@ -37,6 +37,7 @@ SIGNATURES = {
     "ln_forward_workspace_init": (_ST, [_P, _SZ, _P]),
     "ln_forward_workspace_check": (_ST, [_P, _SZ, _P]),
     "ln_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P, _P, ctypes.c_int, _P]),
+    "ln_forward_noalloc": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _P, ctypes.c_int, _P]),
     "ln_forward_stats": (_ST, [_P, _I64, _I64, _F, _P, _SZ, _P, _P, _P]),
     "ln_forward_apply": (_ST, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "gn_lrelu_x2_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _F, _F, _P]),
@@ -239,6 +240,27 @@ def ln_forward(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, varian
     _invoke("ln_forward", _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, float(eps), _ptr(ws),
                             ws.numel() * ws.element_size(), _ptr(mean_out), _ptr(rstd_out), int(variant),
                             _stream(dev))
+    return y
+
+
+def ln_forward_noalloc(x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, variant=3, out=None,
+                       mean_out=None, rstd_out=None):
+    """ln_forward on the library's own static scratch instead of a workspace (no device allocation in the
+    library; ``out`` is still allocated here when None).  Calls that may overlap on one GPU race on that
+    scratch; shapes whose workspace exceeds it raise NORMFWD_ERR_UNSUPPORTED."""
+    _need(x, "x")
+    dev = x.device
+    outer, inner = _ln_shape(x, normalized_ndim)
+    _opt(weight, "weight", inner, dev)
+    _opt(bias, "bias", inner, dev)
+    _opt(mean_out, "mean_out", outer, dev)
+    _opt(rstd_out, "rstd_out", outer, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", dev)
+    if y.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    _invoke("ln_forward_noalloc", _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), outer, inner, float(eps),
+            _ptr(mean_out), _ptr(rstd_out), int(variant), _stream(dev))
     return y
 
 

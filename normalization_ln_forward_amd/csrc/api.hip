@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <limits>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -104,6 +105,47 @@ LaunchEvents take_launch_events()
 }
 
 }  // namespace normfwd
+
+namespace {
+
+// One ln_forward call on a workspace of the layout `lay`: one workgroup per
+// sample for short samples, else the schedule `variant` selects.
+normfwd_status ln_dispatch(const float* x, const float* weight, const float* bias, float* y, int64_t outer,
+                           int64_t inner, float eps, void* workspace, const normfwd::LnLayout& lay, float* mean_out,
+                           float* rstd_out, int variant, hipStream_t st)
+{
+    hipError_t re = hipSuccess;
+    if (normfwd::launch_ln_rows(x, weight, bias, y, outer, inner, eps, mean_out, rstd_out, st, re))
+        return hip_status(re, "ln_forward (one workgroup per sample) launch");
+    if (variant == 3) variant = normfwd::ln_auto_variant(x, weight, bias, y, outer, inner);
+    if (variant != 0)
+        return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
+                                                    rstd_out, variant, st),
+                          "ln_forward (single kernel) launch");
+    hipError_t e = normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out, st);
+    if (e != hipSuccess) return hip_status(e, "ln_forward stats launch");
+    return hip_status(normfwd::launch_ln_apply(x, weight, bias, y, outer, inner, workspace, lay, st),
+                      "ln_forward normalize launch");
+}
+
+// ln_forward_noalloc's workspace: a file-scope device array, one copy per
+// GPU, kept until the process ends.  Host code never passes `scratch` itself
+// to a kernel (on the host that name is only a stand-in for the symbol);
+// it uses the device address hipGetSymbolAddress returns for the current
+// device, looked up on the first call on that device.
+constexpr size_t kLnScratchBytes = NORMFWD_LN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kLnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchState {
+    void* ptr = nullptr;  // device address of `scratch` on this device
+    int64_t outer = -1;   // shape the scratch was last laid out for
+    int64_t inner = -1;
+};
+std::mutex g_scratch_mu;
+ScratchState g_scratch[kMaxDevices];
+
+}  // namespace
 
 extern "C" {
 
@@ -206,19 +248,51 @@ normfwd_status ln_forward(const float* x, const float* weight, const float* bias
     s = check_ws(workspace, workspace_bytes, lay.total, "ln_forward");
     if (s != NORMFWD_OK) return s;
     (void)hipGetLastError();
+    return ln_dispatch(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out, rstd_out, variant,
+                       (hipStream_t)stream);
+}
+
+normfwd_status ln_forward_noalloc(const float* x, const float* weight, const float* bias, float* y, int64_t outer,
+                                  int64_t inner, float eps, float* mean_out, float* rstd_out, int variant,
+                                  void* stream)
+{
+    if (outer == 0 && inner >= 0 && variant >= 0 && variant <= 3) return ok();  // empty batch: nothing to do
+    normfwd_status s = check_ln(x, y, outer, inner, eps);
+    if (s != NORMFWD_OK) return s;
+    if (variant < 0 || variant > 3)
+        return fail(NORMFWD_ERR_INVALID, "ln_forward_noalloc: variant must be 0, 1, 2 or 3");
+    const normfwd::LnLayout lay = normfwd::ln_layout(outer, inner);
+    if (lay.total > kLnScratchBytes)
+        return fail(NORMFWD_ERR_UNSUPPORTED,
+                    "ln_forward_noalloc: shape [%lld, %lld] needs %zu bytes of workspace, more than the %zu bytes "
+                    "of the library's static scratch; use ln_forward with a caller workspace",
+                    (long long)outer, (long long)inner, lay.total, kLnScratchBytes);
+    (void)hipGetLastError();
     hipStream_t st = (hipStream_t)stream;
-    hipError_t re = hipSuccess;
-    if (normfwd::launch_ln_rows(x, weight, bias, y, outer, inner, eps, mean_out, rstd_out, st, re))
-        return hip_status(re, "ln_forward (one workgroup per sample) launch");
-    if (variant == 3) variant = normfwd::ln_auto_variant(x, weight, bias, y, outer, inner);
-    if (variant != 0)
-        return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
-                                                    rstd_out, variant, st),
-                          "ln_forward (single kernel) launch");
-    hipError_t e = normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out, st);
-    if (e != hipSuccess) return hip_status(e, "ln_forward stats launch");
-    return hip_status(normfwd::launch_ln_apply(x, weight, bias, y, outer, inner, workspace, lay, st),
-                      "ln_forward normalize launch");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "ln_forward_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(NORMFWD_ERR_UNSUPPORTED, "ln_forward_noalloc: device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchState& sc = g_scratch[dev];
+    if (!sc.ptr) {
+        // once per device, with that device current: each GPU holds its own
+        // copy of `scratch`, at its own address
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                     "ln_forward_noalloc: hipGetSymbolAddress(scratch)");
+        sc.ptr = p;
+    }
+    if (sc.outer != outer || sc.inner != inner) {
+        // The workspace regions sit at offsets that depend on the shape: a new
+        // shape starts from a zeroed scratch (a kernel, not a memset)
+        e = normfwd::launch_zero_words(sc.ptr, lay.total, st);
+        if (e != hipSuccess) return hip_status(e, "ln_forward_noalloc: zeroing the scratch");
+        sc.outer = outer;
+        sc.inner = inner;
+    }
+    return ln_dispatch(x, weight, bias, y, outer, inner, eps, sc.ptr, lay, mean_out, rstd_out, variant, st);
 }
 
 normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const float* beta, float* y, int64_t N,

@@ -179,3 +179,19 @@ def test_empty_work_is_a_no_op_that_touches_nothing():
     # still invalid: a bad group count or a negative size
     assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 100, 7, 1e-5, 0.01, None) == 1
     assert lib.rmsnorm_ch_forward(None, None, -1, 64, 1024, 1e-5, None) == 1
+
+
+def test_ln_noalloc_validation():
+    """ln_forward_noalloc validates like ln_forward and refuses shapes whose workspace exceeds its static
+    scratch, all before touching the device."""
+    lib = _lib.lib()
+    st, msg = _err(lib.ln_forward_noalloc(None, None, None, FAKE, 2, 8, 1e-5, None, None, 3, None))
+    assert st == 1 and "NULL" in msg
+    st, _ = _err(lib.ln_forward_noalloc(FAKE, None, None, FAKE, 2, 8, 1e-5, None, None, 4, None))
+    assert st == 1
+    st, _ = _err(lib.ln_forward_noalloc(FAKE, None, None, FAKE, 2, 8, -1.0, None, None, 3, None))
+    assert st == 1
+    assert lib.ln_forward_workspace_size(1024, 1 << 20) > (8 << 20)
+    st, msg = _err(lib.ln_forward_noalloc(FAKE, None, None, FAKE, 1024, 1 << 20, 1e-5, None, None, 3, None))
+    assert st == 2 and "scratch" in msg
+    assert lib.ln_forward_noalloc(FAKE, None, None, FAKE, 0, 8, 1e-5, None, None, 3, None) == 0  # empty batch
