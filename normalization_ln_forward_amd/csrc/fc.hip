@@ -160,11 +160,16 @@ __device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __re
                 const float g = (gamma && col_ok) ? gamma[col] : 1.0f;
                 const float be = (beta && col_ok) ? beta[col] : 0.0f;
                 constexpr float inv_m = 1.0f / GM;
+                // statistics around the group's first channel k: h_c - h_k =
+                // (acc_c - acc_k) + (b_c - b_k), so neither a large bias nor
+                // an offset of the group from 0 is ever rounded at its own
+                // magnitude (h itself never exists in fp32 here)
+                const float db = bb - group_first<GM>(bb);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float hv = acc[i][j][r] + bb;
-                    const float s1 = group_lanes_sum<GM>(hv);
-                    const float d = hv - s1 * inv_m;
+                    const float hk = (acc[i][j][r] - group_first<GM>(acc[i][j][r])) + db;
+                    const float s1 = group_lanes_sum<GM>(hk);
+                    const float d = hk - s1 * inv_m;
                     const float s2 = group_lanes_sum<GM>(d * d);
                     const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
                     const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
@@ -181,11 +186,16 @@ __device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __re
         const float g0 = (gamma && ok0) ? gamma[c0] : 1.0f, g1 = (gamma && ok1) ? gamma[c1] : 1.0f;
         const float be0 = (beta && ok0) ? beta[c0] : 0.0f, be1 = (beta && ok1) ? beta[c1] : 0.0f;
         constexpr float inv_m = 1.0f / 64.0f;
+        // around the group's first channel k (tile 0, this half's first lane),
+        // as for the smaller groups: h_c - h_k = (acc_c - acc_k) + (b_c - b_k)
+        const float bk = group_first<32>(bb0);
+        const float db0 = bb0 - bk, db1 = bb1 - bk;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float h0 = acc[i][0][r] + bb0, h1 = acc[i][1][r] + bb1;
+                const float ak = group_first<32>(acc[i][0][r]);
+                const float h0 = (acc[i][0][r] - ak) + db0, h1 = (acc[i][1][r] - ak) + db1;
                 const float s1 = group_lanes_sum<32>(h0) + group_lanes_sum<32>(h1);
                 const float d0 = h0 - s1 * inv_m, d1 = h1 - s1 * inv_m;
                 const float s2 = group_lanes_sum<32>(d0 * d0) + group_lanes_sum<32>(d1 * d1);

@@ -11,10 +11,14 @@
 // owns a tile of ITEMS*64 float4s of one row (ITEMS*256 channels; the whole
 // 8192-channel row when ITEMS = 32, i.e. one wave per row) and
 //   1. issues all ITEMS 128-bit loads up front (the row stays in VGPRs),
-//   2. reduces each group's sum across its L lanes with DPP quad_perm
-//      (L = 4: two row-local DPP adds, no LDS traffic), forms the mean,
-//   3. reduces the sum of squared deviations the same way (two-pass in
-//      registers), forms rstd,
+//   2. shifts the group by its first element K (broadcast from the group's
+//      first lane), reduces the group's sum of d = x - K across its L lanes
+//      with DPP quad_perm (L = 4: two row-local DPP adds, no LDS traffic) and
+//      forms mean_d (the mean is K + mean_d; the shift keeps the sum exact
+//      to fp32 rounding of the deviations, not of the values, so a group far
+//      from 0, e.g. after a large fc bias, keeps its accuracy),
+//   3. reduces the sum of squared deviations e = d - mean_d the same way
+//      (two-pass in registers), forms rstd,
 //   4. applies gamma/beta (read through L2: 32 KiB each, shared by all
 //      rows), LeakyReLU and the doubling, and writes y with nontemporal
 //      128-bit stores.
@@ -73,8 +77,9 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const int64_t c4 = c4_0 + i * kWave;
-        const float mean = group_sum<L>((v[i].x + v[i].y) + (v[i].z + v[i].w)) * inv_m;
-        const f4 d = v[i] - mean;
+        const f4 dk = v[i] - group_first<L>(v[i].x);
+        const float md = group_sum<L>((dk.x + dk.y) + (dk.z + dk.w)) * inv_m;
+        const f4 d = dk - md;
         const float ssd = group_sum<L>((d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w));
         const float rstd = 1.0f / sqrtf(ssd * inv_m + eps);
         if (c4 < C4) {
@@ -95,7 +100,8 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 }
 
 // Generic: one lane per (row, group); two passes over the group's M
-// channels for the statistics, a third for the output.
+// channels for the statistics (around the group's first element K, as in
+// the fast kernel), a third for the output.
 __global__ void __launch_bounds__(256)
 gn_lane_kernel(const float* x, const float* __restrict__ gamma, const float* __restrict__ beta, float* y,
                int64_t n_groups_total, int64_t G, int64_t C, int M, float eps, float slope)
@@ -104,18 +110,19 @@ gn_lane_kernel(const float* x, const float* __restrict__ gamma, const float* __r
     if (t >= n_groups_total) return;
     const int64_t row = t / G, g = t - row * G;
     const int64_t base = row * C + g * M;
+    const float K = x[base];
     float sum = 0.0f;
-    for (int j = 0; j < M; ++j) sum += x[base + j];
-    const float mean = sum / (float)M;
+    for (int j = 0; j < M; ++j) sum += x[base + j] - K;
+    const float md = sum / (float)M;
     float ssd = 0.0f;
     for (int j = 0; j < M; ++j) {
-        const float d = x[base + j] - mean;
+        const float d = (x[base + j] - K) - md;
         ssd += d * d;
     }
     const float rstd = 1.0f / sqrtf(ssd / (float)M + eps);
     for (int j = 0; j < M; ++j) {
         const int64_t c = g * M + j;
-        float z = (x[base + j] - mean) * rstd;
+        float z = ((x[base + j] - K) - md) * rstd;
         if (gamma) z = z * gamma[c];
         if (beta) z = z + beta[c];
         y[base + j] = lrelu_x2(z, slope);
@@ -132,12 +139,13 @@ gn_wave_kernel(const float* x, const float* __restrict__ gamma, const float* __r
     if (t >= n_groups_total) return;
     const int64_t row = t / G, g = t - row * G;
     const int64_t base = row * C + g * M;
+    const float K = x[base];  // shift: the group's first element
     float sum = 0.0f;
-    for (int64_t j = lane; j < M; j += kWave) sum += x[base + j];
-    const float mean = wave_sum(sum) / (float)M;
+    for (int64_t j = lane; j < M; j += kWave) sum += x[base + j] - K;
+    const float md = wave_sum(sum) / (float)M;
     float ssd = 0.0f;
     for (int64_t j = lane; j < M; j += kWave) {
-        const float d = x[base + j] - mean;
+        const float d = (x[base + j] - K) - md;
         ssd += d * d;
     }
     const float rstd = 1.0f / sqrtf(wave_sum(ssd) / (float)M + eps);
@@ -145,7 +153,7 @@ gn_wave_kernel(const float* x, const float* __restrict__ gamma, const float* __r
     // (wave_sum is a wave-wide exchange), which keeps y == x safe.
     for (int64_t j = lane; j < M; j += kWave) {
         const int64_t c = g * M + j;
-        float z = (x[base + j] - mean) * rstd;
+        float z = ((x[base + j] - K) - md) * rstd;
         if (gamma) z = z * gamma[c];
         if (beta) z = z + beta[c];
         y[base + j] = lrelu_x2(z, slope);

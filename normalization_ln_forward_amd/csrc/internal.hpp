@@ -72,6 +72,9 @@ constexpr size_t kLnErrorWordOffset = 8;
 // Byte offset of the control-wave kernel's count of workgroup sums that a
 // reader computed itself (after waiting past its spin limit, or forced).
 constexpr size_t kLnRecomputedWordOffset = 12;
+// Byte offset of the control-wave kernel's generation (launches so far on
+// the workspace, mod 255); its exchange tags derive from it.
+constexpr size_t kLnCtlGenWordOffset = 16;
 // Test knob, read once from NORMFWD_LN_FORCE_RECOMPUTE (0 = off): a power of
 // two k makes the control-wave kernel ignore the published sums of every
 // workgroup j with j % k == k - 1 and compute them from x instead, which

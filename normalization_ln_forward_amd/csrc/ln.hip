@@ -49,6 +49,7 @@
 // loads and stores (see the protocol notes below), never with fences.
 #include "common.hpp"
 #include "internal.hpp"
+#include "ln_tag.hpp"
 
 #include <algorithm>
 #include <cstddef>
@@ -62,15 +63,17 @@ struct alignas(32) Partial {
 };
 
 struct LnCtrl {
-    uint32_t gen;    // generation: incremented by the last workgroup of each single-kernel launch
-    uint32_t done;   // completion counter of the current launch (returns to 0)
+    uint32_t gen;    // last-workgroup-merges kernel: launches so far (its flags carry the next value)
+    uint32_t done;   // completion counter of the current single-kernel launch (returns to 0)
     uint32_t error;  // set to 1 if a wait ran past its spin limit (last-workgroup-merges kernel)
-    uint32_t recomputed;  // control-wave kernel: workgroup sums computed by a reader instead (diagnostic)
-    uint32_t pad[60];
+    uint32_t recomputed;  // control-wave kernel: workgroup moments computed by a reader instead (diagnostic)
+    uint32_t gen_ctl;     // control-wave kernel: launches so far mod 255 (its exchange tags derive from the next value)
+    uint32_t pad[59];
 };
 static_assert(sizeof(LnCtrl) == 256, "control block is 256 bytes");
 static_assert(offsetof(LnCtrl, error) == kLnErrorWordOffset, "error word where the API reads it");
 static_assert(offsetof(LnCtrl, recomputed) == kLnRecomputedWordOffset, "recompute count where the tests read it");
+static_assert(offsetof(LnCtrl, gen_ctl) == kLnCtlGenWordOffset, "control-wave generation where the tests read it");
 
 constexpr int kLnThreads = 256;
 // The single kernel's arrival counters: a ring of kRing, each on its own
@@ -82,10 +85,14 @@ constexpr int kRing = 4;
 // launch, so a launch whose workgroups are not all resident ends instead of
 // hanging.
 constexpr uint32_t kSpinLimit = 1u << 18;
-// The control-wave kernel, once one of its waits has run out: later waits
-// give up after this many polls (~1-2 ms), since the missing workgroup is
-// most likely still not resident.
-constexpr uint32_t kSpinLimitAfterMiss = 1u << 10;
+// The control-wave kernel needs no co-residency for its result: a reader
+// that has polled this often for a workgroup's moments (~0.3-0.5 ms, tens of
+// samples' streaming time, far beyond the skew of a healthy launch) computes
+// them from x itself; once one wait has run out, later waits give up after
+// kSpinLimitAfterMiss polls, since the missing workgroup is most likely
+// still not resident.
+constexpr uint32_t kCtlSpinLimit = 1u << 8;
+constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 
 // Split schedule tuning: elements per partial-moment workgroup, rows in
 // flight per thread in the moments pass, XCD-aware row order in the
@@ -184,42 +191,18 @@ __device__ __forceinline__ void chan_merge(double& n, double& m, double& m2, dou
     n = nn;
 }
 
-// Workgroup-wide sums of the lane accumulators a1 (sum of d) and a2 (sum of
-// d^2), widened to fp64, in a fixed order; the result is valid in thread 0.
-// red: LDS of 2*(NT/64) doubles.
-__device__ __forceinline__ void block_moments(f4 a1, f4 a2, double* red, double& s1, double& s2)
+// Sum of one double per thread over the workgroup, fixed order; valid in
+// every thread on return.  red: LDS of NT/64 + 1 doubles.
+__device__ __forceinline__ double block_sum(double v, double* red)
 {
-    double t1 = ((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w);
-    double t2 = ((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w);
-    t1 = wave_sum(t1);
-    t2 = wave_sum(t2);
+    v = wave_sum(v);
     const int wave = threadIdx.x / kWave;
     __syncthreads();  // red may still be read from a previous use
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-        red[2 * wave] = t1;
-        red[2 * wave + 1] = t2;
-    }
+    if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        s1 = red[0];
-        s2 = red[1];
-        for (int w = 1; w < kLnThreads / kWave; ++w) {
-            s1 += red[2 * w];
-            s2 += red[2 * w + 1];
-        }
-    }
-}
-
-__device__ __forceinline__ Partial make_partial(int64_t n, float K, double s1, double s2)
-{
-    Partial p{};
-    if (n > 0) {
-        const double dn = (double)n;
-        p.n = dn;
-        p.mean = (double)K + s1 / dn;
-        p.m2 = fmax(s2 - s1 * (s1 / dn), 0.0);
-    }
-    return p;
+    double t = red[0];
+    for (int w = 1; w < kLnThreads / kWave; ++w) t += red[w];
+    return t;
 }
 
 // Cross-workgroup protocol.  The 8 XCDs have their own L2s, which are not
@@ -403,7 +386,7 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
 {
     using V = typename LnVec<VEC>::T;
     constexpr int U = NORMFWD_LN_PARTIAL_UNROLL;
-    __shared__ double red[2 * kLnThreads / kWave];
+    __shared__ double red[kLnThreads / kWave];
     const int64_t blk = NORMFWD_LN_XCD_CONTIG ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
     const int64_t b = blk / P;
     const int64_t p = blk - b * P;
@@ -411,14 +394,22 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
     const V* xv = reinterpret_cast<const V*>(xb);
     const int64_t nu = inner / VEC;
     const int64_t nrows = ceil_div(nu, (int64_t)kLnThreads);
-    const float K = xb[0];
+    // Every float4 component of a thread sums d = x - K and d^2 around its own
+    // shift K, the first value it reads: a member of the very set it sums,
+    // so the cancellation in M2 = sum d^2 - (sum d)^2 / n costs at most a few
+    // fp32 roundings of that set's own M2, whatever its offset from 0.
+    // (Positions past the end load K: d = 0, and they are not counted.)
+    const int64_t j_first = p * kLnThreads + threadIdx.x;
+    const V K = j_first < nu ? xv[j_first] : V(0.0f);
     V a1 = V(0.0f), a2 = V(0.0f);
+    int cnt = 0;
     for (int64_t r = p; r < nrows; r += P * U) {
         V v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t j = (r + (int64_t)u * P) * kLnThreads + threadIdx.x;
-            v[u] = j < nu ? (NORMFWD_LN_PARTIAL_NT ? ld_nt(xv + j) : xv[j]) : V(K);
+            cnt += j < nu;
+            v[u] = j < nu ? (NORMFWD_LN_PARTIAL_NT ? ld_nt(xv + j) : xv[j]) : K;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -427,25 +418,48 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
             a2 += d * d;
         }
     }
-    f4 a1f, a2f;
+    // Per component: n = cnt, mean_c = K_c + a1_c / n, M2_c = a2_c - a1_c^2 / n;
+    // merged over the workgroup in a fixed order: mean = sum n mean_c / N,
+    // M2 = sum (M2_c + n (mean_c - mean)^2) (the k-way pairwise update).
+    f4 K4, a14, a24;
     if constexpr (VEC == 4) {
-        a1f = a1;
-        a2f = a2;
+        K4 = K;
+        a14 = a1;
+        a24 = a2;
     } else {
-        a1f = f4{a1, 0.0f, 0.0f, 0.0f};
-        a2f = f4{a2, 0.0f, 0.0f, 0.0f};
+        K4 = f4{K, 0.0f, 0.0f, 0.0f};
+        a14 = f4{a1, 0.0f, 0.0f, 0.0f};
+        a24 = f4{a2, 0.0f, 0.0f, 0.0f};
     }
-    double s1 = 0.0, s2 = 0.0;
-    block_moments(a1f, a2f, red, s1, s2);
+    const double nl = (double)cnt;
+    double mc[VEC], sum_nm = 0.0;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+        mc[c] = cnt ? (double)K4[c] + (double)a14[c] / nl : 0.0;
+        sum_nm += nl * mc[c];
+    }
+    const double n_wg = (double)(rows_owned_units(nu, p, P) * VEC);
+    const double mean = n_wg > 0.0 ? block_sum(sum_nm, red) / n_wg : 0.0;
+    double sum_m2 = 0.0;
+    if (cnt) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            const double t1 = (double)a14[c], dm = mc[c] - mean;
+            sum_m2 += fmax((double)a24[c] - t1 * (t1 / nl), 0.0) + nl * (dm * dm);
+        }
+    }
+    Partial q{};
+    q.n = n_wg;
+    q.mean = mean;
+    q.m2 = block_sum(sum_m2, red);
     Partial* pb = parts + b * P_cap;
     if (counters == nullptr) {
-        if (threadIdx.x == 0) pb[p] = make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2);
+        if (threadIdx.x == 0) pb[p] = q;
         return;
     }
     __shared__ int last;
     uint32_t* counter = counters + b * kCounterStride;
-    if (threadIdx.x == 0)
-        last = deliver_partial(&pb[p], make_partial(rows_owned_units(nu, p, P) * VEC, K, s1, s2), counter, P);
+    if (threadIdx.x == 0) last = deliver_partial(&pb[p], q, counter, P);
     __syncthreads();
     if (!last || threadIdx.x >= kWave) return;
     double n, m, m2;
@@ -561,20 +575,6 @@ ln_normalize_rows_kernel(const float* x, const float* w, const float* bias, floa
 
 // ---------------------------------------------------------------- one workgroup per sample
 
-// Sum of one double per thread over the workgroup, fixed order; valid in
-// every thread on return.  red: LDS of NT/64 + 1 doubles.
-__device__ __forceinline__ double block_sum(double v, double* red)
-{
-    v = wave_sum(v);
-    const int wave = threadIdx.x / kWave;
-    __syncthreads();  // red may still be read from a previous use
-    if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
-    __syncthreads();
-    double t = red[0];
-    for (int w = 1; w < kLnThreads / kWave; ++w) t += red[w];
-    return t;
-}
-
 // Samples of at most 256 * UPT units (a unit is one float4, or one float
 // on the scalar path): one workgroup holds the whole sample in VGPRs, takes
 // the two passes over registers (mean of d = x - K with K the sample's first
@@ -609,21 +609,32 @@ ln_row_kernel(const float* x, const float* w, const float* bias, float* y, int64
     const double n = (double)inner;
     const double mean_d = block_sum(t, red) / n;
     const float md = (float)mean_d;
-    V q = V(0.0f);
+    // second pass around K + md, which lies inside the data: the sums of
+    // e = (x - K) - md and e^2 are accurate whatever the first pass's rounding
+    // (its fp32 sums of d may be far from 0 when K is not typical of the
+    // sample), and sum e / n corrects the mean: mean = K + md + sum e / n,
+    // var = sum e^2 / n - (sum e / n)^2
+    V q = V(0.0f), q1 = V(0.0f);
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
         const V e = (v[k] - K) - md;  // padding lanes hold K: e = -md, masked below
         const int64_t j = threadIdx.x + (int64_t)k * kLnThreads;
-        if (j < nu) q += e * e;
+        if (j < nu) {
+            q1 += e;
+            q += e * e;
+        }
     }
-    if constexpr (VEC == 4)
+    double t1;
+    if constexpr (VEC == 4) {
         t = ((double)q.x + (double)q.y) + ((double)q.z + (double)q.w);
-    else
+        t1 = ((double)q1.x + (double)q1.y) + ((double)q1.z + (double)q1.w);
+    } else {
         t = (double)q;
-    // sum of (d - md)^2 = sum of (d - mean_d)^2 + n (mean_d - md)^2
-    const double dm = mean_d - (double)md;
-    const double var = fmax(block_sum(t, red) / n - dm * dm, 0.0);
-    const double mean = (double)K + mean_d;
+        t1 = (double)q1;
+    }
+    const double de = block_sum(t1, red) / n;
+    const double var = fmax(block_sum(t, red) / n - de * de, 0.0);
+    const double mean = ((double)K + (double)md) + de;
     const double rstd = 1.0 / sqrt(var + (double)eps);
     const float hi = (float)mean;
     const float lo = (float)(mean - (double)hi);
@@ -646,6 +657,104 @@ ln_row_kernel(const float* x, const float* w, const float* bias, float* y, int64
 }
 
 // ---------------------------------------------------------------- single-kernel variant
+
+// One float4 of d = x - m into a thread's running sums of d and d^2.  Every
+// place that must reproduce these sums bit for bit goes through here, so
+// they round the same way (the square and the add contract to one fused
+// multiply-add on gfx950).
+__device__ __forceinline__ void shifted_acc(f4& a1, f4& a2, const f4 d)
+{
+    a1 += d;
+    a2 += d * d;
+}
+
+// A wave's sums of its lanes' (a1, a2), widened to fp64, in a fixed order
+// (wave_total); uniform on return.
+__device__ __forceinline__ void wave_moments(const f4 a1, const f4 a2, double& t1, double& t2)
+{
+    t1 = wave_total(((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w));
+    t2 = wave_total(((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w));
+}
+
+// Layout of ln_single_ctl_kernel: DW data waves of 64 threads, F4PT float4
+// per thread; thread i of workgroup j holds float4s j*RW + i + k*P*RW (k <
+// F4PT, RW = 64 DW) of each sample, where those are < nv.  Elements (fp32
+// values) data wave w of workgroup j holds of one sample:
+template <int F4PT, int DW>
+__device__ __forceinline__ uint32_t ctl_wave_elems(uint32_t j, int w, uint32_t P, int64_t nv)
+{
+    constexpr int64_t RW = DW * kWave;
+    uint32_t n = 0;
+#pragma unroll 1
+    for (int k = 0; k < F4PT; ++k) {
+        const int64_t left = nv - ((int64_t)j * RW + (int64_t)w * kWave + (int64_t)k * P * RW);
+        n += (uint32_t)(left <= 0 ? 0 : left >= kWave ? kWave : left);
+    }
+    return 4u * n;
+}
+// ... and workgroup j as a whole:
+template <int F4PT, int DW>
+__device__ __forceinline__ uint32_t ctl_wg_elems(uint32_t j, uint32_t P, int64_t nv)
+{
+    constexpr int64_t RW = DW * kWave;
+    uint32_t n = 0;
+#pragma unroll 1
+    for (int k = 0; k < F4PT; ++k) {
+        const int64_t left = nv - ((int64_t)j * RW + (int64_t)k * P * RW);
+        n += (uint32_t)(left <= 0 ? 0 : left >= RW ? RW : left);
+    }
+    return 4u * n;
+}
+
+// Moments of one data wave's share of a sample, two passes over the
+// registers that hold it:
+//   1. m = the wave's mean in fp32 (a float4 sum per lane over its valid
+//      elements, in element order, then wave_shift): only a shift, so its
+//      rounding does not matter, but it sits inside the data, so
+//   2. the sums of d = x - m and d^2 (shifted_acc per element in element
+//      order, fp32 per lane, then wave_moments in fp64) lose nothing to
+//      cancellation, whatever the data's offset from 0: the wave's M2 is
+//      t2 - t1^2 / n with t1 ~ 0.
+// The data waves and a reader that recomputes a missing workgroup's
+// moments (ctl_recompute) run these same steps on the same elements, so they
+// get the same bits.  (The two loops are written out at both places: a
+// helper taking the register tile by reference measured 18 spilled VGPRs in
+// the data waves' loop, the loops inline none.)
+struct WaveMoments {
+    double t1, t2;  // sums of d and d^2 over the wave's elements
+    float m;        // the shift
+};
+__device__ __forceinline__ float wave_shift(const f4 s, uint32_t n)
+{
+    const float tot = wave_total((s.x + s.y) + (s.z + s.w));
+    return n ? tot / (float)n : 0.0f;
+}
+
+// A workgroup's (mean, M2) from its waves' moments (rd[3w .. 3w+2] = t1,
+// t2, m of wave w; cnt[w] its element count), merged in wave order:
+// mean = sum n_w mean_w / n, M2 = sum (M2_w + n_w (mean_w - mean)^2), the
+// k-way form of the pairwise (Chan) update.  Thread-local arithmetic in a
+// fixed order, so every caller gets the same bits.
+template <int DW>
+__device__ __forceinline__ void merge_wave_moments(const double* rd, const uint32_t* cnt, double& mean, double& m2)
+{
+    double n = 0.0, sm = 0.0;
+    for (int w = 0; w < DW; ++w) {
+        if (!cnt[w]) continue;
+        const double nw = (double)cnt[w];
+        n += nw;
+        sm += nw * (rd[3 * w + 2] + rd[3 * w] / nw);
+    }
+    mean = n > 0.0 ? sm / n : 0.0;
+    m2 = 0.0;
+    for (int w = 0; w < DW; ++w) {
+        if (!cnt[w]) continue;
+        const double nw = (double)cnt[w];
+        const double t1 = rd[3 * w];
+        const double d = (rd[3 * w + 2] + t1 / nw) - mean;
+        m2 += fmax(rd[3 * w + 1] - t1 * (t1 / nw), 0.0) + nw * (d * d);
+    }
+}
 
 // Last arriver of sample t in the single kernel: merge its partials, store
 // the statistics, reset the sample's counter and announce flag[t] = target.
@@ -705,6 +814,8 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     __shared__ double lds[3 * kLnThreads];
+    __shared__ double red[3 * (kLnThreads / kWave)];  // [wave]: t1, t2, shift
+    __shared__ uint32_t cnt[kLnThreads / kWave];      // [wave]: elements it holds
     __shared__ int s_last;
     __shared__ f4 s_stats;
     f4* w_s = reinterpret_cast<f4*>(smem_raw);
@@ -739,22 +850,40 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
         }
     }
     const int64_t n_mine = rows_owned_units(nv, p, P) * 4;
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid / kWave);
+    uint32_t n_wave = 0;  // elements this wave holds of each sample
+#pragma unroll
+    for (int k = 0; k < F4PT; ++k) n_wave += 4u * (uint32_t)__builtin_popcountll(__ballot(valid(k)));
+    if ((tid & (kWave - 1)) == 0) cnt[wave_id] = n_wave;
     __syncthreads();
 
     for (int64_t t = 0; t <= outer; ++t) {
         if (t < outer) {
-            const float K = x[t * inner];
+            // two passes over the wave's registers (see WaveMoments), then the
+            // waves' moments merged in wave order by thread 0
+            f4 s = f4(0.0f);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) s += valid(k) ? cur[k] : f4(0.0f);
+            const float m = wave_shift(s, n_wave);
             f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
-            for (int k = 0; k < F4PT; ++k) {
-                const f4 d = valid(k) ? cur[k] - K : f4(0.0f);
-                a1 += d;
-                a2 += d * d;
+            for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? cur[k] - m : f4(0.0f));
+            double t1, t2;
+            wave_moments(a1, a2, t1, t2);
+            __syncthreads();  // red may still be read from the previous sample
+            if ((tid & (kWave - 1)) == 0) {
+                red[3 * wave_id] = t1;
+                red[3 * wave_id + 1] = t2;
+                red[3 * wave_id + 2] = (double)m;
             }
-            double s1 = 0.0, s2 = 0.0;
-            block_moments(a1, a2, lds, s1, s2);
+            __syncthreads();
             uint32_t* counter = counters + (t % kRing) * kCounterStride;
-            if (tid == 0) s_last = deliver_partial(parts + t * P_cap + p, make_partial(n_mine, K, s1, s2), counter, P);
+            if (tid == 0) {
+                Partial q{};
+                q.n = (double)n_mine;
+                merge_wave_moments<kLnThreads / kWave>(red, cnt, q.mean, q.m2);
+                s_last = deliver_partial(parts + t * P_cap + p, q, counter, P);
+            }
             __syncthreads();
             if (s_last)
                 merge_and_announce(parts + t * P_cap, P, eps, lds, stats + t, mean_out ? mean_out + t : nullptr,
@@ -799,81 +928,48 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
     }
 }
 
-// Generation-tagged fp64 words: the low 8 bits of the mantissa carry the
-// launch generation, so a reader can tell this launch's value from the one a
-// previous launch left in the same slot without a separate flag (an aligned
-// 8-byte store is seen whole or not at all).  The reader clears the tag
-// before use; the 2^-44 relative change is the same in every launch.
-__device__ __forceinline__ double tag_word(double v, uint32_t tag)
-{
-    return __longlong_as_double((long long)(((uint64_t)__double_as_longlong(v) & ~0xFFull) | (tag & 0xFFu)));
-}
-__device__ __forceinline__ bool has_tag(double v, uint32_t tag)
-{
-    return ((uint64_t)__double_as_longlong(v) & 0xFFull) == (tag & 0xFFu);
-}
-__device__ __forceinline__ double untag(double v)
-{
-    return __longlong_as_double((long long)((uint64_t)__double_as_longlong(v) & ~0xFFull));
-}
-
-// One float4 of d = x - K into a thread's running sums of d and d^2.  Every
-// place that must reproduce these sums bit for bit goes through here, so
-// they round the same way (the square and the add contract to one fused
-// multiply-add on gfx950).
-__device__ __forceinline__ void shifted_acc(f4& a1, f4& a2, const f4 d)
-{
-    a1 += d;
-    a2 += d * d;
-}
-
-// A wave's sums of its lanes' (a1, a2), widened to fp64 in a fixed order;
-// every lane ends with the same bits (each butterfly step adds the same two
-// values on both partners).
-__device__ __forceinline__ void wave_moments(const f4 a1, const f4 a2, double& t1, double& t2)
-{
-    t1 = wave_sum(((double)a1.x + (double)a1.y) + ((double)a1.z + (double)a1.w));
-    t2 = wave_sum(((double)a2.x + (double)a2.y) + ((double)a2.z + (double)a2.w));
-}
-
-// The sums workgroup j of ln_single_ctl_kernel publishes for one sample
-// (xs: the sample's float4s), computed by one whole wave from x: lane l
-// replays thread w * 64 + l of j's data waves for w = 0 .. DW-1 with the
-// same elements, the same order of additions and the same wave reduction,
-// and the wave totals are added in wave order, so the result has exactly
-// the bits j itself would publish.  Used when j's sums do not arrive.
-// One load in flight at a time: few registers, so that this rarely taken
-// path does not raise the kernel's register count (the data waves' loop sits
-// at its limit), and no call.
-struct CtlSums {
-    double s1, s2;
-};
+// The (mean, M2) workgroup j of ln_single_ctl_kernel publishes for one
+// sample (xs: the sample's float4s), computed by one whole wave from x: for
+// each data wave w of j, lane l loads what thread w * 64 + l of j holds and
+// takes the same two passes (wave_two_pass), and the wave results are merged
+// by merge_wave_moments in wave order, so the result has exactly the bits j itself
+// publishes.  Used when j's moments do not arrive.  rc: LDS for 3 DW doubles
+// and DW counts, private to the calling wave.
 template <int F4PT, int DW>
-__device__ __forceinline__ CtlSums ctl_recompute_sums(const f4* xs, float K, uint32_t j, uint32_t P, int64_t nv)
+__device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, double* rc, uint32_t* rc_cnt,
+                              double& mean, double& m2)
 {
-    double s1 = 0.0, s2 = 0.0;
-    constexpr int RW = DW * kWave;
+    constexpr uint32_t RW = DW * kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t stride = P * (uint32_t)RW;
-    for (int w = 0; w < DW; ++w) {
-        const uint32_t off0 = j * (uint32_t)RW + (uint32_t)(w * kWave + lane);
-        f4 a1 = f4(0.0f), a2 = f4(0.0f);
+    const uint32_t stride = P * RW;
 #pragma unroll 1
-        for (int k = 0; k < F4PT; ++k) {
-            const uint32_t idx = off0 + (uint32_t)k * stride;
-            shifted_acc(a1, a2, (int64_t)idx < nv ? ld_nt(xs + idx) - K : f4(0.0f));
-        }
-        double t1, t2;
-        wave_moments(a1, a2, t1, t2);
-        if (w == 0) {
-            s1 = t1;
-            s2 = t2;
-        } else {
-            s1 += t1;
-            s2 += t2;
+    for (int w = 0; w < DW; ++w) {
+        const uint32_t off0 = j * RW + (uint32_t)(w * kWave + lane);
+        auto ok = [&](int k) { return (int64_t)(off0 + (uint32_t)k * stride) < nv; };
+        f4 v[F4PT];
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) v[k] = ok(k) ? ld_nt(xs + off0 + (uint32_t)k * stride) : f4(0.0f);
+        const uint32_t n = ctl_wave_elems<F4PT, DW>(j, w, P, nv);
+        // the data waves' two passes (see WaveMoments)
+        f4 s = f4(0.0f);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) s += ok(k) ? v[k] : f4(0.0f);
+        WaveMoments r;
+        r.m = wave_shift(s, n);
+        f4 a1 = f4(0.0f), a2 = f4(0.0f);
+#pragma unroll
+        for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, ok(k) ? v[k] - r.m : f4(0.0f));
+        wave_moments(a1, a2, r.t1, r.t2);
+        if (lane == 0) {
+            rc[3 * w] = r.t1;
+            rc[3 * w + 1] = r.t2;
+            rc[3 * w + 2] = (double)r.m;
+            rc_cnt[w] = n;
         }
     }
-    return CtlSums{s1, s2};
+    if (lane == 0) merge_wave_moments<DW>(rc, rc_cnt, mean, m2);
+    mean = __shfl(mean, 0);
+    m2 = __shfl(m2, 0);
 }
 
 // Single-read schedule with a control wave.  DW data waves hold the
@@ -884,21 +980,21 @@ __device__ __forceinline__ CtlSums ctl_recompute_sums(const f4* xs, float K, uin
 // polled memory would also wait for its own prefetch).  One workgroup
 // barrier per sample; sample s is normalized LAG iterations after its
 // moments:
-//   data waves, iteration t:  moments of sample t -> per-wave sums in LDS;
-//       barrier t; normalize and store sample t-LAG with the statistics the
-//       control wave left in LDS, then load sample t-LAG+NT into the freed
-//       registers (NT = LAG + 2 register tiles: sample t+1 is in flight
-//       while t is reduced, and t+2 is issued at the end of the iteration).
-//   control wave, after barrier t:  publish this workgroup's sums of
-//       d = x - K and d^2 for sample t (K the sample's first element, shared
-//       by every workgroup) as two generation-tagged words; then read all P
-//       workgroups' sums of sample t-LAG+1 until every tag is current, add
-//       them in a fixed order (every workgroup computes the same statistics:
-//       mean = K + S1/N, sum of squared deviations = S2 - S1^2/N, the shifted
-//       form of the pairwise merge when all parts share one shift) and leave
-//       the statistics in LDS before barrier t+1.
+//   data waves, iteration t:  two-pass moments of their share of sample t
+//       (wave_two_pass) -> LDS; barrier t; normalize and store sample t-LAG
+//       with the statistics the control wave left in LDS, then load sample
+//       t-LAG+NT into the freed registers (NT = LAG + 2 register tiles:
+//       sample t+1 is in flight while t is reduced, and t+2 is issued at
+//       the end of the iteration).
+//   control wave, after barrier t:  merge the data waves' moments of sample
+//       t into this workgroup's (mean, M2) (merge_wave_moments) and publish them
+//       as two generation-tagged words; then read all P workgroups' words
+//       for sample t-LAG+1 until every tag is current, merge them in a fixed
+//       order (every workgroup computes the same statistics; the k-way
+//       pairwise update around one shift, workgroup 0's mean, in fp64) and
+//       leave the statistics in LDS before barrier t+1.
 // With LAG = 2 every workgroup has had a whole iteration to publish the
-// sums the control wave gathers, so the gather rarely waits and the data
+// moments the control wave gathers, so the gather rarely waits and the data
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges protocol of
 // ln_single_hold_kernel measured slower here: its chain of arrival atomic,
@@ -938,9 +1034,10 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    __shared__ double red[2][2 * DW];  // [sample parity][wave]: sum d, sum d^2
+    __shared__ double red[2][3 * DW];  // [sample parity][wave]: t1, t2, shift
     __shared__ f4 s_stats[2];          // [sample parity]: mean hi, mean lo, rstd
-    __shared__ float s_K[4];           // [sample % 4]: the sample's shift K (its first element)
+    __shared__ double rc[3 * DW];      // control wave: a recomputed workgroup's wave moments
+    __shared__ uint32_t cnt[2][DW];    // control wave: element counts of this workgroup's / a recomputed one's waves
     f4* w_s = reinterpret_cast<f4*>(smem_raw);
     f4* b_s = w_s + (w ? F4PT * RW : 0);
     // `groups` groups of P workgroups; group gr takes samples gr, gr + groups,
@@ -966,54 +1063,37 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     const int64_t steps = outer + LAG;  // iterations = barriers after the prologue
 
     if (tid >= RW) {
-        // ---- control wave.  It also hands the data waves each sample's
-        // shift: K of sample t+2 is written during iteration t, so the data
-        // waves find it in LDS when they reduce that sample (after barrier
-        // t+1), and their memory counters see only x tiles and y stores.
-        const uint32_t target = dev_load(&ctrl->gen) + 1u;
+        // ---- control wave
+        const uint32_t gen_target = ln_next_generation(dev_load(&ctrl->gen_ctl));
+        const uint32_t tag = ln_tag_of(gen_target);
         uint32_t limit = spin_limit;
-        // test knob: a silent workgroup publishes its sums under a tag no
-        // reader of this launch accepts (the generation with its top bit
-        // flipped: never the next launch's either), so every reader (itself
-        // included) computes them from x
+        // test knob: a silent workgroup does not publish at all, so every
+        // reader (itself included) computes its moments from x
         const bool silent = ((uint32_t)p & silent_mask) == silent_mask;
-        const uint32_t pub_tag = silent ? target ^ 0x80u : target;
-        if (lane == 0) {
-            s_K[0] = x[0];
-            if (outer > 1) s_K[1] = x[sstride];
-        }
-        __syncthreads();  // prologue: w/b and the first shifts in LDS
+        if (lane < DW) cnt[0][lane] = ctl_wave_elems<F4PT, DW>((uint32_t)p, lane, (uint32_t)P, nv);
+        __syncthreads();  // prologue: w/b in LDS
         for (int64_t t = 0; t < steps; ++t) {
-            __syncthreads();  // barrier t: the wave sums of sample t are in LDS
-            const bool next_k = t + 2 < outer;
-            const float k_next = next_k ? x[(t + 2) * sstride] : 0.0f;
-            if (t < outer && lane == 0) {
-                // this workgroup's sums of d = x - K and d^2 over its elements of sample t
-                const double* rd = red[t & 1];
-                double s1 = rd[0], s2 = rd[1];
-                for (int wv = 1; wv < DW; ++wv) {
-                    s1 += rd[2 * wv];
-                    s2 += rd[2 * wv + 1];
-                }
-                Partial* q = parts + t * pstride + p;
-                dev_store(&q->n, tag_word(s1, pub_tag));
-                dev_store(&q->mean, tag_word(s2, pub_tag));
+            __syncthreads();  // barrier t: the wave moments of sample t are in LDS
+            if (t < outer && lane == 0 && !silent) {
+                // this workgroup's (mean, M2) over its elements of sample t
+                double mean, m2;
+                merge_wave_moments<DW>(red[t & 1], cnt[0], mean, m2);
+                double* q = reinterpret_cast<double*>(parts + t * pstride + p);
+                dev_store(q, ln_tag_word(mean, tag));
+                dev_store(q + 1, ln_tag_word(m2, tag));
             }
             const int64_t g = t - (LAG - 1);  // the sample gathered now, normalized after barrier g + LAG
-            if (g < 0 || g >= outer) {
-                if (next_k && lane == 0) s_K[(t + 2) & 3] = k_next;
-                continue;
-            }
-            const float K = s_K[g & 3];
-            // gather every workgroup's sums (lane l: workgroups l, l + 64, ...),
-            // retrying until every tag is current, then a fixed-order sum.
-            // Sums that have not arrived after `limit` polls (their workgroup
-            // is not resident: an ordinary launch does not promise that every
-            // workgroup runs at once) are computed here from x, with the same
-            // bits; x of sample g is still intact then, also in place, since a
-            // workgroup overwrites its rows of g only after publishing its sums.
+            if (g < 0 || g >= outer) continue;
+            // gather every workgroup's words (lane l: workgroups l, l + 64,
+            // ...), retrying until every tag is current.  Words that have not
+            // arrived after `limit` polls (their workgroup is not resident:
+            // an ordinary launch does not promise that every workgroup runs
+            // at once) are computed here from x, with the same bits, and
+            // published in the owner's slot for the other readers (the owner,
+            // once it runs, stores the same bits there).  x of sample g is
+            // still intact: the kernel does not run in place.
             const Partial* pb = parts + g * pstride;
-            double S1 = 0.0, S2 = 0.0;
+            double c = 0.0, A = 0.0, B = 0.0;  // shift, sum n_j (mean_j - c), sum M2_j + n_j (mean_j - c)^2
             for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
                 double a[4], b2[4];
                 uint32_t spins = 0;
@@ -1023,10 +1103,10 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int64_t j = j0 + lane + (int64_t)u * kWave;
-                        const Partial* q = pb + (j < P ? j : p);
-                        a[u] = dev_load(&q->n);
-                        b2[u] = dev_load(&q->mean);
-                        ok = ok && has_tag(a[u], target) && has_tag(b2[u], target);
+                        const double* q = reinterpret_cast<const double*>(pb + (j < P ? j : p));
+                        a[u] = dev_load(q);
+                        b2[u] = dev_load(q + 1);
+                        ok = ok && ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag);
                     }
                     if (__all(ok)) break;
                     __builtin_amdgcn_s_sleep(2);
@@ -1043,15 +1123,22 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int64_t j = j0 + lane + (int64_t)u * kWave;
-                        uint64_t todo = __ballot(j < P && !(has_tag(a[u], target) && has_tag(b2[u], target)));
+                        uint64_t todo = __ballot(j < P && !(ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag)));
                         while (todo) {
                             const int l = __builtin_ctzll(todo);
                             todo &= todo - 1;
-                            const CtlSums r =
-                                ctl_recompute_sums<F4PT, DW>(xg, K, (uint32_t)(j0 + l + u * kWave), (uint32_t)P, nv);
+                            const uint32_t jj = (uint32_t)(j0 + l + u * kWave);
+                            double mean, m2;
+                            ctl_recompute<F4PT, DW>(xg, jj, (uint32_t)P, nv, rc, cnt[1], mean, m2);
+                            const double tm = ln_tag_word(mean, tag), tv = ln_tag_word(m2, tag);
                             if (lane == l) {
-                                a[u] = tag_word(r.s1, target);
-                                b2[u] = tag_word(r.s2, target);
+                                a[u] = tm;
+                                b2[u] = tv;
+                            }
+                            if (lane == 0) {
+                                double* q = reinterpret_cast<double*>(parts + g * pstride + jj);
+                                dev_store(q, tm);
+                                dev_store(q + 1, tv);
                             }
                             ++n_done;
                         }
@@ -1059,28 +1146,30 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                     if (lane == 0)
                         __hip_atomic_fetch_add(&ctrl->recomputed, n_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
+                if (j0 == 0) c = ln_untag(__shfl(a[0], 0));  // workgroup 0's mean
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    if (j0 + lane + (int64_t)u * kWave < P) {
-                        S1 += untag(a[u]);
-                        S2 += untag(b2[u]);
+                    const int64_t j = j0 + lane + (int64_t)u * kWave;
+                    if (j < P) {
+                        const double nj = (double)ctl_wg_elems<F4PT, DW>((uint32_t)j, (uint32_t)P, nv);
+                        const double d = ln_untag(a[u]) - c;
+                        A += nj * d;
+                        B += ln_untag(b2[u]) + nj * (d * d);
                     }
                 }
             }
-            S1 = wave_sum(S1);
-            S2 = wave_sum(S2);
+            A = wave_sum(A);
+            B = wave_sum(B);
             if (lane == 0) {
-                // mean = K + S1/N; sum of squared deviations = S2 - S1^2/N
                 const double N = (double)inner;
-                const double md = S1 / N;
-                const f4 st = finish_stats(N, (double)K + md, fmax(S2 - S1 * md, 0.0), eps);
+                const double md = A / N;
+                const f4 st = finish_stats(N, c + md, fmax(B - A * md, 0.0), eps);
                 s_stats[g & 1] = st;
                 if (p == 0) {
                     stats[g * groups] = st;
                     if (mean_out) mean_out[g * groups] = st.x;
                     if (rstd_out) rstd_out[g * groups] = st.z;
                 }
-                if (next_k) s_K[(t + 2) & 3] = k_next;
             }
         }
         // completion: the last workgroup out advances the generation
@@ -1090,7 +1179,7 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                 gridDim.x - 1u) {
                 dev_store(&ctrl->done, 0u);
                 vmem_drain();
-                dev_store(&ctrl->gen, target);
+                dev_store(&ctrl->gen_ctl, gen_target);
             }
         }
         return;
@@ -1102,6 +1191,9 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     // memory counter retires in issue order, so with a fixed number of loads
     // per iteration a wave can wait for one tile while the next is in flight.
     // A tile past the last sample reads one fixed address (no traffic).
+    // the wave's index, in a scalar register (it is the same in every lane)
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t n_wave = ctl_wave_elems<F4PT, DW>((uint32_t)p, wave_id, (uint32_t)P, nv);
     uint32_t off0 = (uint32_t)p * RW + (uint32_t)tid;
     const uint32_t stride = (uint32_t)P * RW;
     auto index = [&](int k) -> uint32_t { return off0 + (uint32_t)k * stride; };
@@ -1144,15 +1236,21 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
         // being kept live across the loop (registers hold NT x tiles)
         asm volatile("" : "+v"(off0));
         if (t < outer) {
-            const float K = s_K[t & 3];
+            // two passes over the tile (see WaveMoments; ctl_recompute repeats them)
+            f4 s = f4(0.0f);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) s += valid(k) ? T[u][k] : f4(0.0f);
+            const float m = wave_shift(s, n_wave);
             f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
-            for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? T[u][k] - K : f4(0.0f));
+            for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? T[u][k] - m : f4(0.0f));
             double t1, t2;
             wave_moments(a1, a2, t1, t2);
             if (lane == 0) {
-                red[t & 1][2 * (tid / kWave)] = t1;
-                red[t & 1][2 * (tid / kWave) + 1] = t2;
+                double* rd = red[t & 1] + 3 * wave_id;
+                rd[0] = t1;
+                rd[1] = t2;
+                rd[2] = (double)m;
             }
         }
         __syncthreads();  // barrier t: sample t-LAG's statistics are in LDS
@@ -1386,35 +1484,40 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     const int64_t P = ceil_div(rows, (int64_t)F4PT);
     if (P > P_cap) return false;
     const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * rw * sizeof(f4);
-    if (lds + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
+    // Whether a tile fits is decided as if both weight and bias were given,
+    // so a shape always runs the same tile (the control-wave kernel's
+    // exchange relies on every launch on a workspace writing the same slots).
+    const size_t lds_max = (size_t)2 * F4PT * rw * sizeof(f4);
+    if (lds_max + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
     const void* fn;
     if constexpr (DW == 0)
         fn = reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>);
     else
         fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>);
     const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
-    const int cap = coresident(fn, lds, threads);
+    const int cap = coresident(fn, lds_max, threads);
     if (cap < P) return false;
     int64_t pcap = P_cap;
     if constexpr (DW > 0) {
         // An ordinary launch (a cooperative one costs ~17 us more per call on
         // MI355X).  The grid fits the device, so normally every workgroup is
         // resident at once; when one is not (another kernel holds its CU), the
-        // others compute its sums themselves after a bounded wait, so the
-        // launch completes with the same result either way.  Test knob: force
-        // that path for every k-th workgroup (not in place, where the forced
-        // workgroup may already have overwritten its rows of x).  Workgroup j
-        // is forced iff (j & mask) == mask; all ones forces none (P <= 1024).
-        // A forced workgroup's sums are never accepted, so the wait for them
-        // is cut short (64 polls) in that mode.
-        const uint32_t k = x == y ? 0u : ln_force_recompute();
+        // others compute its moments themselves after a bounded wait, so the
+        // launch completes with the same result either way.  That needs x
+        // intact until the end, so in place (y == x) never comes here.  Test
+        // knob: force that path for every k-th workgroup: workgroup j is
+        // forced (publishes nothing) iff (j & mask) == mask; all ones forces
+        // none (P <= 1024).  The wait for a forced workgroup is cut short (8
+        // polls) in that mode.
+        if (x == y) return false;
+        const uint32_t k = ln_force_recompute();
         const uint32_t force = k ? k - 1u : 0xFFFFFFFFu;
         // as many groups of P workgroups (each taking every groups-th
         // sample) as stay co-resident, at most one per sample
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
         err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)(groups * P)),
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, parts,
-                            mean_out, rstd_out, groups, k ? 64u : kSpinLimit, force);
+                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force);
         return true;
     }
     void* args[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
@@ -1447,9 +1550,11 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
 int ln_auto_variant(const float* x, const float* w, const float* b, const float* y, int64_t outer, int64_t inner)
 {
     (void)outer;
-    if (!ln_single_supported(inner, x, w, b, y)) return 0;
+    // in place the control-wave kernel does not run (a reader may need x
+    // after its owner has overwritten it): the split schedule does
+    if (!ln_single_supported(inner, x, w, b, y) || x == y) return 0;
     const int64_t P = ceil_div(ceil_div(inner / 4, (int64_t)8 * kWave), (int64_t)8);
-    const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * 8 * 8 * kWave * sizeof(f4);
+    const size_t lds = (size_t)2 * 8 * 8 * kWave * sizeof(f4);
     const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG>);
     return coresident(fn, lds, 9 * kWave) >= P ? 1 : 0;
 }
@@ -1467,7 +1572,8 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
 
     // A single-read kernel, when a co-resident grid can hold every sample's
     // rows (tuned tile first, then the others).
-    if (ln_single_supported(inner, x, w, b, y)) {
+    // (in place the control-wave kernel does not run and variant 1 takes the split)
+    if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
 #define NORMFWD_TRY_HOLD(F, DW)                                                                                \
     if (try_launch_hold<F, DW>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, lay.P_cap,      \

@@ -30,7 +30,7 @@ def run_cases():
         rstd = torch.empty(outer, device="cuda")
         y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws, mean_out=mean, rstd_out=rstd)
         if (outer, inner) == CASES[0][:2]:
-            # past the wrap of the 8-bit generation tag: a sum that is never accepted stays so
+            # past the 255-launch cycle of the exchange tags: words that are never accepted stay so
             for _ in range(300):
                 again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, workspace=ws)
                 if not torch.equal(again, y):

@@ -226,8 +226,8 @@ def test_ln_many_short_samples(outer, inner, dist):
     np.testing.assert_allclose(_np(mean), om, rtol=1e-6, atol=1e-6)
     np.testing.assert_allclose(_np(rstd), 1.0 / np.sqrt(ov + np.float32(1e-5)), rtol=1e-5)
     x = d["x"].clone()
-    nf.ln_forward(x, d["weight"], d["bias"], out=x)  # in place
-    assert torch.equal(x, y)
+    nf.ln_forward(x, d["weight"], d["bias"], out=x)  # in place: the split schedule (or the row kernel)
+    assert torch.equal(x, nf.ln_forward(d["x"], d["weight"], d["bias"], variant=0))
 
 
 @pytest.mark.parametrize("name", ["ln_16x64x256x256", "ln_stress_16x64x256x256"])
@@ -288,13 +288,16 @@ def test_ln_single_kernel_repeated_and_split_halves(variant):
     _, ws = nf.alloc_workspace(nbytes, "cuda")
     nf.ln_forward_workspace_init(ws)
     first = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
-    for _ in range(300):  # the generation tag wraps at 256
+    for _ in range(300):  # the control-wave kernel's tags cycle every 255 launches
         again = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, workspace=ws)
         assert torch.equal(first, again)
     torch.cuda.synchronize()
-    ctrl = ws[:16].view(torch.int32).cpu().tolist()  # gen, done, error, recomputed
+    ctrl = ws[:20].view(torch.int32).cpu().tolist()  # gen, done, error, recomputed, gen_ctl
     assert ctrl[1] == 0 and ctrl[2] == 0, ctrl
-    assert ctrl[0] == 301, ctrl
+    if variant == 1:
+        assert ctrl[4] == 301 % 255 and ctrl[0] == 0, ctrl
+    else:
+        assert ctrl[0] == 301 and ctrl[4] == 0, ctrl
     assert ctrl[3] == 0, f"every workgroup was resident, none had its sums recomputed: {ctrl}"
     ws0 = nf.ln_forward_stats(d["x"])
     halves = nf.ln_forward_apply(d["x"], d["weight"], d["bias"], ws0)
@@ -417,8 +420,8 @@ def test_captured_graph_replays_match_eager():
         for o, e, name in zip(outs, (ln_eager, gn_eager, rms_eager, fc_eager, single_eager),
                               ("ln", "gn", "rms", "fc", "ln single-read")):
             assert torch.equal(o, e), f"replay {rep}: {name} differs from eager"
-    ctrl = ws1[:16].view(torch.int32).cpu().tolist()  # gen, done, error, recomputed
-    assert ctrl[0] == 4 and ctrl[1] == 0 and ctrl[3] == 0, ctrl
+    ctrl = ws1[:20].view(torch.int32).cpu().tolist()  # gen, done, error, recomputed, gen_ctl
+    assert ctrl[4] == 4 and ctrl[1] == 0 and ctrl[3] == 0, ctrl
 
 
 def test_modules_match_the_functions():
