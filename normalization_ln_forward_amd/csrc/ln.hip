@@ -724,36 +724,44 @@ struct WaveMoments {
     double t1, t2;  // sums of d and d^2 over the wave's elements
     float m;        // the shift
 };
-__device__ __forceinline__ float wave_shift(const f4 s, uint32_t n)
+// inv_n: 1 / (the wave's element count), or 0 for a wave with none
+__device__ __forceinline__ float wave_shift(const f4 s, float inv_n)
 {
-    const float tot = wave_total((s.x + s.y) + (s.z + s.w));
-    return n ? tot / (float)n : 0.0f;
+    return wave_total((s.x + s.y) + (s.z + s.w)) * inv_n;
 }
+__device__ __forceinline__ float inv_count_f32(uint32_t n) { return n ? 1.0f / (float)n : 0.0f; }
+__device__ __forceinline__ double inv_count_f64(uint32_t n) { return n ? 1.0 / (double)n : 0.0; }
 
 // A workgroup's (mean, M2) from its waves' moments (rd[3w .. 3w+2] = t1,
-// t2, m of wave w; cnt[w] its element count), merged in wave order:
-// mean = sum n_w mean_w / n, M2 = sum (M2_w + n_w (mean_w - mean)^2), the
-// k-way form of the pairwise (Chan) update.  Thread-local arithmetic in a
-// fixed order, so every caller gets the same bits.
+// t2, m of wave w; cnt[w] its element count, inv[w] = inv_count_f64(cnt[w]),
+// inv_n the same of their total), merged around c, wave 0's mean (wave 0
+// always holds elements): lane w < DW forms mean_w = m_w + t1_w / n_w and
+// M2_w = t2_w - t1_w^2 / n_w, then A = sum n_w (mean_w - c) and B = sum
+// (M2_w + n_w (mean_w - c)^2) over the lanes (wave_total, a fixed order), and
+// mean = c + A / n, M2 = B - A^2 / n (the k-way pairwise update; with c a
+// wave mean of the same data the last subtraction loses nothing that
+// matters).  A wave with no elements adds nothing.  Called by a whole wave;
+// the result is uniform, and every call on the same moments gets the same
+// bits.
 template <int DW>
-__device__ __forceinline__ void merge_wave_moments(const double* rd, const uint32_t* cnt, double& mean, double& m2)
+__device__ __forceinline__ void merge_wave_moments(const double* rd, const uint32_t* cnt, const double* inv,
+                                                   double inv_n, double& mean, double& m2)
 {
-    double n = 0.0, sm = 0.0;
-    for (int w = 0; w < DW; ++w) {
-        if (!cnt[w]) continue;
-        const double nw = (double)cnt[w];
-        n += nw;
-        sm += nw * (rd[3 * w + 2] + rd[3 * w] / nw);
+    const int lane = threadIdx.x & (kWave - 1);
+    double mw = 0.0, m2w = 0.0, nw = 0.0;
+    if (lane < DW) {
+        const double t1 = rd[3 * lane], iw = inv[lane];
+        nw = (double)cnt[lane];
+        mw = rd[3 * lane + 2] + t1 * iw;
+        m2w = fmax(rd[3 * lane + 1] - t1 * (t1 * iw), 0.0);
     }
-    mean = n > 0.0 ? sm / n : 0.0;
-    m2 = 0.0;
-    for (int w = 0; w < DW; ++w) {
-        if (!cnt[w]) continue;
-        const double nw = (double)cnt[w];
-        const double t1 = rd[3 * w];
-        const double d = (rd[3 * w + 2] + t1 / nw) - mean;
-        m2 += fmax(rd[3 * w + 1] - t1 * (t1 / nw), 0.0) + nw * (d * d);
-    }
+    const double c = lane_f64(mw, 0);
+    const double d = mw - c;
+    const double A = wave_total(nw * d);
+    const double B = wave_total(m2w + nw * (d * d));
+    const double md = A * inv_n;
+    mean = c + md;
+    m2 = fmax(B - A * md, 0.0);
 }
 
 // Last arriver of sample t in the single kernel: merge its partials, store
@@ -816,6 +824,7 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
     __shared__ double lds[3 * kLnThreads];
     __shared__ double red[3 * (kLnThreads / kWave)];  // [wave]: t1, t2, shift
     __shared__ uint32_t cnt[kLnThreads / kWave];      // [wave]: elements it holds
+    __shared__ double cnt_inv[kLnThreads / kWave];    // [wave]: 1 / cnt
     __shared__ int s_last;
     __shared__ f4 s_stats;
     f4* w_s = reinterpret_cast<f4*>(smem_raw);
@@ -854,7 +863,12 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
     uint32_t n_wave = 0;  // elements this wave holds of each sample
 #pragma unroll
     for (int k = 0; k < F4PT; ++k) n_wave += 4u * (uint32_t)__builtin_popcountll(__ballot(valid(k)));
-    if ((tid & (kWave - 1)) == 0) cnt[wave_id] = n_wave;
+    const float inv_wave = inv_count_f32(n_wave);
+    if ((tid & (kWave - 1)) == 0) {
+        cnt[wave_id] = n_wave;
+        cnt_inv[wave_id] = inv_count_f64(n_wave);
+    }
+    const double inv_mine = inv_count_f64((uint32_t)n_mine);
     __syncthreads();
 
     for (int64_t t = 0; t <= outer; ++t) {
@@ -864,7 +878,7 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
             f4 s = f4(0.0f);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) s += valid(k) ? cur[k] : f4(0.0f);
-            const float m = wave_shift(s, n_wave);
+            const float m = wave_shift(s, inv_wave);
             f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? cur[k] - m : f4(0.0f));
@@ -878,11 +892,11 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
             }
             __syncthreads();
             uint32_t* counter = counters + (t % kRing) * kCounterStride;
-            if (tid == 0) {
+            if (wave_id == 0) {
                 Partial q{};
                 q.n = (double)n_mine;
-                merge_wave_moments<kLnThreads / kWave>(red, cnt, q.mean, q.m2);
-                s_last = deliver_partial(parts + t * P_cap + p, q, counter, P);
+                merge_wave_moments<kLnThreads / kWave>(red, cnt, cnt_inv, inv_mine, q.mean, q.m2);
+                if (tid == 0) s_last = deliver_partial(parts + t * P_cap + p, q, counter, P);
             }
             __syncthreads();
             if (s_last)
@@ -937,7 +951,7 @@ ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* 
 // and DW counts, private to the calling wave.
 template <int F4PT, int DW>
 __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, double* rc, uint32_t* rc_cnt,
-                              double& mean, double& m2)
+                              double* rc_inv, double& mean, double& m2)
 {
     constexpr uint32_t RW = DW * kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -955,7 +969,7 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 #pragma unroll
         for (int k = 0; k < F4PT; ++k) s += ok(k) ? v[k] : f4(0.0f);
         WaveMoments r;
-        r.m = wave_shift(s, n);
+        r.m = wave_shift(s, inv_count_f32(n));
         f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
         for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, ok(k) ? v[k] - r.m : f4(0.0f));
@@ -965,11 +979,10 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
             rc[3 * w + 1] = r.t2;
             rc[3 * w + 2] = (double)r.m;
             rc_cnt[w] = n;
+            rc_inv[w] = inv_count_f64(n);
         }
     }
-    if (lane == 0) merge_wave_moments<DW>(rc, rc_cnt, mean, m2);
-    mean = __shfl(mean, 0);
-    m2 = __shfl(m2, 0);
+    merge_wave_moments<DW>(rc, rc_cnt, rc_inv, inv_count_f64(ctl_wg_elems<F4PT, DW>(j, P, nv)), mean, m2);
 }
 
 // Single-read schedule with a control wave.  DW data waves hold the
@@ -1038,6 +1051,8 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     __shared__ f4 s_stats[2];          // [sample parity]: mean hi, mean lo, rstd
     __shared__ double rc[3 * DW];      // control wave: a recomputed workgroup's wave moments
     __shared__ uint32_t cnt[2][DW];    // control wave: element counts of this workgroup's / a recomputed one's waves
+    __shared__ double cnt_inv[2][DW];  // ... and their reciprocals
+    __shared__ float wg_cnt[1024];     // control wave: element count of every workgroup of a group (P <= 1024)
     f4* w_s = reinterpret_cast<f4*>(smem_raw);
     f4* b_s = w_s + (w ? F4PT * RW : 0);
     // `groups` groups of P workgroups; group gr takes samples gr, gr + groups,
@@ -1070,50 +1085,70 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
         // test knob: a silent workgroup does not publish at all, so every
         // reader (itself included) computes its moments from x
         const bool silent = ((uint32_t)p & silent_mask) == silent_mask;
-        if (lane < DW) cnt[0][lane] = ctl_wave_elems<F4PT, DW>((uint32_t)p, lane, (uint32_t)P, nv);
+        if (lane < DW) {
+            const uint32_t n = ctl_wave_elems<F4PT, DW>((uint32_t)p, lane, (uint32_t)P, nv);
+            cnt[0][lane] = n;
+            cnt_inv[0][lane] = inv_count_f64(n);
+        }
+        for (int64_t j = lane; j < P; j += kWave) wg_cnt[j] = (float)ctl_wg_elems<F4PT, DW>((uint32_t)j, (uint32_t)P, nv);
+        const double inv_mine = inv_count_f64(ctl_wg_elems<F4PT, DW>((uint32_t)p, (uint32_t)P, nv));
+        const double inv_N = 1.0 / (double)inner;
         __syncthreads();  // prologue: w/b in LDS
         for (int64_t t = 0; t < steps; ++t) {
             __syncthreads();  // barrier t: the wave moments of sample t are in LDS
-            if (t < outer && lane == 0 && !silent) {
+            const int64_t g = t - (LAG - 1);  // the sample gathered now, normalized after barrier g + LAG
+            const bool gather = g >= 0 && g < outer;
+            // gather every workgroup's words for sample g (lane l: workgroups
+            // l, l + 64, ...), retrying until every tag is current.  The first
+            // loads are issued before this workgroup merges and publishes its
+            // own moments of sample t, so that work overlaps their latency.
+            const Partial* pb = parts + (gather ? g : 0) * pstride;
+            double a[4], b2[4];
+            auto load_block = [&](int64_t j0) __attribute__((always_inline)) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t j = j0 + lane + (int64_t)u * kWave;
+                    const double* q = reinterpret_cast<const double*>(pb + (j < P ? j : p));
+                    a[u] = dev_load(q);
+                    b2[u] = dev_load(q + 1);
+                }
+            };
+            auto block_ok = [&]() __attribute__((always_inline)) {
+                bool ok = true;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) ok = ok && ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag);
+                return __all(ok);
+            };
+            if (gather) load_block(0);
+            if (t < outer) {
                 // this workgroup's (mean, M2) over its elements of sample t
                 double mean, m2;
-                merge_wave_moments<DW>(red[t & 1], cnt[0], mean, m2);
-                double* q = reinterpret_cast<double*>(parts + t * pstride + p);
-                dev_store(q, ln_tag_word(mean, tag));
-                dev_store(q + 1, ln_tag_word(m2, tag));
+                merge_wave_moments<DW>(red[t & 1], cnt[0], cnt_inv[0], inv_mine, mean, m2);
+                if (lane == 0 && !silent) {
+                    double* q = reinterpret_cast<double*>(parts + t * pstride + p);
+                    dev_store(q, ln_tag_word(mean, tag));
+                    dev_store(q + 1, ln_tag_word(m2, tag));
+                }
             }
-            const int64_t g = t - (LAG - 1);  // the sample gathered now, normalized after barrier g + LAG
-            if (g < 0 || g >= outer) continue;
-            // gather every workgroup's words (lane l: workgroups l, l + 64,
-            // ...), retrying until every tag is current.  Words that have not
-            // arrived after `limit` polls (their workgroup is not resident:
-            // an ordinary launch does not promise that every workgroup runs
-            // at once) are computed here from x, with the same bits, and
-            // published in the owner's slot for the other readers (the owner,
-            // once it runs, stores the same bits there).  x of sample g is
-            // still intact: the kernel does not run in place.
-            const Partial* pb = parts + g * pstride;
+            if (!gather) continue;
+            // Words that have not arrived after `limit` polls (their workgroup
+            // is not resident: an ordinary launch does not promise that every
+            // workgroup runs at once) are computed here from x, with the same
+            // bits, and published in the owner's slot for the other readers
+            // (the owner, once it runs, stores the same bits there).  x of
+            // sample g is still intact: the kernel does not run in place.
             double c = 0.0, A = 0.0, B = 0.0;  // shift, sum n_j (mean_j - c), sum M2_j + n_j (mean_j - c)^2
             for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
-                double a[4], b2[4];
+                if (j0 > 0) load_block(j0);
                 uint32_t spins = 0;
                 bool late = false;
-                for (;;) {
-                    bool ok = true;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int64_t j = j0 + lane + (int64_t)u * kWave;
-                        const double* q = reinterpret_cast<const double*>(pb + (j < P ? j : p));
-                        a[u] = dev_load(q);
-                        b2[u] = dev_load(q + 1);
-                        ok = ok && ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag);
-                    }
-                    if (__all(ok)) break;
+                while (!block_ok()) {
                     __builtin_amdgcn_s_sleep(2);
                     if (++spins > limit) {
                         late = true;
                         break;
                     }
+                    load_block(j0);
                 }
                 if (late) {
                     // from now on this workgroup waits only briefly
@@ -1129,7 +1164,7 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                             todo &= todo - 1;
                             const uint32_t jj = (uint32_t)(j0 + l + u * kWave);
                             double mean, m2;
-                            ctl_recompute<F4PT, DW>(xg, jj, (uint32_t)P, nv, rc, cnt[1], mean, m2);
+                            ctl_recompute<F4PT, DW>(xg, jj, (uint32_t)P, nv, rc, cnt[1], cnt_inv[1], mean, m2);
                             const double tm = ln_tag_word(mean, tag), tv = ln_tag_word(m2, tag);
                             if (lane == l) {
                                 a[u] = tm;
@@ -1146,24 +1181,23 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                     if (lane == 0)
                         __hip_atomic_fetch_add(&ctrl->recomputed, n_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (j0 == 0) c = ln_untag(__shfl(a[0], 0));  // workgroup 0's mean
+                if (j0 == 0) c = ln_untag(lane_f64(a[0], 0));  // workgroup 0's mean
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int64_t j = j0 + lane + (int64_t)u * kWave;
                     if (j < P) {
-                        const double nj = (double)ctl_wg_elems<F4PT, DW>((uint32_t)j, (uint32_t)P, nv);
+                        const double nj = (double)wg_cnt[j];
                         const double d = ln_untag(a[u]) - c;
                         A += nj * d;
                         B += ln_untag(b2[u]) + nj * (d * d);
                     }
                 }
             }
-            A = wave_sum(A);
-            B = wave_sum(B);
+            A = wave_total(A);
+            B = wave_total(B);
             if (lane == 0) {
-                const double N = (double)inner;
-                const double md = A / N;
-                const f4 st = finish_stats(N, c + md, fmax(B - A * md, 0.0), eps);
+                const double md = A * inv_N;
+                const f4 st = finish_stats((double)inner, c + md, fmax(B - A * md, 0.0), eps);
                 s_stats[g & 1] = st;
                 if (p == 0) {
                     stats[g * groups] = st;
@@ -1193,7 +1227,7 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     // A tile past the last sample reads one fixed address (no traffic).
     // the wave's index, in a scalar register (it is the same in every lane)
     const int wave_id = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const uint32_t n_wave = ctl_wave_elems<F4PT, DW>((uint32_t)p, wave_id, (uint32_t)P, nv);
+    const float inv_wave = inv_count_f32(ctl_wave_elems<F4PT, DW>((uint32_t)p, wave_id, (uint32_t)P, nv));
     uint32_t off0 = (uint32_t)p * RW + (uint32_t)tid;
     const uint32_t stride = (uint32_t)P * RW;
     auto index = [&](int k) -> uint32_t { return off0 + (uint32_t)k * stride; };
@@ -1240,7 +1274,7 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
             f4 s = f4(0.0f);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) s += valid(k) ? T[u][k] : f4(0.0f);
-            const float m = wave_shift(s, n_wave);
+            const float m = wave_shift(s, inv_wave);
             f4 a1 = f4(0.0f), a2 = f4(0.0f);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? T[u][k] - m : f4(0.0f));
