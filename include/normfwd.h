@@ -18,7 +18,9 @@
  *     taken when pointers are 16-byte aligned and the contiguous extent is a
  *     multiple of 4; otherwise a scalar path computes the same result.
  *   - In place (y == x) is allowed: every element is read before the same
- *     lane writes it.  Partial overlap of inputs and outputs is undefined.
+ *     lane writes it (LayerNorm in place runs the split schedule under
+ *     variants 1 and 3).  Partial overlap of inputs and outputs is
+ *     undefined.
  *   - Results are run-to-run bitwise deterministic: no floating-point
  *     atomics, every reduction has a fixed order.
  *   - Size limits (beyond them NORMFWD_ERR_UNSUPPORTED): at most 2^40
@@ -121,15 +123,16 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 sample through generation-tagged words (no atomics) while
  *                 the data waves stream the next samples.  It is an
  *                 ordinary launch: if a workgroup is not resident (another
- *                 kernel holds its CU), the others stop waiting for its
- *                 moments after a bounded number of polls and compute them
- *                 from x themselves, bit for bit the same, so the result
- *                 never depends on residency (a forced-recompute GPU test
- *                 checks that bitwise).  The grid takes one workgroup per
- *                 CU, so two such launches running at once on different
- *                 streams each finish correctly but slowly (their waits
- *                 run out first, a fraction of a second); order them on
- *                 one stream or with an event;
+ *                 kernel holds its CU), the others wait for its moments
+ *                 for at most 256 polls (~0.3-0.5 ms, which absorbs a
+ *                 kernel running alongside on another stream), then compute
+ *                 them from x themselves, bit for bit the same, and publish
+ *                 them for the other readers; later waits of that launch
+ *                 last at most 32 polls.  The result never depends on
+ *                 residency (GPU tests check it bitwise, with workgroups
+ *                 forced silent and beside other kernels on other
+ *                 streams).  Since readers need x intact until the end, in
+ *                 place (y == x) this variant runs the split schedule;
  *             2 = single kernel in which the last workgroup to deliver a
  *                 sample's partial merges it and announces the statistics
  *                 with a flag (LN page, turn 6: last-block-done), the others
@@ -137,19 +140,21 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 waits need every workgroup resident.
  *             3 = automatic: variant 1 wherever it can run (it measured
  *                 faster than the split, or within 1 us of it on calls of
- *                 ~10 us, at every shape tried), otherwise variant 0.  The
- *                 choice depends only on the shape, the pointers' alignment
- *                 and the device, so it is the same on every call.
+ *                 ~10 us, at every shape tried), otherwise variant 0 (also
+ *                 in place).  The choice depends only on the shape, the
+ *                 pointers (alignment, y == x) and the device, so it is the
+ *                 same on every call with the same tensors.
  *             Shapes a single kernel cannot hold (inner % 4 != 0, unaligned
  *             pointers, more rows than co-resident workgroups can keep) run
  *             the split schedule instead.
  *
- * Statistics are exact to about 1e-7 relative even when |mean| >> std: the
- * partial moments are accumulated around a per-sample shift (the sample's
- * first element), handed between workgroups in fp64, merged in a fixed
- * order (Chan's pairwise update; variant 1 adds the workgroups' shifted
- * sums, the same merge when every part has the same shift), and the mean is
- * applied as an fp32 hi + lo pair.
+ * Statistics are exact to about 1e-7 relative even when |mean| >> std and
+ * whatever the values of particular elements: every sum of squares is taken
+ * around a shift that lies inside the data it sums (a wave's own mean in
+ * the single-kernel variants, a thread's own first value in the split's
+ * moments pass), partial moments travel in fp64 and are merged in a fixed
+ * order (Chan's pairwise update), and the mean is applied as an fp32 hi +
+ * lo pair.
  * ---------------------------------------------------------------------- */
 size_t ln_forward_workspace_size(int64_t outer, int64_t inner);
 

@@ -10,17 +10,26 @@
 // normalizes).
 //
 // Numerics (the page's own one-pass E[x^2] - mean^2 loses everything when
-// |mean| >> std, e.g. N(100, 0.01) data):
-//   * lanes accumulate d = x - K, with K the sample's first element, in fp32
-//     (for data clustered around K the subtraction is exact), one sum and
-//     one sum of squares per float4 component;
-//   * lane sums are widened to fp64 and reduced over the workgroup in a fixed
-//     order; a workgroup's moments (n, mean, M2) are stored in fp64;
-//   * the workgroups' moments are merged with Chan's pairwise update (LN
-//     page, turn 2 derives the same merge for Welford partials) in
-//     workgroup order;
+// |mean| >> std, e.g. N(100, 0.01) data, and a sum of squares around a shift
+// that is not typical of the data loses as much; LN page, turn 2 asks for
+// per-thread moments merged pairwise for this reason):
+//   * every sum of squares is taken around a shift that lies inside the data
+//     it sums: in the single-read kernels each wave first takes its mean in
+//     fp32 (a wave sum of its registers) and then sums d = x - mean_w and d^2
+//     (a true two-pass over registers); in the split moments pass every
+//     float4 component of a thread shifts by the first value it reads (a
+//     member of the very set it sums); the one-workgroup-per-sample kernel
+//     takes two passes and corrects the mean with the second pass's sum;
+//   * lane sums are widened to fp64 and reduced in a fixed order; moments
+//     (n, mean, M2) travel in fp64;
+//   * moments of different parts are merged with the pairwise (Chan) update,
+//     in its k-way form around one part's mean, in a fixed order (LN page,
+//     turn 2 derives the same merge for Welford partials);
 //   * the mean is handed to the normalize pass as an fp32 pair hi + lo, so
 //     (x - hi) - lo keeps ~48 bits of the mean.
+// No statistic depends on which element a kernel reads first: tests plant
+// outliers at the first element of the sample, of workgroups' and of waves'
+// shares.
 //
 // Schedules of the same arithmetic:
 //   split (variant 0): ln_partial_kernel (-> ln_merge_kernel from 1024
@@ -34,16 +43,17 @@
 //          pass to the normalize pass, so x is read once, and the
 //          workgroups exchange each sample's moments in the middle:
 //          ln_single_ctl_kernel (variant 1, an ordinary launch): a control
-//          wave per workgroup publishes generation-tagged sums and gathers
-//          everyone's, while the data waves stream the next samples; sums
-//          that do not arrive within a bounded wait (their workgroup is not
-//          resident) are computed by the reader from x, with the same bits;
+//          wave per workgroup publishes generation-tagged moments and
+//          gathers everyone's, while the data waves stream the next samples;
+//          moments that do not arrive within a bounded wait (their workgroup
+//          is not resident) are computed by the reader from x, with the same
+//          bits (so it never runs in place: y == x takes the split);
 //          ln_single_hold_kernel (variant 2, a cooperative launch): the
 //          last workgroup to deliver a sample's partial merges it and
 //          announces the statistics with a flag (LN page, turn 6:
 //          last-block-done).
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
-//          shape, from measurements.
+//          shape, from measurements (the split in place).
 //   short samples (inner <= 8192): ln_row_kernel, one workgroup per sample.
 // Cross-workgroup data is only ever accessed with device-coherent atomic
 // loads and stores (see the protocol notes below), never with fences.
@@ -954,32 +964,46 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
                               double* rc_inv, double& mean, double& m2)
 {
     constexpr uint32_t RW = DW * kWave;
+    static_assert(DW % 2 == 0, "two data waves per batch");
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t stride = P * RW;
+    // two data waves' elements per batch: twice the loads in flight per round
+    // trip, at 2 F4PT float4 registers per lane
 #pragma unroll 1
-    for (int w = 0; w < DW; ++w) {
-        const uint32_t off0 = j * RW + (uint32_t)(w * kWave + lane);
-        auto ok = [&](int k) { return (int64_t)(off0 + (uint32_t)k * stride) < nv; };
-        f4 v[F4PT];
+    for (int w0 = 0; w0 < DW; w0 += 2) {
+        f4 v[2][F4PT];
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) v[k] = ok(k) ? ld_nt(xs + off0 + (uint32_t)k * stride) : f4(0.0f);
-        const uint32_t n = ctl_wave_elems<F4PT, DW>(j, w, P, nv);
-        // the data waves' two passes (see WaveMoments)
-        f4 s = f4(0.0f);
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t off0 = j * RW + (uint32_t)((w0 + h) * kWave + lane);
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) s += ok(k) ? v[k] : f4(0.0f);
-        WaveMoments r;
-        r.m = wave_shift(s, inv_count_f32(n));
-        f4 a1 = f4(0.0f), a2 = f4(0.0f);
+            for (int k = 0; k < F4PT; ++k) {
+                const uint32_t idx = off0 + (uint32_t)k * stride;
+                v[h][k] = (int64_t)idx < nv ? ld_nt(xs + idx) : f4(0.0f);
+            }
+        }
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, ok(k) ? v[k] - r.m : f4(0.0f));
-        wave_moments(a1, a2, r.t1, r.t2);
-        if (lane == 0) {
-            rc[3 * w] = r.t1;
-            rc[3 * w + 1] = r.t2;
-            rc[3 * w + 2] = (double)r.m;
-            rc_cnt[w] = n;
-            rc_inv[w] = inv_count_f64(n);
+        for (int h = 0; h < 2; ++h) {
+            const int w = w0 + h;
+            const uint32_t off0 = j * RW + (uint32_t)(w * kWave + lane);
+            auto ok = [&](int k) { return (int64_t)(off0 + (uint32_t)k * stride) < nv; };
+            const uint32_t n = ctl_wave_elems<F4PT, DW>(j, w, P, nv);
+            // the data waves' two passes (see WaveMoments)
+            f4 s = f4(0.0f);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) s += ok(k) ? v[h][k] : f4(0.0f);
+            WaveMoments r;
+            r.m = wave_shift(s, inv_count_f32(n));
+            f4 a1 = f4(0.0f), a2 = f4(0.0f);
+#pragma unroll
+            for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, ok(k) ? v[h][k] - r.m : f4(0.0f));
+            wave_moments(a1, a2, r.t1, r.t2);
+            if (lane == 0) {
+                rc[3 * w] = r.t1;
+                rc[3 * w + 1] = r.t2;
+                rc[3 * w + 2] = (double)r.m;
+                rc_cnt[w] = n;
+                rc_inv[w] = inv_count_f64(n);
+            }
         }
     }
     merge_wave_moments<DW>(rc, rc_cnt, rc_inv, inv_count_f64(ctl_wg_elems<F4PT, DW>(j, P, nv)), mean, m2);
