@@ -263,6 +263,25 @@ normfwd_status fc_gn_forward(const float* x, const float* W, const float* b,
                              float negative_slope, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement references (not normalization operations): plain copies with
+ * the access patterns of the kernels above, so that each kernel's HBM rate
+ * can be set beside what a copy of the same bytes reaches on the same
+ * device in the same run.
+ *
+ *   pattern 0   dense streaming copy of B * C * S floats (one 128-bit load
+ *               and nontemporal store per thread, consecutive workgroups on
+ *               consecutive addresses)
+ *   pattern 1   rmsnorm_ch_forward's access pattern on [B, C, S] (the same
+ *               grid, workgroup order, loads and stores), dst = src
+ *   src, dst    device buffers of B * C * S floats, 16-byte aligned, not
+ *               overlapping
+ * Other shapes than those the patterns cover (a multiple of 4 floats;
+ * pattern 1: S % 4 == 0, C <= 64, S <= 2^26) return NORMFWD_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+normfwd_status normfwd_copy_reference(const float* src, float* dst, int64_t B, int64_t C, int64_t S,
+                                      int pattern, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ the kernels replace.
 from ._lib import (  # noqa: F401
     NormFwdError,
     alloc_workspace,
+    copy_reference,
     fc_gn_forward,
     gn_lrelu_x2_forward,
     lib,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     ln_forward_workspace_init,
     ln_forward_workspace_size,
     prepare,
+    release_cached_workspaces,
     rmsnorm_ch_forward,
     time_next_kernel,
 )

@@ -42,6 +42,7 @@ SIGNATURES = {
     "ln_forward_apply": (_ST, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "gn_lrelu_x2_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _F, _F, _P]),
     "rmsnorm_ch_forward": (_ST, [_P, _P, _I64, _I64, _I64, _F, _P]),
+    "normfwd_copy_reference": (_ST, [_P, _P, _I64, _I64, _I64, ctypes.c_int, _P]),
     "fc_gn_forward_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "fc_gn_forward": (_ST, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P, _SZ, _P]),
 }
@@ -170,6 +171,14 @@ def alloc_workspace(nbytes, device):
 # ---------------------------------------------------------------- LayerNorm
 
 _LN_WS = {}
+
+
+def release_cached_workspaces():
+    """Drop the workspaces the binding keeps per shape (LayerNorm) and per device (fc + GroupNorm).  For an
+    orderly end of a process that used them: call it once the device is idle (prepared calls that captured
+    a released workspace must not run afterwards; later ordinary calls allocate new ones)."""
+    _LN_WS.clear()
+    _FC_WS.clear()
 
 
 def ln_forward_workspace_size(outer, inner):
@@ -354,3 +363,23 @@ def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.0
                                int(num_groups), float(eps), float(negative_slope), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(dev))
     return y
+
+
+# ---------------------------------------------------------------- measurement references
+
+def copy_reference(src, out, pattern=0):
+    """A plain copy src -> out with one of the library's access patterns (normfwd_copy_reference):
+    0 = dense streaming copy, 1 = rmsnorm_ch_forward's pattern on src viewed as [B, C, *spatial]."""
+    _need(src, "src")
+    _need(out, "out", src.device)
+    if out.shape != src.shape:
+        raise ValueError("out must have src's shape")
+    if pattern == 1:
+        if src.dim() < 2:
+            raise ValueError("pattern 1 needs [B, C, *spatial]")
+        B, C = src.shape[0], src.shape[1]
+        S = src.numel() // (B * C)
+    else:
+        B, C, S = 1, 1, src.numel()
+    _invoke("normfwd_copy_reference", _ptr(src), _ptr(out), B, C, S, int(pattern), _stream(src.device))
+    return out

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libnormfwd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "ln.hip", "gn.hip", "rms.hip", "fc.hip"]
+SOURCES = ["api.hip", "ln.hip", "gn.hip", "rms.hip", "fc.hip", "ref.hip"]
 
 
 def hipcc() -> str:

@@ -330,6 +330,25 @@ normfwd_status rmsnorm_ch_forward(const float* x, float* y, int64_t B, int64_t C
     return hip_status(normfwd::launch_rms_ch(x, y, B, C, S, eps, (hipStream_t)stream), "rmsnorm_ch_forward launch");
 }
 
+normfwd_status normfwd_copy_reference(const float* src, float* dst, int64_t B, int64_t C, int64_t S, int pattern,
+                                      void* stream)
+{
+    if (!src || !dst) return fail(NORMFWD_ERR_INVALID, "normfwd_copy_reference: src and dst must not be NULL");
+    if (B <= 0 || C <= 0 || S <= 0 || B > kMaxElems / C || B * C > kMaxElems / S)
+        return fail(NORMFWD_ERR_INVALID, "normfwd_copy_reference: B, C, S must be > 0 (at most 2^40 elements)");
+    if (pattern != 0 && pattern != 1) return fail(NORMFWD_ERR_INVALID, "normfwd_copy_reference: pattern must be 0 or 1");
+    const bool al = !(reinterpret_cast<uintptr_t>(src) & 15) && !(reinterpret_cast<uintptr_t>(dst) & 15);
+    if (!al || (pattern == 0 && (B * C * S) % 4 != 0) || (pattern == 1 && (S % 4 != 0 || C > 64 || S > ((int64_t)1 << 26))))
+        return fail(NORMFWD_ERR_UNSUPPORTED,
+                    "normfwd_copy_reference: needs 16-byte aligned buffers and a multiple of 4 floats (pattern 1: "
+                    "S %% 4 == 0, C <= 64, S <= 2^26)");
+    (void)hipGetLastError();
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(pattern == 0 ? normfwd::launch_copy_dense(src, dst, B * C * S, st)
+                                   : normfwd::launch_rms_copy_pattern(src, dst, B, C, S, st),
+                      "normfwd_copy_reference launch");
+}
+
 size_t fc_gn_forward_workspace_size(int64_t N, int64_t K, int64_t C)
 {
     (void)K;

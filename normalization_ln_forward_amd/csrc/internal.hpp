@@ -105,6 +105,11 @@ int ln_auto_variant(const float* x, const float* w, const float* b, const float*
 // can sit inside a captured HIP graph).
 hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t st);
 
+// Measurement references (plain copies): a dense streaming copy of n
+// floats, and rmsnorm_ch_forward's access pattern without its arithmetic.
+hipError_t launch_copy_dense(const float* src, float* dst, int64_t n, hipStream_t st);
+hipError_t launch_rms_copy_pattern(const float* x, float* y, int64_t B, int64_t C, int64_t S, hipStream_t st);
+
 hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
                         float* y, int64_t N, int64_t K, int64_t C, int64_t G, float eps, float slope, void* ws,
                         hipStream_t st);

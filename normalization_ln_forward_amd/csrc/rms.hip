@@ -57,9 +57,12 @@ struct VecOf<1> { using T = float; };
 // the compiler's VGPR limit (512 / waves-per-SIMD) above that.
 constexpr int hold_max_threads(int vecs) { return vecs <= 16 ? 1024 : vecs <= 32 ? 512 : 256; }
 
-template <int CPW, int PPL, int VEC>
-__global__ void __launch_bounds__(hold_max_threads(CPW * PPL))
-rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+// The register-held kernel's body.  NORM = false: the same loads, stores,
+// grid and workgroup order with the arithmetic left out (y = x), a
+// measurement reference for what this access pattern costs by itself
+// (rms_copy_pattern_kernel).
+template <int CPW, int PPL, int VEC, bool NORM>
+__device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
 {
     using V = typename VecOf<VEC>::T;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -101,20 +104,27 @@ rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, fl
             }
     }
     V acc[PPL];
+    if constexpr (NORM) {
 #pragma unroll
-    for (int j = 0; j < PPL; ++j) {
-        acc[j] = V(0.0f);
+        for (int j = 0; j < PPL; ++j) {
+            acc[j] = V(0.0f);
 #pragma unroll
-        for (int k = 0; k < CPW; ++k) acc[j] += v[k][j] * v[k][j];
-        part[(wave * PPL + j) * kWave + lane] = acc[j];
+            for (int k = 0; k < CPW; ++k) acc[j] += v[k][j] * v[k][j];
+            part[(wave * PPL + j) * kWave + lane] = acc[j];
+        }
+        __syncthreads();
     }
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
-        V tot = part[j * kWave + lane];
-        for (int w = 1; w < nwaves; ++w) tot += part[(w * PPL + j) * kWave + lane];
+        V tot = V(0.0f);
+        if constexpr (NORM) {
+            tot = part[j * kWave + lane];
+            for (int w = 1; w < nwaves; ++w) tot += part[(w * PPL + j) * kWave + lane];
+        }
         V inv;
-        if constexpr (VEC == 4) {
+        if constexpr (!NORM) {
+            inv = V(1.0f);
+        } else if constexpr (VEC == 4) {
             inv.x = 1.0f / sqrtf(tot.x / (float)C + eps);
             inv.y = 1.0f / sqrtf(tot.y / (float)C + eps);
             inv.z = 1.0f / sqrtf(tot.z / (float)C + eps);
@@ -127,13 +137,28 @@ rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, fl
         for (int k = 0; k < CPW; ++k) {
             if (okj && (interior || c0 + k < C)) {
                 V* dst = reinterpret_cast<V*>(y + base + (int64_t)k * S + j * kWave * VEC);
+                const V o = NORM ? v[k][j] * inv : v[k][j];
                 if (NORMFWD_RMS_NT_STORE)
-                    st_nt(v[k][j] * inv, dst);
+                    st_nt(o, dst);
                 else
-                    *dst = v[k][j] * inv;
+                    *dst = o;
             }
         }
     }
+}
+
+template <int CPW, int PPL, int VEC>
+__global__ void __launch_bounds__(hold_max_threads(CPW * PPL))
+rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+{
+    rms_hold_body<CPW, PPL, VEC, true>(x, y, C, S, tiles, eps);
+}
+
+template <int CPW, int PPL, int VEC>
+__global__ void __launch_bounds__(hold_max_threads(CPW * PPL))
+rms_copy_pattern_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+{
+    rms_hold_body<CPW, PPL, VEC, false>(x, y, C, S, tiles, eps);
 }
 
 // Streaming variant for large C: 4 waves split the channels; pass 1 sums
@@ -184,7 +209,7 @@ rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, 
 
 // Larger tensors are launched in batches of whole samples (samples_per_launch).
 
-template <int CPW, int PPL, int VEC>
+template <int CPW, int PPL, int VEC, bool NORM = true>
 static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
                               hipStream_t st)
 {
@@ -195,8 +220,11 @@ static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, in
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
         const int64_t off = b0 * C * S;
-        const hipError_t e = launch_kernel((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
-                                           dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
+        const hipError_t e =
+            NORM ? launch_kernel((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
+                                 dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps)
+                 : launch_kernel((rms_copy_pattern_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
+                                 dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -237,6 +265,18 @@ hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t
     const bool vec4 = (S % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
                       ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
     return vec4 ? launch_vec<4>(x, y, B, C, S, eps, st) : launch_vec<1>(x, y, B, C, S, eps, st);
+}
+
+// Measurement reference: rmsnorm_ch_forward's access pattern on [B, C, S]
+// (the tuned register-held kernel: same grid, order, loads and stores) as a
+// plain copy.  Needs 16-byte aligned tensors, S % 4 == 0 and C <= 64.
+hipError_t launch_rms_copy_pattern(const float* x, float* y, int64_t B, int64_t C, int64_t S, hipStream_t st)
+{
+    constexpr int cpw = NORMFWD_RMS_CPW, ppl = NORMFWD_RMS_PPL;
+    if (S % 4 != 0 || (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 15) ||
+        ceil_div(C, cpw) * kWave > hold_max_threads(cpw * ppl))
+        return hipErrorInvalidValue;
+    return launch_hold<cpw, ppl, 4, false>(x, y, B, C, S, 0.0f, st);
 }
 
 }  // namespace normfwd

@@ -38,6 +38,8 @@ KERNEL_SOURCES = {
     "rms_ch_hold_kernel": ["rms.hip", "common.hpp"],
     "fc_mfma_kernel": ["fc.hip", "common.hpp"],
     "fc_dma_kernel": ["fc.hip", "common.hpp"],
+    "copy_dense_kernel": ["ref.hip", "common.hpp"],
+    "rms_copy_pattern_kernel": ["rms.hip", "common.hpp"],
 }
 
 

@@ -62,13 +62,16 @@ class Oracle:
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
-    def ln(self, x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, return_stats=False):
+    def ln(self, x, weight=None, bias=None, eps=1e-5, normalized_ndim=None, return_stats=False, out=None):
         """LayerNorm over the trailing dims of each sample (LN page, turn 1).
 
         ``x`` has shape ``[outer, *normalized_shape]``; by default every dim
         but the first is normalized (the LN page normalizes (C, H, W) of
         NCHW).  ``weight``/``bias`` have ``normalized_shape`` or are None.
         Returns y (float64, x's shape) and optionally (mean[outer], var[outer]).
+        Inputs that already are C-contiguous float64 arrays are used as they
+        are (no copy), and ``out`` (a C-contiguous float64 array of x's shape)
+        receives y if given, so a caller can time the computation alone.
         """
         xd = _f64(x)
         nd = xd.ndim - 1 if normalized_ndim is None else normalized_ndim
@@ -79,7 +82,11 @@ class Oracle:
             assert w.size == inner
         if b is not None:
             assert b.size == inner
-        y = np.empty_like(xd)
+        if out is not None:
+            assert out.dtype == np.float64 and out.shape == xd.shape and out.flags.c_contiguous
+            y = out
+        else:
+            y = np.empty_like(xd)
         mean = np.empty(outer, np.float64)
         var = np.empty(outer, np.float64)
         self.lib.oracle_ln(_ptr(xd), _ptr(w), _ptr(b), outer, inner, as_f32_scalar(eps),
