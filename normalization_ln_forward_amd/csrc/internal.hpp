@@ -64,6 +64,7 @@ struct LnLayout {
     size_t off_split_counter;  // split schedule: per-sample arrival counters (128-byte lines)
     size_t off_stats;
     size_t off_part;
+    size_t off_xchg;  // control-wave kernel's exchange: per sample, P_cap tagged means then P_cap tagged M2s
     size_t total;
 };
 // Byte offset, in an LN workspace, of the word the single kernels set when

@@ -150,6 +150,16 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 #define NORMFWD_LN_CTL_LAG 2
 #endif
 
+// Doubles per workgroup in the control-wave kernel's exchange region (0:
+// all means of a sample, then all M2s).  Measured on MI355X at [16, 4M]
+// (kernel duration, one call, three alternations): 4 (32 bytes, the mean
+// and M2 words then padding) 99.1-99.5 us, 8 99.2-99.6, 16 101.4-101.8, 0
+// 101.6-102.2: packing many workgroups' words into one line (fewer poll
+// requests) or giving each its own 128-byte line is slower.
+#ifndef NORMFWD_LN_XCHG_SLOT
+#define NORMFWD_LN_XCHG_SLOT 4
+#endif
+
 #ifndef NORMFWD_LN_FUSE_BELOW
 #define NORMFWD_LN_FUSE_BELOW 1024
 #endif
@@ -179,6 +189,8 @@ LnLayout ln_layout(int64_t outer, int64_t inner)
     off += align256(16 * (size_t)outer);
     L.off_part = off;
     off += align256(sizeof(Partial) * (size_t)outer * (size_t)L.P_cap);
+    L.off_xchg = off;
+    off += align256((NORMFWD_LN_XCHG_SLOT ? NORMFWD_LN_XCHG_SLOT : 2) * sizeof(double) * (size_t)outer * (size_t)L.P_cap);
     L.total = off;
     return L;
 }
@@ -1065,7 +1077,7 @@ __device__ __forceinline__ bool ctl_steps(int64_t t0, int64_t steps, F& f)
 template <int F4PT, int DW, int LAG>
 __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, float* y_all, int64_t outer_all,
-                     int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, Partial* parts_all,
+                     int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, double* xchg_all,
                      float* mean_all, float* rstd_all, int64_t groups, uint32_t spin_limit, uint32_t silent_mask)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
@@ -1082,16 +1094,22 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     // `groups` groups of P workgroups; group gr takes samples gr, gr + groups,
     // ... as its own sequence (local sample i is sample gr + i * groups), so
     // a grid of groups x P workgroups fills the GPU when one sample spreads
-    // over fewer.  Below, x, y, parts, stats, mean_out, rstd_out and outer
+    // over fewer.  Below, x, y, xchg, stats, mean_out, rstd_out and outer
     // are the group's view: local sample i at x + i * sstride, and so on.
+    // Workgroup j's exchange words for a sample are its tagged mean and M2,
+    // at the start of its slot of XS doubles.
     const int64_t P = gridDim.x / groups;
     const int64_t gr = blockIdx.x / P;
     const int64_t p = blockIdx.x - gr * P;
-    const int64_t sstride = groups * inner;   // elements between the group's samples
-    const int64_t pstride = groups * P_cap;   // partial slots between the group's samples
+    const int64_t sstride = groups * inner;       // elements between the group's samples
+    constexpr int64_t XS = NORMFWD_LN_XCHG_SLOT;  // doubles per workgroup slot (0: all means, then all M2s)
+    const int64_t sw = XS ? XS * P_cap : 2 * P_cap;  // exchange words per sample
+    const int64_t xstride = groups * sw;          // exchange words between the group's samples
+    const int64_t xm2 = XS ? 1 : P_cap;           // M2 word relative to the mean word
+    const int64_t xj = XS ? XS : 1;               // words between workgroups
     const float* x = x_all + gr * inner;
     float* y = y_all + gr * inner;
-    Partial* parts = parts_all + gr * P_cap;
+    double* xchg = xchg_all + gr * sw;
     f4* stats = stats_all + gr;
     float* mean_out = mean_all ? mean_all + gr : nullptr;
     float* rstd_out = rstd_all ? rstd_all + gr : nullptr;
@@ -1126,15 +1144,15 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
             // l, l + 64, ...), retrying until every tag is current.  The first
             // loads are issued before this workgroup merges and publishes its
             // own moments of sample t, so that work overlaps their latency.
-            const Partial* pb = parts + (gather ? g : 0) * pstride;
+            const double* xb = xchg + (gather ? g : 0) * xstride;
             double a[4], b2[4];
             auto load_block = [&](int64_t j0) __attribute__((always_inline)) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int64_t j = j0 + lane + (int64_t)u * kWave;
-                    const double* q = reinterpret_cast<const double*>(pb + (j < P ? j : p));
-                    a[u] = dev_load(q);
-                    b2[u] = dev_load(q + 1);
+                    const int64_t jj = j < P ? j : p;
+                    a[u] = dev_load(xb + jj * xj);
+                    b2[u] = dev_load(xb + jj * xj + xm2);
                 }
             };
             auto block_ok = [&]() __attribute__((always_inline)) {
@@ -1149,9 +1167,9 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                 double mean, m2;
                 merge_wave_moments<DW>(red[t & 1], cnt[0], cnt_inv[0], inv_mine, mean, m2);
                 if (lane == 0 && !silent) {
-                    double* q = reinterpret_cast<double*>(parts + t * pstride + p);
-                    dev_store(q, ln_tag_word(mean, tag));
-                    dev_store(q + 1, ln_tag_word(m2, tag));
+                    double* xt = xchg + t * xstride;
+                    dev_store(xt + p * xj, ln_tag_word(mean, tag));
+                    dev_store(xt + p * xj + xm2, ln_tag_word(m2, tag));
                 }
             }
             if (!gather) continue;
@@ -1195,9 +1213,9 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                                 b2[u] = tv;
                             }
                             if (lane == 0) {
-                                double* q = reinterpret_cast<double*>(parts + g * pstride + jj);
-                                dev_store(q, tm);
-                                dev_store(q + 1, tv);
+                                double* xq = xchg + g * xstride;
+                                dev_store(xq + jj * xj, tm);
+                                dev_store(xq + jj * xj + xm2, tv);
                             }
                             ++n_done;
                         }
@@ -1531,7 +1549,8 @@ static int coresident(const void* fn, size_t lds, int threads)
 template <int F4PT, int DW>
 static bool try_launch_hold(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner,
                             float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats, Partial* parts,
-                            int64_t P_cap, float* mean_out, float* rstd_out, hipStream_t st, hipError_t& err)
+                            double* xchg, int64_t P_cap, float* mean_out, float* rstd_out, hipStream_t st,
+                            hipError_t& err)
 {
     DeviceInfo d;
     if (!device_info(d)) return false;
@@ -1574,7 +1593,7 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
         // sample) as stay co-resident, at most one per sample
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
         err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)(groups * P)),
-                            dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, parts,
+                            dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
                             mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force);
         return true;
     }
@@ -1627,6 +1646,7 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     uint32_t* flag = reinterpret_cast<uint32_t*>(base + lay.off_flag);
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
+    double* xchg = reinterpret_cast<double*>(base + lay.off_xchg);
 
     // A single-read kernel, when a co-resident grid can hold every sample's
     // rows (tuned tile first, then the others).
@@ -1634,7 +1654,7 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
 #define NORMFWD_TRY_HOLD(F, DW)                                                                                \
-    if (try_launch_hold<F, DW>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, lay.P_cap,      \
+    if (try_launch_hold<F, DW>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, xchg, lay.P_cap, \
                                mean_out, rstd_out, st, err))                                                      \
         return err;
         if (protocol == 1) {  // control wave, tagged gather

@@ -10,14 +10,14 @@
 //
 // The generation is kept in [0, 255) (it advances as (g + 1) mod 255, so no
 // counter wrap ever makes two consecutive launches share a tag) and the tag
-// is 1 + generation, never 0.  Every other writer of the
-// same slots stores a word that no tag matches: the zeroing kernel stores 0,
-// and the split and last-workgroup-merges schedules store an element count
-// (an integer below 2^44 as a double, whose low 8 mantissa bits are 0) in
-// the first word.  Consecutive generations have different tags, and a
-// control-wave launch writes every slot it reads, so the only words a reader
-// can find are the current launch's, the previous control-wave launch's, or
-// words no tag matches.
+// is 1 + generation, never 0.  The words live in a region of the workspace
+// that only control-wave launches write, besides the zeroing kernel, whose
+// 0 no tag matches (nor would an element count, an integer below 2^44 as a
+// double, whose low 8 mantissa bits are 0, as the other schedules store in
+// their own slots).  Consecutive generations have different tags, and a
+// control-wave launch writes every word it reads (a shape always runs the
+// same tile), so the only words a reader can find are the current launch's,
+// the previous control-wave launch's, or words no tag matches.
 //
 // Host and device versions are the same code (a CPU test checks them).
 #pragma once

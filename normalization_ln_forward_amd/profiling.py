@@ -13,6 +13,11 @@
         bytes whatever unit the counter uses.  With --json, the entries are
         written to that file together with the hash of the kernel sources, so
         bench.py reports them only while the kernels are unchanged.
+
+    python -m normalization_ln_forward_amd.profiling counters <counter_collection.csv>...
+        --kernels k1,k2 --command "<cmd>"
+        Markdown table of the per-dispatch mean of every counter of the named
+        kernels, from one or more `rocprofv3 --pmc` passes.
 """
 import argparse
 import csv
@@ -113,6 +118,27 @@ def traffic(fetch_csv, write_csv, copy_mib, kernels):
     return out
 
 
+def counters_markdown(paths, kernels, command):
+    """Per-dispatch means of every counter in one or more `rocprofv3 --pmc` CSVs, one row per kernel (a
+    kernel's dispatches averaged), one column per counter."""
+    vals = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"]).split("<")[0]
+            if k not in kernels:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    out = [f"Command: `{command}`", "", "| kernel | " + " | ".join(names) + " |",
+           "|---|" + "---:|" * len(names)]
+    for k in kernels:
+        if k not in vals:
+            continue
+        cells = [f"{statistics.mean(vals[k][c]):.4g}" if c in vals[k] else "" for c in names]
+        out.append(f"| {k} | " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -126,9 +152,16 @@ def main(argv=None):
     b.add_argument("--kernels", required=True)
     b.add_argument("--command", required=True)
     b.add_argument("--json")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernels", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         sys.stdout.write(stats_markdown(args.csv, args.command))
+        return
+    if args.cmd == "counters":
+        sys.stdout.write(counters_markdown(args.csv, args.kernels.split(","), args.command))
         return
     res = traffic(args.fetch_csv, args.write_csv, args.copy_mib, args.kernels.split(","))
     for k, v in res.items():
