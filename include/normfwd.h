@@ -231,11 +231,19 @@ normfwd_status ln_forward_apply(const float* x, const float* weight, const float
  *
  *   x, y          [N, C] fp32
  *   gamma, beta   [C] fp32, or NULL (= ones / zeros)
+ *   mean_out, rstd_out
+ *                 [N, num_groups] fp32, both or neither (one alone is
+ *                 NORMFWD_ERR_INVALID): each (row, group)'s mean and
+ *                 1 / sqrt(var + eps), rounded to fp32, the statistics the
+ *                 framework layer keeps for its backward pass (GN page,
+ *                 turn 1)
  *   C % num_groups != 0 -> NORMFWD_ERR_INVALID (the GN page checks the same)
+ * Statistics are taken around each group's first element, so groups far
+ * from 0 (e.g. after a large fc bias) keep their accuracy.
  * ---------------------------------------------------------------------- */
 normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const float* beta, float* y,
                                    int64_t N, int64_t C, int64_t num_groups, float eps,
-                                   float negative_slope, void* stream);
+                                   float negative_slope, float* mean_out, float* rstd_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * RMSNorm along dim 1 (RMS page, turns 1-2: rms = sqrt(mean over the
@@ -248,20 +256,42 @@ normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const flo
 normfwd_status rmsnorm_ch_forward(const float* x, float* y, int64_t B, int64_t C, int64_t S,
                                   float eps, void* stream);
 
+/* The same on strided views (the RMS page, turn 2, weighs the tensor's
+ * layout and its wrapper's contiguity handling; a channel slice or a
+ * batch-strided view is normalized here without a copy).  Element (b, c, s)
+ * of x is at x[b * x_batch_stride + c * x_channel_stride + s], of y at
+ * y[b * y_batch_stride + c * y_channel_stride + s]: the S positions of one
+ * (b, c) stay contiguous, strides are in elements and >= 0.  y's rows must
+ * not overlap one another (NORMFWD_ERR_INVALID otherwise); x may be any
+ * view, and y may be x itself with the same strides.
+ *   rstd_out  [B, S] fp32 or NULL: 1 / sqrt(mean over C of x^2 + eps) per
+ *             position, contiguous
+ * The 128-bit path needs 16-byte aligned pointers, S and every stride a
+ * multiple of 4; otherwise a scalar path computes the same result.
+ * rmsnorm_ch_forward(x, y, B, C, S, ...) equals this call with strides
+ * (C * S, S, C * S, S) and no rstd_out. */
+normfwd_status rmsnorm_ch_forward_strided(const float* x, float* y, int64_t B, int64_t C, int64_t S,
+                                          int64_t x_batch_stride, int64_t x_channel_stride,
+                                          int64_t y_batch_stride, int64_t y_channel_stride,
+                                          float eps, float* rstd_out, void* stream);
+
 /* ------------------------------------------------------------------------
  * fc followed by GroupNorm -> LeakyReLU -> x + x (GN page, turn 1: h = x W^T
  * + b with x [N, K], W [C, K], b [C]; then the GN epilogue above on h).
  *
  *   workspace  device buffer of at least fc_gn_forward_workspace_size(N, K,
- *              C) bytes (holds h, [N, C] fp32), 256-byte aligned
+ *              C) bytes (holds h, [N, C] fp32, for group sizes the GEMM's
+ *              epilogue does not handle itself), 256-byte aligned
  *   b, gamma, beta may be NULL.
+ *   mean_out, rstd_out  as for gn_lrelu_x2_forward: the statistics of h's
+ *              (row, group)s, [N, num_groups] fp32, both or neither.
  * ---------------------------------------------------------------------- */
 size_t fc_gn_forward_workspace_size(int64_t N, int64_t K, int64_t C);
 normfwd_status fc_gn_forward(const float* x, const float* W, const float* b,
                              const float* gamma, const float* beta, float* y,
                              int64_t N, int64_t K, int64_t C, int64_t num_groups, float eps,
                              float negative_slope, void* workspace, size_t workspace_bytes,
-                             void* stream);
+                             float* mean_out, float* rstd_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement references (not normalization operations): plain copies with

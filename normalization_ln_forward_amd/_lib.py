@@ -40,11 +40,12 @@ SIGNATURES = {
     "ln_forward_noalloc": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _P, ctypes.c_int, _P]),
     "ln_forward_stats": (_ST, [_P, _I64, _I64, _F, _P, _SZ, _P, _P, _P]),
     "ln_forward_apply": (_ST, [_P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
-    "gn_lrelu_x2_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _F, _F, _P]),
+    "gn_lrelu_x2_forward": (_ST, [_P, _P, _P, _P, _I64, _I64, _I64, _F, _F, _P, _P, _P]),
     "rmsnorm_ch_forward": (_ST, [_P, _P, _I64, _I64, _I64, _F, _P]),
+    "rmsnorm_ch_forward_strided": (_ST, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P, _P]),
     "normfwd_copy_reference": (_ST, [_P, _P, _I64, _I64, _I64, ctypes.c_int, _P]),
     "fc_gn_forward_workspace_size": (_SZ, [_I64, _I64, _I64]),
-    "fc_gn_forward": (_ST, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P, _SZ, _P]),
+    "fc_gn_forward": (_ST, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _F, _P, _SZ, _P, _P, _P]),
 }
 
 _LIB = None
@@ -302,8 +303,17 @@ def ln_forward_apply(x, weight, bias, workspace, normalized_ndim=None, out=None)
 
 # ---------------------------------------------------------------- GroupNorm + LeakyReLU + x2
 
-def gn_lrelu_x2_forward(x, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01, out=None):
-    """GroupNorm(num_groups) on [N, C], then LeakyReLU(negative_slope), then x + x."""
+def _gn_stats(mean_out, rstd_out, N, G, dev):
+    if (mean_out is None) != (rstd_out is None):
+        raise ValueError("give both mean_out and rstd_out, or neither")
+    _opt(mean_out, "mean_out", N * G, dev)
+    _opt(rstd_out, "rstd_out", N * G, dev)
+
+
+def gn_lrelu_x2_forward(x, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01, out=None, mean_out=None,
+                        rstd_out=None):
+    """GroupNorm(num_groups) on [N, C], then LeakyReLU(negative_slope), then x + x.  ``mean_out`` and
+    ``rstd_out`` ([N, num_groups], both or neither) receive each (row, group)'s statistics."""
     _need(x, "x")
     if x.dim() != 2:
         raise ValueError("x must be [N, C]")
@@ -311,25 +321,59 @@ def gn_lrelu_x2_forward(x, gamma, beta, num_groups, eps=1e-5, negative_slope=0.0
     dev = x.device
     _opt(gamma, "gamma", C, dev)
     _opt(beta, "beta", C, dev)
+    _gn_stats(mean_out, rstd_out, N, int(num_groups), dev)
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", dev)
     _invoke("gn_lrelu_x2_forward", _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), N, C, int(num_groups),
-                                     float(eps), float(negative_slope), _stream(dev))
+                                     float(eps), float(negative_slope), _ptr(mean_out), _ptr(rstd_out), _stream(dev))
     return y
 
 
 # ---------------------------------------------------------------- RMSNorm over dim 1
 
-def rmsnorm_ch_forward(x, eps=1e-5, out=None):
-    """y = x / sqrt(mean over dim 1 of x^2 + eps) for x of shape [B, C, *spatial]."""
-    _need(x, "x")
+def _rms_strides(t, name):
+    """(batch stride, channel stride) of a [B, C, *spatial] view whose spatial block is contiguous."""
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    expect = 1
+    for d in range(t.dim() - 1, 1, -1):
+        if t.shape[d] != 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: the dims after dim 1 must be contiguous (a batch or channel stride is fine)")
+        expect *= t.shape[d]
+    return t.stride(0), t.stride(1)
+
+
+def rmsnorm_ch_forward(x, eps=1e-5, out=None, rstd_out=None):
+    """y = x / sqrt(mean over dim 1 of x^2 + eps) for x of shape [B, C, *spatial].
+
+    x (and ``out``) may be strided in dims 0 and 1 (a channel slice, a batch-strided view) as long as the
+    trailing dims are contiguous; ``rstd_out`` ([B, *spatial], contiguous) receives 1 / rms per position.
+    Contiguous tensors without ``rstd_out`` go through rmsnorm_ch_forward, the rest through
+    rmsnorm_ch_forward_strided."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
     if x.dim() < 2:
         raise ValueError("x must have at least 2 dims")
     B, C = x.shape[0], x.shape[1]
     S = x.numel() // (B * C) if B * C else 0
-    y = torch.empty_like(x) if out is None else out
-    _need(y, "out", x.device)
-    _invoke("rmsnorm_ch_forward", _ptr(x), _ptr(y), B, C, S, float(eps), _stream(x.device))
+    xsb, xsc = _rms_strides(x, "x")
+    y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    if y.device != x.device:
+        raise ValueError(f"out is on {y.device}, expected {x.device}")
+    ysb, ysc = _rms_strides(y, "out")
+    if rstd_out is not None:
+        _need(rstd_out, "rstd_out", x.device)
+        if rstd_out.numel() != B * S:
+            raise ValueError(f"rstd_out has {rstd_out.numel()} elements, expected {B * S}")
+    if x.is_contiguous() and y.is_contiguous() and rstd_out is None:
+        _invoke("rmsnorm_ch_forward", _ptr(x), _ptr(y), B, C, S, float(eps), _stream(x.device))
+    else:
+        _invoke("rmsnorm_ch_forward_strided", _ptr(x), _ptr(y), B, C, S, xsb, xsc, ysb, ysc, float(eps),
+                _ptr(rstd_out), _stream(x.device))
     return y
 
 
@@ -338,8 +382,10 @@ def rmsnorm_ch_forward(x, eps=1e-5, out=None):
 _FC_WS = {}
 
 
-def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01, out=None, workspace=None):
-    """h = x W^T + b (fp32 on the matrix cores), then gn_lrelu_x2_forward on h."""
+def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01, out=None, workspace=None,
+                  mean_out=None, rstd_out=None):
+    """h = x W^T + b (fp32 on the matrix cores), then gn_lrelu_x2_forward on h (``mean_out`` and ``rstd_out``:
+    h's (row, group) statistics, [N, num_groups], both or neither)."""
     _need(x, "x")
     _need(W, "W", x.device)
     if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[1]:
@@ -350,6 +396,7 @@ def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.0
     _opt(b, "b", C, dev)
     _opt(gamma, "gamma", C, dev)
     _opt(beta, "beta", C, dev)
+    _gn_stats(mean_out, rstd_out, N, int(num_groups), dev)
     y = torch.empty((N, C), dtype=torch.float32, device=dev) if out is None else out
     _need(y, "out", dev)
     nbytes = int(lib().fc_gn_forward_workspace_size(N, K, C))
@@ -361,7 +408,8 @@ def fc_gn_forward(x, W, b, gamma, beta, num_groups, eps=1e-5, negative_slope=0.0
         workspace = hit[1]
     _invoke("fc_gn_forward", _ptr(x), _ptr(W), _ptr(b), _ptr(gamma), _ptr(beta), _ptr(y), N, K, C,
                                int(num_groups), float(eps), float(negative_slope), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(dev))
+                               workspace.numel() * workspace.element_size(), _ptr(mean_out), _ptr(rstd_out),
+                               _stream(dev))
     return y
 
 

@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <limits>
 #include <mutex>
+#include <utility>
 
 #include "internal.hpp"
 
@@ -296,7 +297,8 @@ normfwd_status ln_forward_noalloc(const float* x, const float* weight, const flo
 }
 
 normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
-                                   int64_t C, int64_t num_groups, float eps, float negative_slope, void* stream)
+                                   int64_t C, int64_t num_groups, float eps, float negative_slope, float* mean_out,
+                                   float* rstd_out, void* stream)
 {
     if (N == 0 && C > 0 && num_groups > 0 && C % num_groups == 0) return ok();  // no rows: nothing to do
     if (!x || !y) return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: x and y must not be NULL");
@@ -312,9 +314,11 @@ normfwd_status gn_lrelu_x2_forward(const float* x, const float* gamma, const flo
     if (C / num_groups > std::numeric_limits<int>::max())
         return fail(NORMFWD_ERR_UNSUPPORTED, "gn_lrelu_x2_forward: group too large");
     if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: eps must be >= 0");
+    if (!mean_out != !rstd_out)
+        return fail(NORMFWD_ERR_INVALID, "gn_lrelu_x2_forward: give both mean_out and rstd_out, or neither");
     (void)hipGetLastError();
-    return hip_status(normfwd::launch_gn_lrelu_x2(x, gamma, beta, y, N, C, num_groups, eps, negative_slope,
-                                                  (hipStream_t)stream),
+    return hip_status(normfwd::launch_gn_lrelu_x2(x, gamma, beta, y, N, C, num_groups, eps, negative_slope, mean_out,
+                                                  rstd_out, (hipStream_t)stream),
                       "gn_lrelu_x2_forward launch");
 }
 
@@ -327,7 +331,55 @@ normfwd_status rmsnorm_ch_forward(const float* x, float* y, int64_t B, int64_t C
         return fail(NORMFWD_ERR_UNSUPPORTED, "rmsnorm_ch_forward: shape too large (C < 2^31, S <= 2^26)");
     if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward: eps must be >= 0");
     (void)hipGetLastError();
-    return hip_status(normfwd::launch_rms_ch(x, y, B, C, S, eps, (hipStream_t)stream), "rmsnorm_ch_forward launch");
+    return hip_status(normfwd::launch_rms_ch(x, y, B, C, S, eps, normfwd::RmsStrides{C * S, S, C * S, S}, nullptr,
+                                             (hipStream_t)stream),
+                      "rmsnorm_ch_forward launch");
+}
+
+normfwd_status rmsnorm_ch_forward_strided(const float* x, float* y, int64_t B, int64_t C, int64_t S,
+                                          int64_t x_batch_stride, int64_t x_channel_stride, int64_t y_batch_stride,
+                                          int64_t y_channel_stride, float eps, float* rstd_out, void* stream)
+{
+    if ((B == 0 || S == 0) && B >= 0 && S >= 0 && C > 0) return ok();  // no positions: nothing to do
+    if (!x || !y) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward_strided: x and y must not be NULL");
+    if (B <= 0 || C <= 0 || S <= 0)
+        return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward_strided: B, C and S must be > 0");
+    if (x_batch_stride < 0 || x_channel_stride < 0 || y_batch_stride < 0 || y_channel_stride < 0)
+        return fail(NORMFWD_ERR_UNSUPPORTED, "rmsnorm_ch_forward_strided: negative strides are not supported");
+    if (C > std::numeric_limits<int>::max() || S > ((int64_t)1 << 26) || B > kMaxElems / S || C > kMaxElems / S)
+        return fail(NORMFWD_ERR_UNSUPPORTED, "rmsnorm_ch_forward_strided: shape too large (C < 2^31, S <= 2^26)");
+    // the last element each tensor addresses must stay below 2^40
+    auto span = [&](int64_t sb, int64_t sc) {
+        const int64_t lim = kMaxElems;
+        if (B > 1 && sb > (lim - S) / (B - 1)) return lim;
+        if (C > 1 && sc > (lim - S) / (C - 1)) return lim;
+        const int64_t a = (B - 1) * sb, c = (C - 1) * sc;
+        return a > lim - S - c ? lim : a + c + S;
+    };
+    if (span(x_batch_stride, x_channel_stride) >= kMaxElems || span(y_batch_stride, y_channel_stride) >= kMaxElems)
+        return fail(NORMFWD_ERR_UNSUPPORTED, "rmsnorm_ch_forward_strided: a view spans 2^40 elements or more");
+    // y's rows of S positions must not overlap one another: ordered by
+    // stride, the smaller one (if its extent is > 1) is at least S and the
+    // larger one (if its extent is > 1) at least that row block
+    {
+        int64_t s1 = y_batch_stride, n1 = B, s2 = y_channel_stride, n2 = C;
+        if (n1 == 1 || (n2 > 1 && s2 < s1)) {
+            std::swap(s1, s2);
+            std::swap(n1, n2);
+        }
+        const int64_t block = n1 > 1 ? s1 * n1 : S;
+        const bool ok1 = n1 == 1 || s1 >= S;
+        const bool ok2 = n2 == 1 || s2 >= block;
+        if (!ok1 || !ok2)
+            return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward_strided: y's strides make its rows overlap");
+    }
+    if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "rmsnorm_ch_forward_strided: eps must be >= 0");
+    (void)hipGetLastError();
+    return hip_status(
+        normfwd::launch_rms_ch(x, y, B, C, S, eps,
+                               normfwd::RmsStrides{x_batch_stride, x_channel_stride, y_batch_stride, y_channel_stride},
+                               rstd_out, (hipStream_t)stream),
+        "rmsnorm_ch_forward_strided launch");
 }
 
 normfwd_status normfwd_copy_reference(const float* src, float* dst, int64_t B, int64_t C, int64_t S, int pattern,
@@ -358,7 +410,8 @@ size_t fc_gn_forward_workspace_size(int64_t N, int64_t K, int64_t C)
 
 normfwd_status fc_gn_forward(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
                              float* y, int64_t N, int64_t K, int64_t C, int64_t num_groups, float eps,
-                             float negative_slope, void* workspace, size_t workspace_bytes, void* stream)
+                             float negative_slope, void* workspace, size_t workspace_bytes, float* mean_out,
+                             float* rstd_out, void* stream)
 {
     if (N == 0 && K >= 0 && C > 0 && num_groups > 0 && C % num_groups == 0) return ok();  // no rows: nothing to do
     if (!x && K > 0) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: x must not be NULL");
@@ -372,11 +425,13 @@ normfwd_status fc_gn_forward(const float* x, const float* W, const float* b, con
     if (N > kMaxElems / C || C > kMaxElems / K1 || N > kMaxElems / K1 || N > (1 << 23) || C > (1 << 24))
         return fail(NORMFWD_ERR_UNSUPPORTED, "fc_gn_forward: shape too large");
     if (!(eps >= 0.0f)) return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: eps must be >= 0");
+    if (!mean_out != !rstd_out)
+        return fail(NORMFWD_ERR_INVALID, "fc_gn_forward: give both mean_out and rstd_out, or neither");
     normfwd_status s = check_ws(workspace, workspace_bytes, fc_gn_forward_workspace_size(N, K, C), "fc_gn_forward");
     if (s != NORMFWD_OK) return s;
     (void)hipGetLastError();
     return hip_status(normfwd::launch_fc_gn(x, W, b, gamma, beta, y, N, K, C, num_groups, eps, negative_slope,
-                                            workspace, (hipStream_t)stream),
+                                            workspace, mean_out, rstd_out, (hipStream_t)stream),
                       "fc_gn_forward launch");
 }
 

@@ -140,7 +140,8 @@ template <int GM>
 __device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __restrict__ bias,
                                             const float* __restrict__ gamma, const float* __restrict__ beta,
                                             float* __restrict__ out, int M, int N, int m0w, int n0w, int li, int lh,
-                                            float eps, float slope)
+                                            float eps, float slope, float* __restrict__ mean_out,
+                                            float* __restrict__ rstd_out)
 {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -164,16 +165,26 @@ __device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __re
                 // (acc_c - acc_k) + (b_c - b_k), so neither a large bias nor
                 // an offset of the group from 0 is ever rounded at its own
                 // magnitude (h itself never exists in fp32 here)
-                const float db = bb - group_first<GM>(bb);
+                const float bk = group_first<GM>(bb);
+                const float db = bb - bk;
+                // the group's first lane writes the (row, group) statistics
+                const bool stats = mean_out && col_ok && (li & (GM - 1)) == 0;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float hk = (acc[i][j][r] - group_first<GM>(acc[i][j][r])) + db;
+                    const float ak = group_first<GM>(acc[i][j][r]);
+                    const float hk = (acc[i][j][r] - ak) + db;
                     const float s1 = group_lanes_sum<GM>(hk);
-                    const float d = hk - s1 * inv_m;
+                    const float md = s1 * inv_m;
+                    const float d = hk - md;
                     const float s2 = group_lanes_sum<GM>(d * d);
                     const float rstd = 1.0f / sqrtf(s2 * inv_m + eps);
                     const int row = m0w + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
                     if (row < M && col_ok) out[(int64_t)row * N + col] = gn_out(d, rstd, g, be, slope);
+                    if (stats && row < M) {
+                        const int64_t gi = (int64_t)row * (N / GM) + col / GM;
+                        mean_out[gi] = (ak + bk) + md;
+                        rstd_out[gi] = rstd;
+                    }
                 }
             }
         }
@@ -204,6 +215,11 @@ __device__ __forceinline__ void fc_epilogue(f16v (&acc)[2][2], const float* __re
                 if (row < M) {
                     if (ok0) out[(int64_t)row * N + c0] = gn_out(d0, rstd, g0, be0, slope);
                     if (ok1) out[(int64_t)row * N + c1] = gn_out(d1, rstd, g1, be1, slope);
+                    if (mean_out && ok0 && li == 0) {  // the group's first lane: (row, group) statistics
+                        const int64_t gi = (int64_t)row * (N / 64) + c0 / 64;
+                        mean_out[gi] = (ak + bk) + s1 * inv_m;
+                        rstd_out[gi] = rstd;
+                    }
                 }
             }
     }
@@ -227,7 +243,7 @@ template <bool VEC, int GM, int WM>
 __global__ void __launch_bounds__(Tile<WM>::kThreads)
 fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
                const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ out, int M,
-               int N, int K, float eps, float slope)
+               int N, int K, float eps, float slope, float* __restrict__ mean_out, float* __restrict__ rstd_out)
 {
     using T = Tile<WM>;
     __shared__ __attribute__((aligned(16))) float As[2][T::kBM * kLdsRow];
@@ -278,7 +294,8 @@ fc_mfma_kernel(const float* __restrict__ x, const float* __restrict__ W, const f
         __syncthreads();
     }
 
-    fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope);
+    fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope, mean_out,
+                    rstd_out);
 }
 
 // Direct-to-LDS variant (K a multiple of 32, 16-byte aligned rows): the
@@ -305,7 +322,7 @@ template <int GM>
 __global__ void __launch_bounds__(kDmaThreads)
 fc_dma_kernel(const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
               const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ out, int M, int N,
-              int K, float eps, float slope)
+              int K, float eps, float slope, float* __restrict__ mean_out, float* __restrict__ rstd_out)
 {
     __shared__ __attribute__((aligned(16))) float lds[kDmaStages * kDmaStageFloats];
 
@@ -396,32 +413,33 @@ fc_dma_kernel(const float* __restrict__ x, const float* __restrict__ W, const fl
         mfma_step(1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the workgroup's LDS
-    fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope);
+    fc_epilogue<GM>(acc, bias, gamma, beta, out, M, N, m0 + wm * 64, n0 + wn * 64, li, lh, eps, slope, mean_out,
+                    rstd_out);
 }
 
 template <int GM>
 static hipError_t launch_gemm(bool vec, const float* x, const float* W, const float* b, const float* gamma,
                               const float* beta, float* out, int64_t N, int64_t K, int64_t C, float eps, float slope,
-                              hipStream_t st)
+                              float* mo, float* ro, hipStream_t st)
 {
     if (NORMFWD_FC_DMA && vec && K >= 32 && K % 32 == 0) {
         const dim3 g((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, kDmaBM));
         return launch_kernel((fc_dma_kernel<GM>), g, dim3(kDmaThreads), 0, st, x, W, b, gamma, beta, out, (int)N,
-                             (int)C, (int)K, eps, slope);
+                             (int)C, (int)K, eps, slope, mo, ro);
     }
     constexpr int WM = NORMFWD_FC_WM;
     using T = Tile<WM>;
     const dim3 grid((unsigned)ceil_div(C, kBN), (unsigned)ceil_div(N, T::kBM));
     if (vec)
         return launch_kernel((fc_mfma_kernel<true, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta,
-                             out, (int)N, (int)C, (int)K, eps, slope);
+                             out, (int)N, (int)C, (int)K, eps, slope, mo, ro);
     return launch_kernel((fc_mfma_kernel<false, GM, WM>), grid, dim3(T::kThreads), 0, st, x, W, b, gamma, beta, out,
-                         (int)N, (int)C, (int)K, eps, slope);
+                         (int)N, (int)C, (int)K, eps, slope, mo, ro);
 }
 
 hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
                         float* y, int64_t N, int64_t K, int64_t C, int64_t G, float eps, float slope, void* ws,
-                        hipStream_t st)
+                        float* mo, float* ro, hipStream_t st)
 {
     // The tile loader reads 16-byte vectors along K when rows allow it.
     auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
@@ -432,18 +450,18 @@ hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const fl
     // a multiple of 64, so no group straddles waves.
     if (NORMFWD_FC_FUSE) {
         switch (M) {
-            case 4: return launch_gemm<4>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
-            case 8: return launch_gemm<8>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
-            case 16: return launch_gemm<16>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
-            case 32: return launch_gemm<32>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
-            case 64: return launch_gemm<64>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, st);
+            case 4: return launch_gemm<4>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, mo, ro, st);
+            case 8: return launch_gemm<8>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, mo, ro, st);
+            case 16: return launch_gemm<16>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, mo, ro, st);
+            case 32: return launch_gemm<32>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, mo, ro, st);
+            case 64: return launch_gemm<64>(vec, x, W, b, gamma, beta, y, N, K, C, eps, slope, mo, ro, st);
             default: break;
         }
     }
     float* h = static_cast<float*>(ws);
-    hipError_t e = launch_gemm<0>(vec, x, W, b, nullptr, nullptr, h, N, K, C, eps, slope, st);
+    hipError_t e = launch_gemm<0>(vec, x, W, b, nullptr, nullptr, h, N, K, C, eps, slope, nullptr, nullptr, st);
     if (e != hipSuccess) return e;
-    return launch_gn_lrelu_x2(h, gamma, beta, y, N, C, G, eps, slope, st);
+    return launch_gn_lrelu_x2(h, gamma, beta, y, N, C, G, eps, slope, mo, ro, st);
 }
 
 }  // namespace normfwd

@@ -54,7 +54,8 @@ __device__ __forceinline__ float lrelu_x2(float z, float slope)
 template <int L, int ITEMS>
 __global__ void __launch_bounds__(256)
 gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __restrict__ beta, float* y,
-               int64_t n_tiles, int64_t tiles_per_row, int64_t C4, int M, float eps, float slope)
+               int64_t n_tiles, int64_t tiles_per_row, int64_t C4, int M, float eps, float slope, float* mean_out,
+               float* rstd_out)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t blk = NORMFWD_GN_XCD ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
@@ -77,11 +78,17 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const int64_t c4 = c4_0 + i * kWave;
-        const f4 dk = v[i] - group_first<L>(v[i].x);
+        const float K = group_first<L>(v[i].x);
+        const f4 dk = v[i] - K;
         const float md = group_sum<L>((dk.x + dk.y) + (dk.z + dk.w)) * inv_m;
         const f4 d = dk - md;
         const float ssd = group_sum<L>((d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w));
         const float rstd = 1.0f / sqrtf(ssd * inv_m + eps);
+        if (mean_out && c4 < C4 && c4 % L == 0) {  // the group's first lane: statistics of (row, group)
+            const int64_t gi = row * (C4 / L) + c4 / L;
+            mean_out[gi] = K + md;
+            rstd_out[gi] = rstd;
+        }
         if (c4 < C4) {
             const f4 g = gamma ? g4[c4] : f4(1.0f);
             const f4 bb = beta ? b4[c4] : f4(0.0f);
@@ -104,7 +111,8 @@ gn_fast_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 // the fast kernel), a third for the output.
 __global__ void __launch_bounds__(256)
 gn_lane_kernel(const float* x, const float* __restrict__ gamma, const float* __restrict__ beta, float* y,
-               int64_t n_groups_total, int64_t G, int64_t C, int M, float eps, float slope)
+               int64_t n_groups_total, int64_t G, int64_t C, int M, float eps, float slope, float* mean_out,
+               float* rstd_out)
 {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n_groups_total) return;
@@ -120,6 +128,10 @@ gn_lane_kernel(const float* x, const float* __restrict__ gamma, const float* __r
         ssd += d * d;
     }
     const float rstd = 1.0f / sqrtf(ssd / (float)M + eps);
+    if (mean_out) {
+        mean_out[t] = K + md;
+        rstd_out[t] = rstd;
+    }
     for (int j = 0; j < M; ++j) {
         const int64_t c = g * M + j;
         float z = ((x[base + j] - K) - md) * rstd;
@@ -132,7 +144,8 @@ gn_lane_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 // Generic: one wave per (row, group) for large M; lanes stride the group.
 __global__ void __launch_bounds__(256)
 gn_wave_kernel(const float* x, const float* __restrict__ gamma, const float* __restrict__ beta, float* y,
-               int64_t n_groups_total, int64_t G, int64_t C, int64_t M, float eps, float slope)
+               int64_t n_groups_total, int64_t G, int64_t C, int64_t M, float eps, float slope, float* mean_out,
+               float* rstd_out)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -149,6 +162,10 @@ gn_wave_kernel(const float* x, const float* __restrict__ gamma, const float* __r
         ssd += d * d;
     }
     const float rstd = 1.0f / sqrtf(wave_sum(ssd) / (float)M + eps);
+    if (mean_out && lane == 0) {
+        mean_out[t] = K + md;
+        rstd_out[t] = rstd;
+    }
     // Every lane has finished reading the group before any lane writes it
     // (wave_sum is a wave-wide exchange), which keeps y == x safe.
     for (int64_t j = lane; j < M; j += kWave) {
@@ -162,7 +179,7 @@ gn_wave_kernel(const float* x, const float* __restrict__ gamma, const float* __r
 
 template <int L, int ITEMS>
 static hipError_t launch_fast(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
-                              int64_t C, int64_t M, float eps, float slope, hipStream_t st)
+                              int64_t C, int64_t M, float eps, float slope, float* mo, float* ro, hipStream_t st)
 {
     const int64_t C4 = C / 4;
     const int64_t tiles_per_row = ceil_div(C4, (int64_t)ITEMS * kWave);
@@ -170,9 +187,10 @@ static hipError_t launch_fast(const float* x, const float* gamma, const float* b
     for (int64_t r0 = 0; r0 < N; r0 += per) {
         const int64_t nr = std::min(per, N - r0);
         const int64_t n_tiles = nr * tiles_per_row;
+        const int64_t G = C / M;
         const hipError_t e = launch_kernel((gn_fast_kernel<L, ITEMS>), dim3((unsigned)ceil_div(n_tiles, 4)), dim3(256),
                                            0, st, x + r0 * C, gamma, beta, y + r0 * C, n_tiles, tiles_per_row, C4,
-                                           (int)M, eps, slope);
+                                           (int)M, eps, slope, mo ? mo + r0 * G : nullptr, ro ? ro + r0 * G : nullptr);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -180,16 +198,19 @@ static hipError_t launch_fast(const float* x, const float* gamma, const float* b
 
 template <int L>
 static hipError_t launch_fast_items(const float* x, const float* gamma, const float* beta, float* y,
-                                    int64_t N, int64_t C, int64_t M, float eps, float slope, hipStream_t st)
+                                    int64_t N, int64_t C, int64_t M, float eps, float slope, float* mo, float* ro,
+                                    hipStream_t st)
 {
     // A wave's tile never needs to be longer than the row.
     constexpr int items = NORMFWD_GN_ITEMS;
-    if (C / 4 <= 1 * kWave || items <= 1) return launch_fast<L, 1>(x, gamma, beta, y, N, C, M, eps, slope, st);
-    if (C / 4 <= 2 * kWave || items <= 2) return launch_fast<L, 2>(x, gamma, beta, y, N, C, M, eps, slope, st);
-    if (C / 4 <= 4 * kWave || items <= 4) return launch_fast<L, 4>(x, gamma, beta, y, N, C, M, eps, slope, st);
-    if (C / 4 <= 8 * kWave || items <= 8) return launch_fast<L, 8>(x, gamma, beta, y, N, C, M, eps, slope, st);
-    if (C / 4 <= 16 * kWave || items <= 16) return launch_fast<L, 16>(x, gamma, beta, y, N, C, M, eps, slope, st);
-    return launch_fast<L, 32>(x, gamma, beta, y, N, C, M, eps, slope, st);
+#define NORMFWD_GN_FAST(I) return launch_fast<L, I>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st)
+    if (C / 4 <= 1 * kWave || items <= 1) NORMFWD_GN_FAST(1);
+    if (C / 4 <= 2 * kWave || items <= 2) NORMFWD_GN_FAST(2);
+    if (C / 4 <= 4 * kWave || items <= 4) NORMFWD_GN_FAST(4);
+    if (C / 4 <= 8 * kWave || items <= 8) NORMFWD_GN_FAST(8);
+    if (C / 4 <= 16 * kWave || items <= 16) NORMFWD_GN_FAST(16);
+    NORMFWD_GN_FAST(32);
+#undef NORMFWD_GN_FAST
 }
 
 bool gn_fast_path_applies(const float* x, const float* gamma, const float* beta, const float* y, int64_t C,
@@ -204,18 +225,18 @@ bool gn_fast_path_applies(const float* x, const float* gamma, const float* beta,
 }
 
 hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
-                              int64_t C, int64_t G, float eps, float slope, hipStream_t st)
+                              int64_t C, int64_t G, float eps, float slope, float* mo, float* ro, hipStream_t st)
 {
     const int64_t M = C / G;
     if (gn_fast_path_applies(x, gamma, beta, y, C, M)) {
         switch (M / 4) {
-            case 1: return launch_fast_items<1>(x, gamma, beta, y, N, C, M, eps, slope, st);
-            case 2: return launch_fast_items<2>(x, gamma, beta, y, N, C, M, eps, slope, st);
-            case 4: return launch_fast_items<4>(x, gamma, beta, y, N, C, M, eps, slope, st);
-            case 8: return launch_fast_items<8>(x, gamma, beta, y, N, C, M, eps, slope, st);
-            case 16: return launch_fast_items<16>(x, gamma, beta, y, N, C, M, eps, slope, st);
-            case 32: return launch_fast_items<32>(x, gamma, beta, y, N, C, M, eps, slope, st);
-            case 64: return launch_fast_items<64>(x, gamma, beta, y, N, C, M, eps, slope, st);
+            case 1: return launch_fast_items<1>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
+            case 2: return launch_fast_items<2>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
+            case 4: return launch_fast_items<4>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
+            case 8: return launch_fast_items<8>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
+            case 16: return launch_fast_items<16>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
+            case 32: return launch_fast_items<32>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
+            case 64: return launch_fast_items<64>(x, gamma, beta, y, N, C, M, eps, slope, mo, ro, st);
             default: break;
         }
     }
@@ -223,11 +244,13 @@ hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* b
     const int64_t per = samples_per_launch(M <= 32 ? G : G * kWave);
     for (int64_t r0 = 0; r0 < N; r0 += per) {
         const int64_t total = std::min(per, N - r0) * G;
+        float* mb = mo ? mo + r0 * G : nullptr;
+        float* rb = ro ? ro + r0 * G : nullptr;
         const hipError_t e =
             M <= 32 ? launch_kernel(gn_lane_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, x + r0 * C,
-                                    gamma, beta, y + r0 * C, total, G, C, (int)M, eps, slope)
+                                    gamma, beta, y + r0 * C, total, G, C, (int)M, eps, slope, mb, rb)
                     : launch_kernel(gn_wave_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, st, x + r0 * C,
-                                    gamma, beta, y + r0 * C, total, G, C, M, eps, slope);
+                                    gamma, beta, y + r0 * C, total, G, C, M, eps, slope, mb, rb);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

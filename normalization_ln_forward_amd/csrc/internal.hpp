@@ -48,11 +48,19 @@ inline int64_t samples_per_launch(int64_t items_per_sample)
     return items_per_sample >= max_grid_items() ? 1 : max_grid_items() / items_per_sample;
 }
 
-hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
-                         hipStream_t st);
+// Element strides of a [B, C, S] view whose S positions of one (b, c) are
+// contiguous: x at b * xsb + c * xsc + s, y at b * ysb + c * ysc + s.
+struct RmsStrides {
+    int64_t xsb, xsc, ysb, ysc;
+};
+// rstd: [B, S] (1 / sqrt(ms + eps) per position) or NULL.
+hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps, const RmsStrides& L,
+                         float* rstd, hipStream_t st);
 
+// mean_out, rstd_out: [N, G] or NULL (both or neither).
 hipError_t launch_gn_lrelu_x2(const float* x, const float* gamma, const float* beta, float* y, int64_t N,
-                              int64_t C, int64_t G, float eps, float slope, hipStream_t st);
+                              int64_t C, int64_t G, float eps, float slope, float* mean_out, float* rstd_out,
+                              hipStream_t st);
 
 // LayerNorm workspace: byte offsets of each region (all 256-byte aligned).
 struct LnLayout {
@@ -113,6 +121,6 @@ hipError_t launch_rms_copy_pattern(const float* x, float* y, int64_t B, int64_t 
 
 hipError_t launch_fc_gn(const float* x, const float* W, const float* b, const float* gamma, const float* beta,
                         float* y, int64_t N, int64_t K, int64_t C, int64_t G, float eps, float slope, void* ws,
-                        hipStream_t st);
+                        float* mean_out, float* rstd_out, hipStream_t st);
 
 }  // namespace normfwd

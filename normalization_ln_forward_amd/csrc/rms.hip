@@ -18,6 +18,13 @@
 //      with nontemporal 128-bit stores.
 // Channel counts beyond what fits in registers use a streaming kernel that
 // reads x twice (the second read is served by L2 / MALL when it hits).
+//
+// Strided views (RMS page, turn 2 reasons about the layout and the
+// wrapper's contiguity handling): the kernels take the batch and channel
+// strides of x and y separately (the positions of one channel row stay
+// contiguous), so a channel slice or a batch-strided view is normalized in
+// place of a copy; rstd (1 / sqrt(ms + eps) per position, [B, S]) is
+// written when asked for.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -62,7 +69,8 @@ constexpr int hold_max_threads(int vecs) { return vecs <= 16 ? 1024 : vecs <= 32
 // measurement reference for what this access pattern costs by itself
 // (rms_copy_pattern_kernel).
 template <int CPW, int PPL, int VEC, bool NORM>
-__device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+__device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps,
+                                              RmsStrides L, float* rstd)
 {
     using V = typename VecOf<VEC>::T;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -78,7 +86,8 @@ __device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, i
     // position of (lane, j): the wave reads PPL adjacent 64*VEC-position segments per channel
     const int64_t s0 = tile * (kWave * PPL * VEC) + (int64_t)lane * VEC;
     const int c0 = wave * CPW;
-    const int64_t base = (b * C + c0) * S + s0;
+    const int64_t base = b * L.xsb + (int64_t)c0 * L.xsc + s0;   // x
+    const int64_t ybase = b * L.ysb + (int64_t)c0 * L.ysc + s0;  // y
 
     V v[CPW][PPL];
     // Interior tiles (every position and channel of this wave in range, the
@@ -90,7 +99,7 @@ __device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, i
         for (int k = 0; k < CPW; ++k)
 #pragma unroll
             for (int j = 0; j < PPL; ++j) {
-                const V* src = reinterpret_cast<const V*>(x + base + (int64_t)k * S + j * kWave * VEC);
+                const V* src = reinterpret_cast<const V*>(x + base + (int64_t)k * L.xsc + j * kWave * VEC);
                 v[k][j] = NORMFWD_RMS_NT_LOAD ? ld_nt(src) : *src;
             }
     } else {
@@ -99,7 +108,7 @@ __device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, i
 #pragma unroll
             for (int j = 0; j < PPL; ++j) {
                 const bool ok = (s0 + j * kWave * VEC < S) && (c0 + k < C);  // VEC == 4 implies S % 4 == 0
-                const V* src = reinterpret_cast<const V*>(x + base + (int64_t)k * S + j * kWave * VEC);
+                const V* src = reinterpret_cast<const V*>(x + base + (int64_t)k * L.xsc + j * kWave * VEC);
                 v[k][j] = ok ? (NORMFWD_RMS_NT_LOAD ? ld_nt(src) : *src) : V(0.0f);
             }
     }
@@ -133,10 +142,11 @@ __device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, i
             inv = 1.0f / sqrtf(tot / (float)C + eps);
         }
         const bool okj = interior || s0 + j * kWave * VEC < S;
+        if (NORM && rstd && wave == 0 && okj) *reinterpret_cast<V*>(rstd + b * S + s0 + j * kWave * VEC) = inv;
 #pragma unroll
         for (int k = 0; k < CPW; ++k) {
             if (okj && (interior || c0 + k < C)) {
-                V* dst = reinterpret_cast<V*>(y + base + (int64_t)k * S + j * kWave * VEC);
+                V* dst = reinterpret_cast<V*>(y + ybase + (int64_t)k * L.ysc + j * kWave * VEC);
                 const V o = NORM ? v[k][j] * inv : v[k][j];
                 if (NORMFWD_RMS_NT_STORE)
                     st_nt(o, dst);
@@ -149,23 +159,24 @@ __device__ __forceinline__ void rms_hold_body(const float* x, float* y, int C, i
 
 template <int CPW, int PPL, int VEC>
 __global__ void __launch_bounds__(hold_max_threads(CPW * PPL))
-rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+rms_ch_hold_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps, RmsStrides L, float* rstd)
 {
-    rms_hold_body<CPW, PPL, VEC, true>(x, y, C, S, tiles, eps);
+    rms_hold_body<CPW, PPL, VEC, true>(x, y, C, S, tiles, eps, L, rstd);
 }
 
 template <int CPW, int PPL, int VEC>
 __global__ void __launch_bounds__(hold_max_threads(CPW * PPL))
-rms_copy_pattern_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+rms_copy_pattern_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps, RmsStrides L,
+                        float* rstd)
 {
-    rms_hold_body<CPW, PPL, VEC, false>(x, y, C, S, tiles, eps);
+    rms_hold_body<CPW, PPL, VEC, false>(x, y, C, S, tiles, eps, L, rstd);
 }
 
 // Streaming variant for large C: 4 waves split the channels; pass 1 sums
 // squares, pass 2 re-reads x and writes y.
 template <int VEC>
 __global__ void __launch_bounds__(256)
-rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps)
+rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, float eps, RmsStrides L, float* rstd)
 {
     using V = typename VecOf<VEC>::T;
     __shared__ V part[4][kWave];
@@ -182,7 +193,7 @@ rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, 
     V acc = V(0.0f);
     if (active) {
         for (int c = c_begin; c < c_end; ++c) {
-            V v = *reinterpret_cast<const V*>(x + (b * C + c) * S + s);
+            V v = *reinterpret_cast<const V*>(x + b * L.xsb + (int64_t)c * L.xsc + s);
             acc += v * v;
         }
     }
@@ -199,10 +210,10 @@ rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, 
         inv = 1.0f / sqrtf(tot / (float)C + eps);
     }
     if (active) {
+        if (rstd && wave == 0) *reinterpret_cast<V*>(rstd + b * S + s) = inv;
         for (int c = c_begin; c < c_end; ++c) {
-            const int64_t off = (b * C + c) * S + s;
-            V v = *reinterpret_cast<const V*>(x + off);
-            st_nt(v * inv, reinterpret_cast<V*>(y + off));
+            V v = *reinterpret_cast<const V*>(x + b * L.xsb + (int64_t)c * L.xsc + s);
+            st_nt(v * inv, reinterpret_cast<V*>(y + b * L.ysb + (int64_t)c * L.ysc + s));
         }
     }
 }
@@ -211,7 +222,7 @@ rms_ch_stream_kernel(const float* x, float* y, int C, int64_t S, int64_t tiles, 
 
 template <int CPW, int PPL, int VEC, bool NORM = true>
 static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
-                              hipStream_t st)
+                              const RmsStrides& L, float* rstd, hipStream_t st)
 {
     const int nwaves = (int)ceil_div(C, CPW);
     const int64_t tiles = ceil_div(S, (int64_t)kWave * PPL * VEC);
@@ -219,12 +230,14 @@ static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, in
     const int64_t per_launch = samples_per_launch(tiles * nwaves * kWave);
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
-        const int64_t off = b0 * C * S;
+        const float* xb = x + b0 * L.xsb;
+        float* yb = y + b0 * L.ysb;
+        float* rb = rstd ? rstd + b0 * S : nullptr;
         const hipError_t e =
             NORM ? launch_kernel((rms_ch_hold_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
-                                 dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps)
+                                 dim3(nwaves * kWave), lds, st, xb, yb, (int)C, S, tiles, eps, L, rb)
                  : launch_kernel((rms_copy_pattern_kernel<CPW, PPL, VEC>), dim3((unsigned)(nb * tiles)),
-                                 dim3(nwaves * kWave), lds, st, x + off, y + off, (int)C, S, tiles, eps);
+                                 dim3(nwaves * kWave), lds, st, xb, yb, (int)C, S, tiles, eps, L, rb);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -232,15 +245,15 @@ static hipError_t launch_hold(const float* x, float* y, int64_t B, int64_t C, in
 
 template <int VEC>
 static hipError_t launch_stream(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
-                                hipStream_t st)
+                                const RmsStrides& L, float* rstd, hipStream_t st)
 {
     const int64_t tiles = ceil_div(S, (int64_t)kWave * VEC);
     const int64_t per_launch = samples_per_launch(tiles * 256);
     for (int64_t b0 = 0; b0 < B; b0 += per_launch) {
         const int64_t nb = std::min(per_launch, B - b0);
-        const int64_t off = b0 * C * S;
         const hipError_t e = launch_kernel((rms_ch_stream_kernel<VEC>), dim3((unsigned)(nb * tiles)), dim3(256), 0,
-                                           st, x + off, y + off, (int)C, S, tiles, eps);
+                                           st, x + b0 * L.xsb, y + b0 * L.ysb, (int)C, S, tiles, eps, L,
+                                           rstd ? rstd + b0 * S : nullptr);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -248,23 +261,24 @@ static hipError_t launch_stream(const float* x, float* y, int64_t B, int64_t C, 
 
 template <int VEC>
 static hipError_t launch_vec(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
-                             hipStream_t st)
+                             const RmsStrides& L, float* rstd, hipStream_t st)
 {
     // Register-held kernel: the tuned shape when its waves fit one block,
     // 16 channels per wave (up to 16 waves) beyond that, streaming above.
     constexpr int cpw = NORMFWD_RMS_CPW, ppl = NORMFWD_RMS_PPL;
     if (ceil_div(C, cpw) * kWave <= hold_max_threads(cpw * ppl))
-        return launch_hold<cpw, ppl, VEC>(x, y, B, C, S, eps, st);
-    if (C <= 16 * 16) return launch_hold<16, 1, VEC>(x, y, B, C, S, eps, st);
-    return launch_stream<VEC>(x, y, B, C, S, eps, st);
+        return launch_hold<cpw, ppl, VEC>(x, y, B, C, S, eps, L, rstd, st);
+    if (C <= 16 * 16) return launch_hold<16, 1, VEC>(x, y, B, C, S, eps, L, rstd, st);
+    return launch_stream<VEC>(x, y, B, C, S, eps, L, rstd, st);
 }
 
-hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps,
-                         hipStream_t st)
+hipError_t launch_rms_ch(const float* x, float* y, int64_t B, int64_t C, int64_t S, float eps, const RmsStrides& L,
+                         float* rstd, hipStream_t st)
 {
-    const bool vec4 = (S % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-                      ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-    return vec4 ? launch_vec<4>(x, y, B, C, S, eps, st) : launch_vec<1>(x, y, B, C, S, eps, st);
+    auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool vec4 = S % 4 == 0 && al(x) && al(y) && (!rstd || al(rstd)) && L.xsb % 4 == 0 && L.xsc % 4 == 0 &&
+                      L.ysb % 4 == 0 && L.ysc % 4 == 0;
+    return vec4 ? launch_vec<4>(x, y, B, C, S, eps, L, rstd, st) : launch_vec<1>(x, y, B, C, S, eps, L, rstd, st);
 }
 
 // Measurement reference: rmsnorm_ch_forward's access pattern on [B, C, S]
@@ -276,7 +290,7 @@ hipError_t launch_rms_copy_pattern(const float* x, float* y, int64_t B, int64_t 
     if (S % 4 != 0 || (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 15) ||
         ceil_div(C, cpw) * kWave > hold_max_threads(cpw * ppl))
         return hipErrorInvalidValue;
-    return launch_hold<cpw, ppl, 4, false>(x, y, B, C, S, 0.0f, st);
+    return launch_hold<cpw, ppl, 4, false>(x, y, B, C, S, 0.0f, RmsStrides{C * S, S, C * S, S}, nullptr, st);
 }
 
 }  // namespace normfwd

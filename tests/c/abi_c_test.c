@@ -76,7 +76,7 @@ static int validate(void)
     void* ws = (void*)(uintptr_t)0x200000;
     fails += ln_forward(NULL, NULL, NULL, fake, 2, 8, 1e-5f, ws, 1 << 20, NULL, NULL, 0, NULL) != NORMFWD_ERR_INVALID;
     fails += ln_forward(fake, NULL, NULL, fake, 2, 8, 1e-5f, NULL, 1 << 20, NULL, NULL, 0, NULL) != NORMFWD_ERR_WORKSPACE;
-    fails += gn_lrelu_x2_forward(fake, NULL, NULL, fake, 4, 10, 3, 1e-5f, 0.01f, NULL) != NORMFWD_ERR_INVALID;
+    fails += gn_lrelu_x2_forward(fake, NULL, NULL, fake, 4, 10, 3, 1e-5f, 0.01f, NULL, NULL, NULL) != NORMFWD_ERR_INVALID;
     fails += rmsnorm_ch_forward(fake, fake, 2, 0, 4, 1e-5f, NULL) != NORMFWD_ERR_INVALID;
     fails += strlen(normfwd_last_error()) == 0;
     fails += strcmp(normfwd_status_string(NORMFWD_OK), "NORMFWD_OK") != 0;
@@ -131,7 +131,7 @@ static int run(void)
         float *dx = to_device(x, n), *dg = to_device(g, (size_t)C), *db = to_device(b, (size_t)C);
         float* dy = to_device(NULL, n);
         if (!dx || !dg || !db || !dy) return 2;
-        if (gn_lrelu_x2_forward(dx, dg, db, dy, N, C, G, 1e-5f, 0.01f, st) != NORMFWD_OK) return 3;
+        if (gn_lrelu_x2_forward(dx, dg, db, dy, N, C, G, 1e-5f, 0.01f, NULL, NULL, st) != NORMFWD_OK) return 3;
         hipStreamSynchronize(st);
         hipMemcpy(y, dy, n * sizeof(float), hipMemcpyDeviceToHost);
         double *xd = promote(x, n), *gd = promote(g, (size_t)C), *bd = promote(b, (size_t)C);

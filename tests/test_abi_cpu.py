@@ -94,13 +94,13 @@ def test_ln_workspace_size_monotone():
 
 def test_gn_validation():
     lib = _lib.lib()
-    st, msg = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 10, 3, 1e-5, 0.01, None))
+    st, msg = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 10, 3, 1e-5, 0.01, None, None, None))
     assert st == 1 and "multiple" in msg
-    st, _ = _err(lib.gn_lrelu_x2_forward(None, None, None, FAKE, 4, 12, 3, 1e-5, 0.01, None))
+    st, _ = _err(lib.gn_lrelu_x2_forward(None, None, None, FAKE, 4, 12, 3, 1e-5, 0.01, None, None, None))
     assert st == 1
-    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, -1, 12, 3, 1e-5, 0.01, None))
+    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, -1, 12, 3, 1e-5, 0.01, None, None, None))
     assert st == 1
-    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 12, 0, 1e-5, 0.01, None))
+    st, _ = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 12, 0, 1e-5, 0.01, None, None, None))
     assert st == 1
 
 
@@ -128,7 +128,7 @@ def test_documented_size_limits_are_refused():
     assert ln(1 << 12, 1 << 29) == 2          # elements per tensor (2^41 > 2^40)
 
     def gn(N, C, G):
-        return _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, N, C, G, 1e-5, 0.01, None))[0]
+        return _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, N, C, G, 1e-5, 0.01, None, None, None))[0]
 
     assert gn(1, 1 << 31, 1) == 2             # channels
     assert gn(1 << 12, 1 << 29, 1 << 20) == 2  # elements per tensor
@@ -142,7 +142,7 @@ def test_documented_size_limits_are_refused():
 
     def fc(N, K, C, G):
         return _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, N, K, C, G, 1e-5, 0.01, FAKE_WS, big_ws,
-                                      None))[0]
+                                      None, None, None))[0]
 
     assert fc((1 << 23) + 1, 16, 64, 4) == 2  # rows
     assert fc(64, 16, (1 << 24) + 16, 16) == 2  # output channels
@@ -153,14 +153,20 @@ def test_fc_validation():
     need = lib.fc_gn_forward_workspace_size(1024, 8192, 8192)
     assert need == 1024 * 8192 * 4
     st, _ = _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, 1024, 8192, 8192, 500, 1e-5, 0.01, FAKE_WS,
-                                   need, None))
+                                   need, None, None, None))
     assert st == 1
     st, _ = _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, 1024, 8192, 8192, 512, 1e-5, 0.01, FAKE_WS,
-                                   need - 4, None))
+                                   need - 4, None, None, None))
     assert st == 3
     st, _ = _err(lib.fc_gn_forward(FAKE, None, None, None, None, FAKE, 1024, 8192, 8192, 512, 1e-5, 0.01, FAKE_WS,
-                                   need, None))
+                                   need, None, None, None))
     assert st == 1
+    # statistics: both outputs or neither
+    st, msg = _err(lib.fc_gn_forward(FAKE, FAKE, None, None, None, FAKE, 1024, 8192, 8192, 512, 1e-5, 0.01,
+                                     FAKE_WS, need, FAKE, None, None))
+    assert st == 1 and "both" in msg
+    st, msg = _err(lib.gn_lrelu_x2_forward(FAKE, None, None, FAKE, 4, 12, 3, 1e-5, 0.01, None, FAKE, None))
+    assert st == 1 and "both" in msg
 
 
 def test_empty_work_is_a_no_op_that_touches_nothing():
@@ -172,12 +178,12 @@ def test_empty_work_is_a_no_op_that_touches_nothing():
     assert lib.ln_forward(None, None, None, None, 0, 4096, 1e-5, None, 0, None, None, 4, None) != 0
     assert lib.ln_forward_stats(None, 0, 4096, 1e-5, None, 0, None, None, None) == 0
     assert lib.ln_forward_apply(None, None, None, None, 0, 4096, None, 0, None) == 0
-    assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 8192, 512, 1e-5, 0.01, None) == 0
+    assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 8192, 512, 1e-5, 0.01, None, None, None) == 0
     assert lib.rmsnorm_ch_forward(None, None, 0, 64, 1024, 1e-5, None) == 0
     assert lib.rmsnorm_ch_forward(None, None, 3, 64, 0, 1e-5, None) == 0
-    assert lib.fc_gn_forward(None, None, None, None, None, None, 0, 64, 128, 8, 1e-5, 0.01, None, 0, None) == 0
+    assert lib.fc_gn_forward(None, None, None, None, None, None, 0, 64, 128, 8, 1e-5, 0.01, None, 0, None, None, None) == 0
     # still invalid: a bad group count or a negative size
-    assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 100, 7, 1e-5, 0.01, None) == 1
+    assert lib.gn_lrelu_x2_forward(None, None, None, None, 0, 100, 7, 1e-5, 0.01, None, None, None) == 1
     assert lib.rmsnorm_ch_forward(None, None, -1, 64, 1024, 1e-5, None) == 1
 
 
@@ -195,3 +201,24 @@ def test_ln_noalloc_validation():
     st, msg = _err(lib.ln_forward_noalloc(FAKE, None, None, FAKE, 1024, 1 << 20, 1e-5, None, None, 3, None))
     assert st == 2 and "scratch" in msg
     assert lib.ln_forward_noalloc(FAKE, None, None, FAKE, 0, 8, 1e-5, None, None, 3, None) == 0  # empty batch
+
+
+def test_rms_strided_validation():
+    """rmsnorm_ch_forward_strided refuses, before touching the device: negative strides, views that span
+    2^40 elements, and y strides under which two of y's rows overlap."""
+    lib = _lib.lib()
+    f = lib.rmsnorm_ch_forward_strided
+    st, _ = _err(f(None, FAKE, 2, 3, 4, 12, 4, 12, 4, 1e-5, None, None))
+    assert st == 1
+    st, _ = _err(f(FAKE, FAKE, 2, 3, 4, -12, 4, 12, 4, 1e-5, None, None))
+    assert st == 2
+    st, _ = _err(f(FAKE, FAKE, 2, 3, 4, 12, 4, 12, 3, 1e-5, None, None))  # y's channel rows overlap
+    assert st == 1
+    st, _ = _err(f(FAKE, FAKE, 2, 3, 4, 12, 4, 8, 4, 1e-5, None, None))   # y's samples overlap
+    assert st == 1
+    st, _ = _err(f(FAKE, FAKE, 2, 3, 4, 1 << 40, 4, 12, 4, 1e-5, None, None))  # x spans over 2^40
+    assert st == 2
+    st, _ = _err(f(FAKE, FAKE, 2, 3, 4, 12, 4, 12, 4, -1.0, None, None))
+    assert st == 1
+    assert f(None, None, 0, 3, 4, 12, 4, 12, 4, 1e-5, None, None) == 0  # no positions
+
