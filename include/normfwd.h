@@ -137,7 +137,11 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 sample's partial merges it and announces the statistics
  *                 with a flag (LN page, turn 6: last-block-done), the others
  *                 waiting for that flag.  A cooperative launch, since its
- *                 waits need every workgroup resident.
+ *                 waits need every workgroup resident.  The runtime grants
+ *                 cooperative launches on a GPU to one process at a time:
+ *                 after another, still running process has made one, this
+ *                 variant returns NORMFWD_ERR_UNSUPPORTED and launches
+ *                 nothing.
  *             3 = automatic: variant 1 wherever it can run (it measured
  *                 faster than the split, or within 1 us of it on calls of
  *                 ~10 us, at every shape tried), otherwise variant 0 (also

@@ -119,10 +119,21 @@ normfwd_status ln_dispatch(const float* x, const float* weight, const float* bia
     if (normfwd::launch_ln_rows(x, weight, bias, y, outer, inner, eps, mean_out, rstd_out, st, re))
         return hip_status(re, "ln_forward (one workgroup per sample) launch");
     if (variant == 3) variant = normfwd::ln_auto_variant(x, weight, bias, y, outer, inner);
-    if (variant != 0)
-        return hip_status(normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay, mean_out,
-                                                    rstd_out, variant, st),
-                          "ln_forward (single kernel) launch");
+    if (variant != 0) {
+        const hipError_t e = normfwd::launch_ln_single(x, weight, bias, y, outer, inner, eps, workspace, lay,
+                                                       mean_out, rstd_out, variant, st);
+        // The runtime grants cooperative launches on a GPU to one process
+        // at a time: once a process has made one, the same launch from
+        // another process is refused until the first process exits
+        // (measured on MI355X: the refused launch returns
+        // hipErrorIllegalState; the first process keeps launching).
+        if (e == hipErrorIllegalState)
+            return fail(NORMFWD_ERR_UNSUPPORTED,
+                        "ln_forward: the cooperative launch of the last-workgroup-merges kernel was refused "
+                        "(hipErrorIllegalState): another process that is still running has made a cooperative "
+                        "launch on this GPU; variants 0, 1 and 3 do not use one");
+        return hip_status(e, "ln_forward (single kernel) launch");
+    }
     hipError_t e = normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out, st);
     if (e != hipSuccess) return hip_status(e, "ln_forward stats launch");
     return hip_status(normfwd::launch_ln_apply(x, weight, bias, y, outer, inner, workspace, lay, st),

@@ -13,6 +13,8 @@ normalizations, independently of ``oracle/oracle.c``:
   per-channel affine, LeakyReLU, doubling.
 * RMSNorm along dim 1 (RMS page "Kimi-K2.6 l1_p36", turns 1-2):
   x / sqrt(mean over channels of x^2 + eps).
+* fc -> GroupNorm -> LeakyReLU -> x + x (GN page, turn 1): h = x W^T + b as
+  exact rationals, then the GroupNorm epilogue above on the exact h.
 """
 from decimal import Decimal, getcontext
 from fractions import Fraction
@@ -72,3 +74,38 @@ def rms_position(vals, eps):
     ms = sum((v * v for v in xs), Fraction(0)) / len(xs)
     denom = _dec(ms + _fr(eps)).sqrt()
     return [_dec(v) / denom for v in xs], ms
+
+
+def _group_epilogue(hs, gamma, beta, G, eps, slope):
+    """GroupNorm -> LeakyReLU -> x + x of one row given as exact rationals."""
+    C = len(hs)
+    M = C // G
+    out = []
+    for g in range(G):
+        seg = hs[g * M:(g + 1) * M]
+        mean = sum(seg, Fraction(0)) / M
+        var = sum(((v - mean) ** 2 for v in seg), Fraction(0)) / M
+        denom = _dec(var + _fr(eps)).sqrt()
+        for j in range(M):
+            c = g * M + j
+            v = _dec(seg[j] - mean) / denom
+            if gamma is not None:
+                v = v * _dec(_fr(gamma[c]))
+            if beta is not None:
+                v = v + _dec(_fr(beta[c]))
+            a = v if v > 0 else _dec(_fr(slope)) * v
+            out.append(a + a)
+    return out
+
+
+def fc_group_norm_lrelu_x2(x_row, W, bias, gamma, beta, G, eps, slope):
+    """One row of x [K] through h = x W^T + b (W [C, K]), exact, then the GroupNorm epilogue: the C
+    outputs as Decimal."""
+    xs = [_fr(v) for v in x_row]
+    hs = []
+    for c in range(len(W)):
+        acc = sum((xs[k] * _fr(W[c][k]) for k in range(len(xs))), Fraction(0))
+        if bias is not None:
+            acc += _fr(bias[c])
+        hs.append(acc)
+    return _group_epilogue(hs, gamma, beta, G, eps, slope)

@@ -89,6 +89,26 @@ def pin_fc_numpy(orc, seed=3):
         np.testing.assert_allclose(h, want, rtol=1e-13, atol=1e-13)
 
 
+def pin_fc_gn_bruteforce(orc, seed=10):
+    """fc -> GroupNorm -> LeakyReLU -> x2 of tiny problems == exact rationals (GN page, turn 1).  eps and
+    negative_slope differ enough that exchanging them changes the result, and the inputs carry enough
+    bits that rounding h to fp32 before the GroupNorm would too."""
+    rng = np.random.default_rng(seed)
+    for N, K, C, G, eps, slope in [(2, 5, 8, 2, 0.3, 0.05), (1, 7, 6, 3, 1e-5, 0.2), (2, 3, 4, 1, 2.0, 0.01)]:
+        x = (rng.standard_normal((N, K)) * 3.0).astype(np.float32)
+        W = rng.uniform(-1, 1, (C, K)).astype(np.float32)
+        b = (rng.uniform(-1, 1, C) + 20.0).astype(np.float32)
+        gamma = (1.0 + 0.5 * rng.standard_normal(C)).astype(np.float32)
+        beta = (0.5 * rng.standard_normal(C)).astype(np.float32)
+        y = orc.fc_gn_lrelu_x2(x, W, b, gamma, beta, G, eps=eps, negative_slope=slope)
+        for n in range(N):
+            ey = exact.fc_group_norm_lrelu_x2(x[n], W, b, gamma, beta, G, float(np.float32(eps)),
+                                              float(np.float32(slope)))
+            for c in range(C):
+                _close(y[n, c], float(ey[c]), 1e-12)
+        assert (y < 0).any() and (y > 0).any()
+
+
 # ------------------------------------------------------- closed forms, invariants
 
 def pin_ln_closed_forms(orc, seed=4):
@@ -193,7 +213,7 @@ def pin_rms_closed_forms(orc, seed=9):
 
 
 ALL_PINS = [
-    pin_ln_bruteforce, pin_gn_bruteforce, pin_rms_bruteforce, pin_fc_numpy,
+    pin_ln_bruteforce, pin_gn_bruteforce, pin_rms_bruteforce, pin_fc_numpy, pin_fc_gn_bruteforce,
     pin_ln_closed_forms, pin_ln_special_cases, pin_ln_uniform_moments, pin_ln_cancellation,
     pin_gn_special_cases, pin_rms_closed_forms,
 ]

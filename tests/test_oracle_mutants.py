@@ -67,3 +67,35 @@ def test_pins_reject_mutant(name, tmp_path):
         except AssertionError:
             failures.append(pin.__name__)
     assert failures, f"no pin caught mutant {name}"
+
+
+# The fc -> GroupNorm composition lives in oracle/__init__.py (Python), so its mutants are subclasses of
+# the oracle that compose the two C functions the wrong way.
+class _SwappedEpsSlope(oracle.Oracle):
+    def fc_gn_lrelu_x2(self, x, W, bias, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01):
+        return self.gn_lrelu_x2(self.fc(x, W, bias), gamma, beta, num_groups, negative_slope, eps)
+
+
+class _RoundedH(oracle.Oracle):
+    def fc_gn_lrelu_x2(self, x, W, bias, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01):
+        h = self.fc(x, W, bias).astype("float32")
+        return self.gn_lrelu_x2(h, gamma, beta, num_groups, eps, negative_slope)
+
+
+class _GroupSizeForCount(oracle.Oracle):
+    def fc_gn_lrelu_x2(self, x, W, bias, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01):
+        h = self.fc(x, W, bias)
+        return self.gn_lrelu_x2(h, gamma, beta, h.shape[1] // num_groups, eps, negative_slope)
+
+
+class _NoBias(oracle.Oracle):
+    def fc_gn_lrelu_x2(self, x, W, bias, gamma, beta, num_groups, eps=1e-5, negative_slope=0.01):
+        return self.gn_lrelu_x2(self.fc(x, W, None), gamma, beta, num_groups, eps, negative_slope)
+
+
+@pytest.mark.parametrize("cls", [_SwappedEpsSlope, _RoundedH, _GroupSizeForCount, _NoBias],
+                         ids=lambda c: c.__name__)
+def test_fc_gn_pin_rejects_composition_mutant(cls):
+    orc = cls(obuild.LIB if os.path.exists(obuild.LIB) else obuild.build())
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_fc_gn_bruteforce(orc)
