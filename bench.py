@@ -150,7 +150,8 @@ def main():
         # (x + y + weight + bias).  Variant 1 is an ordinary launch that stamps the armed events itself
         # (kernel start to end); variant 2's cooperative launch cannot, so there the events bracket each
         # launch and its duration includes the cooperative launch's own cost.
-        dom_kernel = "ln_single_ctl_kernel" if variant == 1 else "ln_single_hold_kernel"
+        # (variant 2 runs ln_single_ctl_kernel with its last-workgroup-merges control wave at this shape)
+        dom_kernel = "ln_single_ctl_kernel"
         dom_bytes, avg_ms, med_ms = LN_NORMALIZE_BYTES, t["kernel_ms"], t["kernel_ms_median"]
     else:
         # the step is the two halves of the split schedule

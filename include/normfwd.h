@@ -136,7 +136,9 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *             2 = single kernel in which the last workgroup to deliver a
  *                 sample's partial merges it and announces the statistics
  *                 with a flag (LN page, turn 6: last-block-done), the others
- *                 waiting for that flag.  A cooperative launch, since its
+ *                 waiting for that flag (a control wave per workgroup does
+ *                 the exchange beside the data waves of variant 1, which
+ *                 read x once; in place is fine).  A cooperative launch, since its
  *                 waits need every workgroup resident.  The runtime grants
  *                 cooperative launches on a GPU to one process at a time:
  *                 after another, still running process has made one, this

@@ -48,10 +48,12 @@
 //          moments that do not arrive within a bounded wait (their workgroup
 //          is not resident) are computed by the reader from x, with the same
 //          bits (so it never runs in place: y == x takes the split);
-//          ln_single_hold_kernel (variant 2, a cooperative launch): the
-//          last workgroup to deliver a sample's partial merges it and
-//          announces the statistics with a flag (LN page, turn 6:
-//          last-block-done).
+//          variant 2 (a cooperative launch): the last workgroup to deliver
+//          a sample's partial merges it and announces the statistics with a
+//          flag (LN page, turn 6: last-block-done), done by the control
+//          wave of ln_single_ctl_kernel (ctl_wave_last_block) beside the
+//          same data waves, or for shapes that tile cannot hold by
+//          ln_single_hold_kernel, whose waves hold data and wait both.
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
 //          shape, from measurements (the split in place).
 //   short samples (inner <= 8192): ln_row_kernel, one workgroup per sample.
@@ -1045,10 +1047,80 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // With LAG = 2 every workgroup has had a whole iteration to publish the
 // moments the control wave gathers, so the gather rarely waits and the data
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
-// counters or flags.  (The last-workgroup-merges protocol of
-// ln_single_hold_kernel measured slower here: its chain of arrival atomic,
-// merge and flag is longer than one sample's streaming time.)
+// counters or flags.  (The last-workgroup-merges exchange beside the same
+// data waves, ctl_wave_last_block below, measured 166-167 us per call
+// against 99-100 us at [16, 4M]: its chain per sample, drain, arrival
+// atomic, the last arrival's merge, flag and the readers' poll, is longer
+// than one sample's streaming time; counting arrivals in two levels, or
+// tagged statistics words in place of the flag, did not shorten it.)
 //
+// Control wave of ln_single_ctl_kernel with the last-workgroup-merges
+// exchange (LN page, turn 6: last-block-done), for ln_forward variant 2, a
+// cooperative launch (its waits need every workgroup resident; each wait
+// has a spin limit that sets the control block's error word instead of
+// hanging).  The data waves are those of the tagged exchange, unchanged, so
+// they never wait on another workgroup.  After barrier t:
+//   merge the data waves' moments of sample t into this workgroup's (n,
+//   mean, M2) (merge_wave_moments), publish it in its partial slot, drain
+//   the stores and count the arrival on the sample's counter (a ring of
+//   kRing); the last of the P arrivals merges the sample's partials in a
+//   fixed order (wave_merge, one wave), stores the statistics, puts the
+//   counter back to 0 and announces the sample with its flag (= the launch
+//   generation);
+//   then wait for the flag of sample t - LAG + 1 and leave its statistics in
+//   LDS before barrier t + 1 (they are normalized after barrier t + 2).
+// The last workgroup out advances the generation.
+template <int DW, int LAG>
+__device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t* cnt, const double* cnt_inv,
+                                    f4* s_stats, int64_t outer, int64_t P, int64_t P_cap, int64_t p,
+                                    uint32_t n_mine, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag,
+                                    Partial* parts, f4* stats, float* mean_out, float* rstd_out)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t target = dev_load(&ctrl->gen) + 1u;
+    const double inv_mine = inv_count_f64(n_mine);
+    const int64_t steps = outer + LAG;
+    __syncthreads();  // prologue: w/b in LDS
+    for (int64_t t = 0; t < steps; ++t) {
+        __syncthreads();  // barrier t: the wave moments of sample t are in LDS
+        if (t < outer) {
+            Partial q{};
+            q.n = (double)n_mine;
+            merge_wave_moments<DW>(red[t & 1], cnt, cnt_inv, inv_mine, q.mean, q.m2);
+            uint32_t* counter = counters + (t % kRing) * kCounterStride;
+            uint32_t last = 0;
+            if (lane == 0) last = deliver_partial(parts + t * P_cap + p, q, counter, P) ? 1u : 0u;
+            if (__builtin_amdgcn_readfirstlane(last)) {
+                double n, m, m2;
+                wave_merge<true>(parts + t * P_cap, P, n, m, m2);
+                if (lane == 0) {
+                    const f4 st = finish_stats(n, m, m2, eps);
+                    float* sp = reinterpret_cast<float*>(stats + t);
+                    dev_store(sp + 0, st.x);
+                    dev_store(sp + 1, st.y);
+                    dev_store(sp + 2, st.z);
+                    if (mean_out) mean_out[t] = st.x;
+                    if (rstd_out) rstd_out[t] = st.z;
+                    dev_store(counter, 0u);
+                    vmem_drain();
+                    dev_store(&flag[t], target);
+                }
+            }
+        }
+        const int64_t g = t - (LAG - 1);
+        if (g >= 0 && g < outer && lane == 0) s_stats[g & 1] = await_stats(flag, stats, g, target, ctrl);
+    }
+    // completion: the last workgroup out advances the generation
+    if (lane == 0) {
+        vmem_drain();
+        if (__hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1)) {
+            dev_store(&ctrl->done, 0u);
+            vmem_drain();
+            dev_store(&ctrl->gen, target);
+        }
+    }
+}
+
 // Iterations of ln_single_ctl_kernel with compile-time tile indices:
 // ctl_first_steps runs iterations 0 .. LAG-1 (moments only); ctl_steps runs
 // t0 + U, t0 + U + 1, ... for U < NT (iteration t uses tile (t0 + U) % NT,
@@ -1074,11 +1146,12 @@ __device__ __forceinline__ bool ctl_steps(int64_t t0, int64_t steps, F& f)
     }
 }
 
-template <int F4PT, int DW, int LAG>
+template <int F4PT, int DW, int LAG, int PROTO>
 __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, float* y_all, int64_t outer_all,
                      int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, double* xchg_all,
-                     float* mean_all, float* rstd_all, int64_t groups, uint32_t spin_limit, uint32_t silent_mask)
+                     float* mean_all, float* rstd_all, int64_t groups, uint32_t spin_limit, uint32_t silent_mask,
+                     uint32_t* counters, uint32_t* flag, Partial* parts)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
@@ -1119,6 +1192,18 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     const int64_t nv = inner / 4;
     const int64_t steps = outer + LAG;  // iterations = barriers after the prologue
 
+    if (tid >= RW && PROTO == 1) {
+        // ---- control wave, last workgroup merges (groups == 1)
+        if (lane < DW) {
+            const uint32_t n = ctl_wave_elems<F4PT, DW>((uint32_t)p, lane, (uint32_t)P, nv);
+            cnt[0][lane] = n;
+            cnt_inv[0][lane] = inv_count_f64(n);
+        }
+        const uint32_t n_mine = ctl_wg_elems<F4PT, DW>((uint32_t)p, (uint32_t)P, nv);
+        ctl_wave_last_block<DW, LAG>(red, cnt[0], cnt_inv[0], s_stats, outer, P, P_cap, p, n_mine, eps, ctrl,
+                                     counters, flag, parts, stats, mean_out, rstd_out);
+        return;
+    }
     if (tid >= RW) {
         // ---- control wave
         const uint32_t gen_target = ln_next_generation(dev_load(&ctrl->gen_ctl));
@@ -1546,7 +1631,7 @@ static int coresident(const void* fn, size_t lds, int threads)
 #endif
 
 
-template <int F4PT, int DW>
+template <int F4PT, int DW, int PROTO = 0>
 static bool try_launch_hold(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner,
                             float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats, Partial* parts,
                             double* xchg, int64_t P_cap, float* mean_out, float* rstd_out, hipStream_t st,
@@ -1555,7 +1640,9 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     DeviceInfo d;
     if (!device_info(d)) return false;
     // DW == 0: ln_single_hold_kernel (rows of kLnThreads float4, every wave
-    // does both jobs); DW > 0: ln_single_ctl_kernel with DW data waves
+    // does both jobs); DW > 0: ln_single_ctl_kernel with DW data waves and
+    // the tagged exchange (PROTO 0, an ordinary launch) or the last
+    // workgroup merging (PROTO 1, a cooperative launch)
     const int64_t rw = DW == 0 ? kLnThreads : DW * kWave;
     const int64_t rows = ceil_div(inner / 4, rw);
     const int64_t P = ceil_div(rows, (int64_t)F4PT);
@@ -1570,12 +1657,12 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
     if constexpr (DW == 0)
         fn = reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>);
     else
-        fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>);
+        fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, PROTO>);
     const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
     const int cap = coresident(fn, lds_max, threads);
     if (cap < P) return false;
     int64_t pcap = P_cap;
-    if constexpr (DW > 0) {
+    if constexpr (DW > 0 && PROTO == 0) {
         // An ordinary launch (a cooperative one costs ~17 us more per call on
         // MI355X).  The grid fits the device, so normally every workgroup is
         // resident at once; when one is not (another kernel holds its CU), the
@@ -1592,18 +1679,29 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
         // as many groups of P workgroups (each taking every groups-th
         // sample) as stay co-resident, at most one per sample
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
-        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG>, dim3((unsigned)(groups * P)),
+        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, 0>, dim3((unsigned)(groups * P)),
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
-                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force);
+                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, flag, parts);
         return true;
     }
-    void* args[] = {(void*)&x,     (void*)&w,       (void*)&b,    (void*)&y,     (void*)&outer,
-                    (void*)&inner, (void*)&pcap,    (void*)&eps,  (void*)&ctrl,  (void*)&counters,
-                    (void*)&flag,  (void*)&stats,   (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
     // a cooperative launch cannot carry events: armed ones bracket it as markers
     const LaunchEvents ev = take_launch_events();
     if (ev.start) (void)hipEventRecord(ev.start, st);
-    err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
+    if constexpr (DW == 0) {
+        void* args[] = {(void*)&x,     (void*)&w,     (void*)&b,     (void*)&y,        (void*)&outer,
+                        (void*)&inner, (void*)&pcap,  (void*)&eps,   (void*)&ctrl,     (void*)&counters,
+                        (void*)&flag,  (void*)&stats, (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
+        err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
+    } else {
+        // one group of P workgroups; the tagged exchange's arguments are unused
+        int64_t groups = 1;
+        uint32_t spin = kSpinLimit, force = 0xFFFFFFFFu;
+        void* args[] = {(void*)&x,        (void*)&w,        (void*)&b,        (void*)&y,      (void*)&outer,
+                        (void*)&inner,    (void*)&pcap,     (void*)&eps,      (void*)&ctrl,   (void*)&stats,
+                        (void*)&xchg,     (void*)&mean_out, (void*)&rstd_out, (void*)&groups, (void*)&spin,
+                        (void*)&force,    (void*)&counters, (void*)&flag,     (void*)&parts};
+        err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
+    }
     if (err == hipSuccess) err = hipGetLastError();
     if (err == hipSuccess && ev.stop) err = hipEventRecord(ev.stop, st);
     return true;
@@ -1632,7 +1730,7 @@ int ln_auto_variant(const float* x, const float* w, const float* b, const float*
     if (!ln_single_supported(inner, x, w, b, y) || x == y) return 0;
     const int64_t P = ceil_div(ceil_div(inner / 4, (int64_t)8 * kWave), (int64_t)8);
     const size_t lds = (size_t)2 * 8 * 8 * kWave * sizeof(f4);
-    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG>);
+    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG, 0>);
     return coresident(fn, lds, 9 * kWave) >= P ? 1 : 0;
 }
 
@@ -1653,15 +1751,19 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     // (in place the control-wave kernel does not run and variant 1 takes the split)
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
-#define NORMFWD_TRY_HOLD(F, DW)                                                                                \
-    if (try_launch_hold<F, DW>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, xchg, lay.P_cap, \
-                               mean_out, rstd_out, st, err))                                                      \
+#define NORMFWD_TRY_HOLD(F, DW, ...)                                                                           \
+    if (try_launch_hold<F, DW, ##__VA_ARGS__>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts,  \
+                                              xchg, lay.P_cap, mean_out, rstd_out, st, err))                      \
         return err;
         if (protocol == 1) {  // control wave, tagged gather
             NORMFWD_TRY_HOLD(8, 8)
             NORMFWD_TRY_HOLD(4, 8)
         }
-        // last workgroup merges (protocol 2, or shapes the above cannot hold)
+        // last workgroup merges (protocol 2, or shapes the above cannot hold):
+        // the control-wave kernel with that exchange, then the all-purpose waves
+        if (protocol == 2) {
+            NORMFWD_TRY_HOLD(8, 8, 1)
+        }
         NORMFWD_TRY_HOLD(NORMFWD_LN_HOLD_F4PT, 0)
         NORMFWD_TRY_HOLD(4, 0)
         NORMFWD_TRY_HOLD(8, 0)
