@@ -99,9 +99,10 @@ hipError_t launch_ln_apply(const float* x, const float* w, const float* b, float
 // 8192 with 128-bit access, <= 2048 otherwise); false if it does not.
 bool launch_ln_rows(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner, float eps,
                     float* mean_out, float* rstd_out, hipStream_t st, hipError_t& err);
-// protocol 1: ln_single_ctl_kernel (control wave, generation-tagged gather);
-// 2: ln_single_hold_kernel (the last workgroup of a sample merges it).
-// Shapes neither kernel can hold run the split schedule.
+// ln_single_ctl_kernel with its control wave running protocol 1 (the
+// generation-tagged gather, an ordinary launch) or 2 (the last workgroup of
+// a sample merges it, a cooperative launch).  Shapes the kernel cannot hold
+// run the split schedule.
 hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                             int64_t inner, float eps, void* ws, const LnLayout& lay, float* mean_out,
                             float* rstd_out, int protocol, hipStream_t st);

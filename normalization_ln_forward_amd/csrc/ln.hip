@@ -52,8 +52,9 @@
 //          a sample's partial merges it and announces the statistics with a
 //          flag (LN page, turn 6: last-block-done), done by the control
 //          wave of ln_single_ctl_kernel (ctl_wave_last_block) beside the
-//          same data waves, or for shapes that tile cannot hold by
-//          ln_single_hold_kernel, whose waves hold data and wait both.
+//          same data waves.
+//          Samples too large for the kernel's co-resident grid take the
+//          split under every variant.
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
 //          shape, from measurements (the split in place).
 //   short samples (inner <= 8192): ln_row_kernel, one workgroup per sample.
@@ -270,36 +271,6 @@ __device__ __forceinline__ bool deliver_partial(Partial* part, const Partial& v,
     dev_store(&part->m2, v.m2);
     vmem_drain();
     return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1);
-}
-
-// Merge parts[0, P) in a fixed order: thread t folds partials t, t + 256,
-// ..., then a fixed tree over the threads.  The result is valid in thread 0.
-// The partials were written by other workgroups of the same launch, so they
-// are read with device-coherent loads.  lds: 3 * 256 doubles.
-__device__ void merge_partials(const Partial* parts, int64_t P, double* lds, double& n, double& m, double& m2)
-{
-    n = 0.0;
-    m = 0.0;
-    m2 = 0.0;
-    for (int64_t j = threadIdx.x; j < P; j += kLnThreads)
-        chan_merge(n, m, m2, dev_load(&parts[j].n), dev_load(&parts[j].mean), dev_load(&parts[j].m2));
-    double* ln_ = lds;
-    double* lm = lds + kLnThreads;
-    double* lm2 = lds + 2 * kLnThreads;
-    __syncthreads();
-    ln_[threadIdx.x] = n;
-    lm[threadIdx.x] = m;
-    lm2[threadIdx.x] = m2;
-    __syncthreads();
-    for (int stride = kLnThreads / 2; stride > 0; stride >>= 1) {
-        if ((int)threadIdx.x < stride) {
-            chan_merge(n, m, m2, ln_[threadIdx.x + stride], lm[threadIdx.x + stride], lm2[threadIdx.x + stride]);
-            ln_[threadIdx.x] = n;
-            lm[threadIdx.x] = m;
-            lm2[threadIdx.x] = m2;
-        }
-        __syncthreads();
-    }
 }
 
 // (mean hi, mean lo, rstd) of a merged sample.
@@ -788,28 +759,6 @@ __device__ __forceinline__ void merge_wave_moments(const double* rd, const uint3
     m2 = fmax(B - A * md, 0.0);
 }
 
-// Last arriver of sample t in the single kernel: merge its partials, store
-// the statistics, reset the sample's counter and announce flag[t] = target.
-__device__ void merge_and_announce(const Partial* parts, int64_t P, float eps, double* lds, f4* stats_t,
-                                   float* mean_out_t, float* rstd_out_t, uint32_t* counter, uint32_t* flag,
-                                   int64_t t, uint32_t target)
-{
-    double n, m, m2;
-    merge_partials(parts, P, lds, n, m, m2);
-    if (threadIdx.x == 0) {
-        const f4 st = finish_stats(n, m, m2, eps);
-        float* sp = reinterpret_cast<float*>(stats_t);
-        dev_store(sp + 0, st.x);
-        dev_store(sp + 1, st.y);
-        dev_store(sp + 2, st.z);
-        if (mean_out_t) *mean_out_t = st.x;
-        if (rstd_out_t) *rstd_out_t = st.z;
-        dev_store(counter, 0u);
-        vmem_drain();
-        dev_store(&flag[t], target);
-    }
-}
-
 // Wait for flag[t] == target and return sample t's statistics (thread 0
 // only).  A spin limit turns a wait that cannot end into an error flag
 // instead of a hang.
@@ -826,144 +775,6 @@ __device__ __forceinline__ f4 await_stats(const uint32_t* flag, const f4* stats,
     }
     const float* sp = reinterpret_cast<const float*>(stats + t);
     return f4{dev_load(sp + 0), dev_load(sp + 1), dev_load(sp + 2), 0.0f};
-}
-
-// Single-read schedule (one cooperative launch; LN page, turn 6 proposes
-// finishing the reduction in the last block to arrive).  Workgroup p owns
-// rows p, p + P, p + 2P, ... of 256 float4 in every sample (the interleaved
-// order that keeps the loads in flight dense), keeps its rows of x in VGPRs
-// (F4PT float4 per thread) from the moments pass to the normalize pass, so
-// x crosses HBM once, and keeps its rows of weight and bias in LDS for all
-// samples.  The pipeline runs one sample behind: iteration t delivers the
-// moments of sample t, issues the loads of sample t+1, then waits for the
-// statistics of sample t-1 (announced one iteration earlier, so normally
-// already there) and normalizes it.  Three register tiles are live.
-template <int F4PT>
-__global__ void __launch_bounds__(kLnThreads)
-ln_single_hold_kernel(const float* x, const float* w, const float* bias, float* y, int64_t outer, int64_t inner,
-                      int64_t P_cap, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats,
-                      Partial* parts, float* mean_out, float* rstd_out)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    __shared__ double lds[3 * kLnThreads];
-    __shared__ double red[3 * (kLnThreads / kWave)];  // [wave]: t1, t2, shift
-    __shared__ uint32_t cnt[kLnThreads / kWave];      // [wave]: elements it holds
-    __shared__ double cnt_inv[kLnThreads / kWave];    // [wave]: 1 / cnt
-    __shared__ int s_last;
-    __shared__ f4 s_stats;
-    f4* w_s = reinterpret_cast<f4*>(smem_raw);
-    f4* b_s = w_s + (w ? F4PT * kLnThreads : 0);
-    const int64_t P = gridDim.x;
-    const int64_t p = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int64_t nv = inner / 4;
-    const int64_t rows = ceil_div(nv, (int64_t)kLnThreads);
-    const uint32_t target = dev_load(&ctrl->gen) + 1u;
-
-    auto index = [&](int k) -> int64_t { return (p + (int64_t)k * P) * kLnThreads + tid; };
-    auto valid = [&](int k) -> bool { return p + (int64_t)k * P < rows && index(k) < nv; };
-
-    // weight / bias rows -> LDS: all loads in flight first, then the LDS stores
-    f4 prev[F4PT], cur[F4PT], nxt[F4PT];
-    for (int which = 0; which < 2; ++which) {
-        const float* src = which == 0 ? w : bias;
-        f4* dst = which == 0 ? w_s : b_s;
-        if (!src) continue;
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) nxt[k] = valid(k) ? reinterpret_cast<const f4*>(src)[index(k)] : f4(0.0f);
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) dst[k * kLnThreads + tid] = nxt[k];
-    }
-    {
-        const f4* x4 = reinterpret_cast<const f4*>(x);
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) {
-            cur[k] = valid(k) ? x4[index(k)] : f4(0.0f);
-            prev[k] = nxt[k] = f4(0.0f);
-        }
-    }
-    const int64_t n_mine = rows_owned_units(nv, p, P) * 4;
-    const int wave_id = __builtin_amdgcn_readfirstlane(tid / kWave);
-    uint32_t n_wave = 0;  // elements this wave holds of each sample
-#pragma unroll
-    for (int k = 0; k < F4PT; ++k) n_wave += 4u * (uint32_t)__builtin_popcountll(__ballot(valid(k)));
-    const float inv_wave = inv_count_f32(n_wave);
-    if ((tid & (kWave - 1)) == 0) {
-        cnt[wave_id] = n_wave;
-        cnt_inv[wave_id] = inv_count_f64(n_wave);
-    }
-    const double inv_mine = inv_count_f64((uint32_t)n_mine);
-    __syncthreads();
-
-    for (int64_t t = 0; t <= outer; ++t) {
-        if (t < outer) {
-            // two passes over the wave's registers (see WaveMoments), then the
-            // waves' moments merged in wave order by thread 0
-            f4 s = f4(0.0f);
-#pragma unroll
-            for (int k = 0; k < F4PT; ++k) s += valid(k) ? cur[k] : f4(0.0f);
-            const float m = wave_shift(s, inv_wave);
-            f4 a1 = f4(0.0f), a2 = f4(0.0f);
-#pragma unroll
-            for (int k = 0; k < F4PT; ++k) shifted_acc(a1, a2, valid(k) ? cur[k] - m : f4(0.0f));
-            double t1, t2;
-            wave_moments(a1, a2, t1, t2);
-            __syncthreads();  // red may still be read from the previous sample
-            if ((tid & (kWave - 1)) == 0) {
-                red[3 * wave_id] = t1;
-                red[3 * wave_id + 1] = t2;
-                red[3 * wave_id + 2] = (double)m;
-            }
-            __syncthreads();
-            uint32_t* counter = counters + (t % kRing) * kCounterStride;
-            if (wave_id == 0) {
-                Partial q{};
-                q.n = (double)n_mine;
-                merge_wave_moments<kLnThreads / kWave>(red, cnt, cnt_inv, inv_mine, q.mean, q.m2);
-                if (tid == 0) s_last = deliver_partial(parts + t * P_cap + p, q, counter, P);
-            }
-            __syncthreads();
-            if (s_last)
-                merge_and_announce(parts + t * P_cap, P, eps, lds, stats + t, mean_out ? mean_out + t : nullptr,
-                                   rstd_out ? rstd_out + t : nullptr, counter, flag, t, target);
-            if (t + 1 < outer) {
-                const f4* x4 = reinterpret_cast<const f4*>(x + (t + 1) * inner);
-#pragma unroll
-                for (int k = 0; k < F4PT; ++k) nxt[k] = valid(k) ? x4[index(k)] : f4(0.0f);
-            }
-        }
-        if (t >= 1) {
-            const int64_t s = t - 1;
-            if (tid == 0) s_stats = await_stats(flag, stats, s, target, ctrl);
-            __syncthreads();
-            const f4 st = s_stats;
-            f4* y4 = reinterpret_cast<f4*>(y + s * inner);
-#pragma unroll
-            for (int k = 0; k < F4PT; ++k) {
-                if (valid(k)) {
-                    const f4 tt = ((prev[k] - st.x) - st.y) * st.z;
-                    const f4 wv = w ? w_s[k * kLnThreads + tid] : f4(1.0f);
-                    const f4 bv = bias ? b_s[k * kLnThreads + tid] : f4(0.0f);
-                    st_nt(tt * wv + bv, y4 + index(k));
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < F4PT; ++k) {
-            prev[k] = cur[k];
-            cur[k] = nxt[k];
-        }
-    }
-    // completion: the last workgroup out resets the counter and advances the generation
-    __syncthreads();
-    if (tid == 0) {
-        vmem_drain();
-        if (__hip_atomic_fetch_add(&ctrl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1)) {
-            dev_store(&ctrl->done, 0u);
-            vmem_drain();
-            dev_store(&ctrl->gen, target);
-        }
-    }
 }
 
 // The (mean, M2) workgroup j of ln_single_ctl_kernel publishes for one
@@ -1626,43 +1437,34 @@ static int coresident(const void* fn, size_t lds, int threads)
     return cap;
 }
 
-#ifndef NORMFWD_LN_HOLD_F4PT
-#define NORMFWD_LN_HOLD_F4PT 16
-#endif
-
-
-template <int F4PT, int DW, int PROTO = 0>
-static bool try_launch_hold(const float* x, const float* w, const float* b, float* y, int64_t outer, int64_t inner,
-                            float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats, Partial* parts,
-                            double* xchg, int64_t P_cap, float* mean_out, float* rstd_out, hipStream_t st,
-                            hipError_t& err)
+// Launches ln_single_ctl_kernel<F4PT, DW, LAG, PROTO> when a co-resident grid
+// of one workgroup per F4PT rows of DW * 64 float4 holds every sample's rows
+// (false: it cannot, nothing launched).  PROTO 0, the tagged exchange: an
+// ordinary launch; PROTO 1, the last workgroup merging: a cooperative one.
+template <int F4PT, int DW, int PROTO>
+static bool try_launch_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
+                              int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats,
+                              Partial* parts, double* xchg, int64_t P_cap, float* mean_out, float* rstd_out,
+                              hipStream_t st, hipError_t& err)
 {
     DeviceInfo d;
     if (!device_info(d)) return false;
-    // DW == 0: ln_single_hold_kernel (rows of kLnThreads float4, every wave
-    // does both jobs); DW > 0: ln_single_ctl_kernel with DW data waves and
-    // the tagged exchange (PROTO 0, an ordinary launch) or the last
-    // workgroup merging (PROTO 1, a cooperative launch)
-    const int64_t rw = DW == 0 ? kLnThreads : DW * kWave;
+    const int64_t rw = DW * kWave;
     const int64_t rows = ceil_div(inner / 4, rw);
     const int64_t P = ceil_div(rows, (int64_t)F4PT);
     if (P > P_cap) return false;
     const size_t lds = (size_t)((w ? 1 : 0) + (b ? 1 : 0)) * F4PT * rw * sizeof(f4);
     // Whether a tile fits is decided as if both weight and bias were given,
-    // so a shape always runs the same tile (the control-wave kernel's
-    // exchange relies on every launch on a workspace writing the same slots).
+    // so a shape always runs the same tile (the tagged exchange relies on
+    // every launch on a workspace writing the same slots).
     const size_t lds_max = (size_t)2 * F4PT * rw * sizeof(f4);
     if (lds_max + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
-    const void* fn;
-    if constexpr (DW == 0)
-        fn = reinterpret_cast<const void*>(&ln_single_hold_kernel<F4PT>);
-    else
-        fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, PROTO>);
-    const int threads = DW == 0 ? kLnThreads : (DW + 1) * kWave;
+    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, PROTO>);
+    const int threads = (DW + 1) * kWave;
     const int cap = coresident(fn, lds_max, threads);
     if (cap < P) return false;
     int64_t pcap = P_cap;
-    if constexpr (DW > 0 && PROTO == 0) {
+    if constexpr (PROTO == 0) {
         // An ordinary launch (a cooperative one costs ~17 us more per call on
         // MI355X).  The grid fits the device, so normally every workgroup is
         // resident at once; when one is not (another kernel holds its CU), the
@@ -1683,15 +1485,6 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
                             mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, flag, parts);
         return true;
-    }
-    // a cooperative launch cannot carry events: armed ones bracket it as markers
-    const LaunchEvents ev = take_launch_events();
-    if (ev.start) (void)hipEventRecord(ev.start, st);
-    if constexpr (DW == 0) {
-        void* args[] = {(void*)&x,     (void*)&w,     (void*)&b,     (void*)&y,        (void*)&outer,
-                        (void*)&inner, (void*)&pcap,  (void*)&eps,   (void*)&ctrl,     (void*)&counters,
-                        (void*)&flag,  (void*)&stats, (void*)&parts, (void*)&mean_out, (void*)&rstd_out};
-        err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
     } else {
         // one group of P workgroups; the tagged exchange's arguments are unused
         int64_t groups = 1;
@@ -1700,11 +1493,14 @@ static bool try_launch_hold(const float* x, const float* w, const float* b, floa
                         (void*)&inner,    (void*)&pcap,     (void*)&eps,      (void*)&ctrl,   (void*)&stats,
                         (void*)&xchg,     (void*)&mean_out, (void*)&rstd_out, (void*)&groups, (void*)&spin,
                         (void*)&force,    (void*)&counters, (void*)&flag,     (void*)&parts};
+        // a cooperative launch cannot carry events: armed ones bracket it as markers
+        const LaunchEvents ev = take_launch_events();
+        if (ev.start) (void)hipEventRecord(ev.start, st);
         err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
+        if (err == hipSuccess) err = hipGetLastError();
+        if (err == hipSuccess && ev.stop) err = hipEventRecord(ev.stop, st);
+        return true;
     }
-    if (err == hipSuccess) err = hipGetLastError();
-    if (err == hipSuccess && ev.stop) err = hipEventRecord(ev.stop, st);
-    return true;
 }
 
 bool ln_single_supported(int64_t inner, const float* x, const float* w, const float* b, const float* y)
@@ -1746,29 +1542,19 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
     double* xchg = reinterpret_cast<double*>(base + lay.off_xchg);
 
-    // A single-read kernel, when a co-resident grid can hold every sample's
-    // rows (tuned tile first, then the others).
-    // (in place the control-wave kernel does not run and variant 1 takes the split)
+    // The single-read kernel, when a co-resident grid can hold every
+    // sample's rows (on MI355X: samples of up to 4M elements).  The tile of
+    // 8 float4 x 8 data waves bounds it: smaller tiles fit more workgroups
+    // per CU but need as many more, so none holds a larger sample.
+    // (in place the tagged exchange does not run and variant 1 takes the split)
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
-#define NORMFWD_TRY_HOLD(F, DW, ...)                                                                           \
-    if (try_launch_hold<F, DW, ##__VA_ARGS__>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts,  \
-                                              xchg, lay.P_cap, mean_out, rstd_out, st, err))                      \
-        return err;
-        if (protocol == 1) {  // control wave, tagged gather
-            NORMFWD_TRY_HOLD(8, 8)
-            NORMFWD_TRY_HOLD(4, 8)
-        }
-        // last workgroup merges (protocol 2, or shapes the above cannot hold):
-        // the control-wave kernel with that exchange, then the all-purpose waves
-        if (protocol == 2) {
-            NORMFWD_TRY_HOLD(8, 8, 1)
-        }
-        NORMFWD_TRY_HOLD(NORMFWD_LN_HOLD_F4PT, 0)
-        NORMFWD_TRY_HOLD(4, 0)
-        NORMFWD_TRY_HOLD(8, 0)
-        NORMFWD_TRY_HOLD(16, 0)
-#undef NORMFWD_TRY_HOLD
+        const bool launched =
+            protocol == 1 ? try_launch_single<8, 8, 0>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats,
+                                                       parts, xchg, lay.P_cap, mean_out, rstd_out, st, err)
+                          : try_launch_single<8, 8, 1>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats,
+                                                       parts, xchg, lay.P_cap, mean_out, rstd_out, st, err);
+        if (launched) return err;
     }
     // Shapes no single-read kernel can hold run the split schedule.
     hipError_t e = launch_ln_stats(x, outer, inner, eps, ws, lay, mean_out, rstd_out, st);

@@ -37,7 +37,6 @@ KERNEL_SOURCES = {
     "ln_merge_kernel": ["ln.hip", "common.hpp"],
     "ln_normalize_rows_kernel": ["ln.hip", "common.hpp"],
     "ln_normalize_kernel": ["ln.hip", "common.hpp"],
-    "ln_single_hold_kernel": ["ln.hip", "common.hpp"],
     "ln_single_ctl_kernel": ["ln.hip", "common.hpp"],
     "gn_fast_kernel": ["gn.hip", "common.hpp"],
     "rms_ch_hold_kernel": ["rms.hip", "common.hpp"],
