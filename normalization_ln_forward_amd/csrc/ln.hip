@@ -147,6 +147,29 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 // ([16, 65536], [8, 2^20]), is even at 1024 and costs 0.6-1.5 us at 1024-4096
 // ([4, 2^22], [16, 2^22]), where the atomics of thousands of workgroups
 // outweigh the saved launch.
+// Single-read kernel tiles: DW data waves (plus the control wave) of F4PT
+// float4 per thread, i.e. a workgroup holds F4PT rows of 64 DW float4 of
+// every sample.  Measured on MI355X at [16, 4M] (kernel duration, one call,
+// three alternations, on two boxes): 11 x 6 96.3-97.0 us, 10 x 7 97.1-97.7,
+// 8 x 8 99.1-100.4, 9 x 8 99.2-99.7, 12 x 6 100.7-101.1, 13/14/15 x 5
+// 99.7-100.5, 7 x 10 99.2-100.2 (DW x F4PT; tiles whose rows of weight and
+// bias overflow LDS or whose grid exceeds 256 workgroups were not run).
+// The wide tile (11 x 6) streams a sample faster but costs more to start
+// and with sample groups: against 8 x 8 (kernel us, one call) [32, 4M]
+// 181.5 vs 188.3, [16, 4M] 97.0 vs 99.4, [12, 4M] 75.0 vs 76.3, [8, 4M]
+// 53.7 vs 54.6, [4, 4M] 30.4 vs 30.4, [2, 4M] 22.0 vs 20.4, [1, 4M] 15.2 vs
+// 14.2, [16, 3M] 77.3 vs 76.3, [32, 3M] 147.0 vs 146.5, [16, 2M] 52.8 vs
+// 50.0, [32, 1M] 52.6 vs 49.4, [8, 1M] 21.4 vs 17.1, [256, 16K] 12.1 vs
+// 11.6.  So the wide tile runs where a sample fills at least 90% of the
+// co-resident grid (one group) and there are at least 8 samples, and where
+// the 8 x 8 tile cannot hold a sample.  The choice depends on the shape and
+// the device only, as the tagged exchange needs (a workspace of one shape
+// always sees the same tile).
+constexpr int kLnTileWaves = 8;
+constexpr int kLnTileF4 = 8;
+constexpr int kLnWideWaves = 11;
+constexpr int kLnWideF4 = 6;
+
 // Single kernel with a control wave: iterations between a sample's moments
 // and its normalize (1 or 2).
 #ifndef NORMFWD_LN_CTL_LAG
@@ -789,11 +812,11 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
                               double* rc_inv, double& mean, double& m2)
 {
     constexpr uint32_t RW = DW * kWave;
-    static_assert(DW % 2 == 0, "two data waves per batch");
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t stride = P * RW;
     // two data waves' elements per batch: twice the loads in flight per round
-    // trip, at 2 F4PT float4 registers per lane
+    // trip, at 2 F4PT float4 registers per lane (with an odd DW the last
+    // batch holds one wave)
 #pragma unroll 1
     for (int w0 = 0; w0 < DW; w0 += 2) {
         f4 v[2][F4PT];
@@ -803,12 +826,13 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) {
                 const uint32_t idx = off0 + (uint32_t)k * stride;
-                v[h][k] = (int64_t)idx < nv ? ld_nt(xs + idx) : f4(0.0f);
+                v[h][k] = (w0 + h < DW && (int64_t)idx < nv) ? ld_nt(xs + idx) : f4(0.0f);
             }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int w = w0 + h;
+            if (w >= DW) break;
             const uint32_t off0 = j * RW + (uint32_t)(w * kWave + lane);
             auto ok = [&](int k) { return (int64_t)(off0 + (uint32_t)k * stride) < nv; };
             const uint32_t n = ctl_wave_elems<F4PT, DW>(j, w, P, nv);
@@ -1508,26 +1532,55 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
     return (inner % 4 == 0) && is_aligned16(x) && is_aligned16(y) && is_aligned16(w) && is_aligned16(b);
 }
 
-// Measured on MI355X (split against the control-wave kernel with sample
-// groups, one call, 200 ms settle per shape): [16, 4M] 134.8 vs 99.1 us,
-// [4, 4M] 41.1 vs 26.6, [32, 2M] 137.3 vs 93.6, [16, 2M] 70.4 vs 50.1,
-// [32, 1M] 67.8 vs 49.3, [16, 1M] 39.1 vs 24.0, [8, 1M] 20.9 vs 15.7, [4, 1M]
-// 11.7 vs 12.1, [2, 1M] 10.5 vs 10.4, [64, 256K] 33.5 vs 23.7, [16, 256K]
-// 11.3 vs 11.9, [4, 256K] 9.5 vs 8.8, [128, 64K] 22.5 vs 14.9, [32, 64K]
-// 11.7 vs 10.0, [256, 16K] 14.8 vs 12.1.  With as many groups of workgroups
-// as stay co-resident, the single-read kernel fills the GPU whatever the
-// sample size and saves one read of x; the split is ahead only by < 1 us
-// on calls of ~10 us.  So it is taken wherever it can run.
+// Workgroups per sample and co-resident workgroups of ln_single_ctl_kernel
+// with the tile <F4PT, DW>.
+template <int F4PT, int DW>
+static void single_grid(int64_t inner, int64_t& P, int& cap)
+{
+    P = ceil_div(ceil_div(inner / 4, (int64_t)DW * kWave), (int64_t)F4PT);
+    const size_t lds = (size_t)2 * F4PT * DW * kWave * sizeof(f4);
+    DeviceInfo d;
+    cap = 0;
+    if (!device_info(d) || lds + 8 * 1024 > (size_t)d.max_lds_per_block) return;
+    cap = coresident(reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, 0>), lds,
+                     (DW + 1) * kWave);
+}
+
+// The wide tile where it measured faster, or where the other cannot hold
+// a sample (see kLnWideWaves).
+static bool ln_wide_tile(int64_t outer, int64_t inner)
+{
+    int64_t Pw = 0, Pn = 0;
+    int capw = 0, capn = 0;
+    single_grid<kLnWideF4, kLnWideWaves>(inner, Pw, capw);
+    single_grid<kLnTileF4, kLnTileWaves>(inner, Pn, capn);
+    if (capn < Pn) return true;
+    return outer >= 8 && Pw <= capw && Pw * 10 >= (int64_t)capw * 9;
+}
+
+// Measured on MI355X (split against the single-read kernel with the tile
+// ln_wide_tile picks and sample groups, per call, one call, 200 ms settle per
+// shape): [16, 4M] 137.1 vs 97.2 us, [4, 4M] 42.6 vs 30.9, [32, 2M] 135.3 vs
+// 94.2, [16, 2M] 72.0 vs 50.7, [4, 2M] 23.8 vs 19.2, [2, 2M] 14.3 vs 13.3,
+// [32, 1M] 69.5 vs 49.7, [16, 1M] 40.7 vs 27.1, [8, 1M] 22.1 vs 17.7,
+// [4, 1M] 12.8 vs 12.6, [2, 1M] 11.0 vs 10.5, [64, 256K] 35.0 vs 28.5,
+// [16, 256K] 12.4 vs 11.9, [4, 256K] 10.2 vs 9.1, [128, 64K] 23.1 vs 17.1,
+// [32, 64K] 11.9 vs 10.1, [256, 16K] 15.8 vs 11.9.  With as many groups of
+// workgroups as stay co-resident, the single-read kernel fills the GPU
+// whatever the sample size and saves one read of x, so it is taken
+// wherever it can run.
 int ln_auto_variant(const float* x, const float* w, const float* b, const float* y, int64_t outer, int64_t inner)
 {
-    (void)outer;
     // in place the control-wave kernel does not run (a reader may need x
     // after its owner has overwritten it): the split schedule does
     if (!ln_single_supported(inner, x, w, b, y) || x == y) return 0;
-    const int64_t P = ceil_div(ceil_div(inner / 4, (int64_t)8 * kWave), (int64_t)8);
-    const size_t lds = (size_t)2 * 8 * 8 * kWave * sizeof(f4);
-    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<8, 8, NORMFWD_LN_CTL_LAG, 0>);
-    return coresident(fn, lds, 9 * kWave) >= P ? 1 : 0;
+    int64_t P = 0;
+    int cap = 0;
+    if (ln_wide_tile(outer, inner))
+        single_grid<kLnWideF4, kLnWideWaves>(inner, P, cap);
+    else
+        single_grid<kLnTileF4, kLnTileWaves>(inner, P, cap);
+    return cap >= P ? 1 : 0;
 }
 
 hipError_t launch_ln_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
@@ -1543,17 +1596,22 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     double* xchg = reinterpret_cast<double*>(base + lay.off_xchg);
 
     // The single-read kernel, when a co-resident grid can hold every
-    // sample's rows (on MI355X: samples of up to 4M elements).  The tile of
-    // 8 float4 x 8 data waves bounds it: smaller tiles fit more workgroups
-    // per CU but need as many more, so none holds a larger sample.
+    // sample's rows (on MI355X: samples of up to 256 x 4224 float4, about
+    // 4.3M elements, with the wide tile).  Smaller tiles fit more workgroups
+    // per CU but need as many more, so none would hold a larger sample.
     // (in place the tagged exchange does not run and variant 1 takes the split)
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
+#define NORMFWD_TRY_SINGLE(F, DW, PR)                                                                         \
+    try_launch_single<F, DW, PR>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, xchg,     \
+                                 lay.P_cap, mean_out, rstd_out, st, err)
+        const bool wide = ln_wide_tile(outer, inner);
         const bool launched =
-            protocol == 1 ? try_launch_single<8, 8, 0>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats,
-                                                       parts, xchg, lay.P_cap, mean_out, rstd_out, st, err)
-                          : try_launch_single<8, 8, 1>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats,
-                                                       parts, xchg, lay.P_cap, mean_out, rstd_out, st, err);
+            protocol == 1 ? (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, 0)
+                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, 0))
+                          : (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, 1)
+                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, 1));
+#undef NORMFWD_TRY_SINGLE
         if (launched) return err;
     }
     // Shapes no single-read kernel can hold run the split schedule.

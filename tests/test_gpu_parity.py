@@ -162,6 +162,12 @@ LN_CASES = [
     (4, 40001, True, 2),
     (3, 300000, False, 2),
     (1, 1 << 20, True, 2),
+    # the wide single-read tile (11 data waves x 6 float4): 8 samples that fill 237 workgroups (ragged
+    # last row), and a sample of 1,081,344 float4 that only the wide tile's 256 workgroups hold
+    (8, 4000000, True, 1),
+    (8, 4000000, True, 2),
+    (2, 4325376, True, 1),
+    (2, 4325376, True, 2),
 ]
 
 
