@@ -165,16 +165,17 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 // the 8 x 8 tile cannot hold a sample.  The choice depends on the shape and
 // the device only, as the tagged exchange needs (a workspace of one shape
 // always sees the same tile).
+// LAG: iterations between a sample's moments and its normalize (register
+// tiles LAG + 2).  The wide tile has room for a lag of 3 (152 VGPRs, no
+// spills; [16, 4M] 95.7-95.9 us against 96.4-96.8 with 2, last-workgroup
+// merges 164-165 against 167-168 us per call); the 8 x 8 tile spills with 3.
 constexpr int kLnTileWaves = 8;
 constexpr int kLnTileF4 = 8;
+constexpr int kLnTileLag = 2;
 constexpr int kLnWideWaves = 11;
 constexpr int kLnWideF4 = 6;
+constexpr int kLnWideLag = 3;
 
-// Single kernel with a control wave: iterations between a sample's moments
-// and its normalize (1 or 2).
-#ifndef NORMFWD_LN_CTL_LAG
-#define NORMFWD_LN_CTL_LAG 2
-#endif
 
 // Doubles per workgroup in the control-wave kernel's exchange region (0:
 // all means of a sample, then all M2s).  Measured on MI355X at [16, 4M]
@@ -871,7 +872,8 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 //       with the statistics the control wave left in LDS, then load sample
 //       t-LAG+NT into the freed registers (NT = LAG + 2 register tiles:
 //       sample t+1 is in flight while t is reduced, and t+2 is issued at
-//       the end of the iteration).
+//       the end of the iteration; samples t-1 .. t-LAG+1 wait for their
+//       statistics).
 //   control wave, after barrier t:  merge the data waves' moments of sample
 //       t into this workgroup's (mean, M2) (merge_wave_moments) and publish them
 //       as two generation-tagged words; then read all P workgroups' words
@@ -879,7 +881,7 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 //       order (every workgroup computes the same statistics; the k-way
 //       pairwise update around one shift, workgroup 0's mean, in fp64) and
 //       leave the statistics in LDS before barrier t+1.
-// With LAG = 2 every workgroup has had a whole iteration to publish the
+// With LAG >= 2 every workgroup has had a whole iteration to publish the
 // moments the control wave gathers, so the gather rarely waits and the data
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
@@ -1465,7 +1467,7 @@ static int coresident(const void* fn, size_t lds, int threads)
 // of one workgroup per F4PT rows of DW * 64 float4 holds every sample's rows
 // (false: it cannot, nothing launched).  PROTO 0, the tagged exchange: an
 // ordinary launch; PROTO 1, the last workgroup merging: a cooperative one.
-template <int F4PT, int DW, int PROTO>
+template <int F4PT, int DW, int LAG, int PROTO>
 static bool try_launch_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                               int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats,
                               Partial* parts, double* xchg, int64_t P_cap, float* mean_out, float* rstd_out,
@@ -1483,7 +1485,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
     // every launch on a workspace writing the same slots).
     const size_t lds_max = (size_t)2 * F4PT * rw * sizeof(f4);
     if (lds_max + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
-    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, PROTO>);
+    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, LAG, PROTO>);
     const int threads = (DW + 1) * kWave;
     const int cap = coresident(fn, lds_max, threads);
     if (cap < P) return false;
@@ -1505,7 +1507,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         // as many groups of P workgroups (each taking every groups-th
         // sample) as stay co-resident, at most one per sample
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
-        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, 0>, dim3((unsigned)(groups * P)),
+        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, LAG, 0>, dim3((unsigned)(groups * P)),
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
                             mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, flag, parts);
         return true;
@@ -1534,7 +1536,7 @@ bool ln_single_supported(int64_t inner, const float* x, const float* w, const fl
 
 // Workgroups per sample and co-resident workgroups of ln_single_ctl_kernel
 // with the tile <F4PT, DW>.
-template <int F4PT, int DW>
+template <int F4PT, int DW, int LAG>
 static void single_grid(int64_t inner, int64_t& P, int& cap)
 {
     P = ceil_div(ceil_div(inner / 4, (int64_t)DW * kWave), (int64_t)F4PT);
@@ -1542,7 +1544,7 @@ static void single_grid(int64_t inner, int64_t& P, int& cap)
     DeviceInfo d;
     cap = 0;
     if (!device_info(d) || lds + 8 * 1024 > (size_t)d.max_lds_per_block) return;
-    cap = coresident(reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, NORMFWD_LN_CTL_LAG, 0>), lds,
+    cap = coresident(reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, LAG, 0>), lds,
                      (DW + 1) * kWave);
 }
 
@@ -1552,8 +1554,8 @@ static bool ln_wide_tile(int64_t outer, int64_t inner)
 {
     int64_t Pw = 0, Pn = 0;
     int capw = 0, capn = 0;
-    single_grid<kLnWideF4, kLnWideWaves>(inner, Pw, capw);
-    single_grid<kLnTileF4, kLnTileWaves>(inner, Pn, capn);
+    single_grid<kLnWideF4, kLnWideWaves, kLnWideLag>(inner, Pw, capw);
+    single_grid<kLnTileF4, kLnTileWaves, kLnTileLag>(inner, Pn, capn);
     if (capn < Pn) return true;
     return outer >= 8 && Pw <= capw && Pw * 10 >= (int64_t)capw * 9;
 }
@@ -1577,9 +1579,9 @@ int ln_auto_variant(const float* x, const float* w, const float* b, const float*
     int64_t P = 0;
     int cap = 0;
     if (ln_wide_tile(outer, inner))
-        single_grid<kLnWideF4, kLnWideWaves>(inner, P, cap);
+        single_grid<kLnWideF4, kLnWideWaves, kLnWideLag>(inner, P, cap);
     else
-        single_grid<kLnTileF4, kLnTileWaves>(inner, P, cap);
+        single_grid<kLnTileF4, kLnTileWaves, kLnTileLag>(inner, P, cap);
     return cap >= P ? 1 : 0;
 }
 
@@ -1602,15 +1604,15 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     // (in place the tagged exchange does not run and variant 1 takes the split)
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
-#define NORMFWD_TRY_SINGLE(F, DW, PR)                                                                         \
-    try_launch_single<F, DW, PR>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, xchg,     \
+#define NORMFWD_TRY_SINGLE(F, DW, LG, PR)                                                                     \
+    try_launch_single<F, DW, LG, PR>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, xchg,     \
                                  lay.P_cap, mean_out, rstd_out, st, err)
         const bool wide = ln_wide_tile(outer, inner);
         const bool launched =
-            protocol == 1 ? (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, 0)
-                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, 0))
-                          : (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, 1)
-                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, 1));
+            protocol == 1 ? (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, kLnWideLag, 0)
+                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 0))
+                          : (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, kLnWideLag, 1)
+                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 1));
 #undef NORMFWD_TRY_SINGLE
         if (launched) return err;
     }
