@@ -167,8 +167,10 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 // always sees the same tile).
 // LAG: iterations between a sample's moments and its normalize (register
 // tiles LAG + 2).  The wide tile has room for a lag of 3 (152 VGPRs, no
-// spills; [16, 4M] 95.7-95.9 us against 96.4-96.8 with 2, last-workgroup
-// merges 164-165 against 167-168 us per call); the 8 x 8 tile spills with 3.
+// spills) or 4 (166): kernel us for lags 2 / 3 / 4, one call: [64, 4M]
+// 352.7 / 352.1 / 364.0, [32, 4M] 183.5 / 182.9 / 185.4, [16, 4M] 96.9 /
+// 96.2 / 96.3, [8, 4M] 53.6 / 50.1 / 49.4 (last-workgroup merges at [16,
+// 4M]: 167-168 / 164-165 us per call).  The 8 x 8 tile spills with 3.
 constexpr int kLnTileWaves = 8;
 constexpr int kLnTileF4 = 8;
 constexpr int kLnTileLag = 2;
