@@ -135,8 +135,8 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 place (y == x) this variant runs the split schedule;
  *             2 = single kernel in which the last workgroup to deliver a
  *                 sample's partial merges it and announces the statistics
- *                 with a flag (LN page, turn 6: last-block-done), the others
- *                 waiting for that flag (a control wave per workgroup does
+ *                 (LN page, turn 6: last-block-done), the others waiting
+ *                 for them (a control wave per workgroup does
  *                 the exchange beside the data waves of variant 1, which
  *                 read x once; in place is fine).  A cooperative launch, since its
  *                 waits need every workgroup resident.  The runtime grants

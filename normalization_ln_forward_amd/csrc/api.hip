@@ -192,7 +192,7 @@ normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes
 {
     if (!workspace || workspace_bytes < 256 || !aligned256(workspace))
         return fail(NORMFWD_ERR_WORKSPACE, "ln_forward_workspace_init: need a 256-byte aligned workspace of >= 256 bytes");
-    // The whole workspace is cleared: control block, counters and flags.
+    // The whole workspace is cleared: control block, counters and exchange words.
     (void)hipGetLastError();
     return hip_status(normfwd::launch_zero_words(workspace, workspace_bytes, (hipStream_t)stream),
                       "ln_forward_workspace_init launch");

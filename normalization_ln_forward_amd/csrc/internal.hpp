@@ -68,11 +68,11 @@ struct LnLayout {
     int64_t P_cap;    // partial-moment slots per sample (>= chunks of either variant)
     size_t off_ctrl;  // control block: generation, completion counter, error word
     size_t off_counter;  // single kernel: ring of arrival counters
-    size_t off_flag;
     size_t off_split_counter;  // split schedule: per-sample arrival counters (128-byte lines)
     size_t off_stats;
     size_t off_part;
     size_t off_xchg;  // control-wave kernel's exchange: per sample, P_cap tagged means then P_cap tagged M2s
+    size_t off_lbd;   // control-wave kernel, last workgroup merging: per sample, tagged mean and rstd (fp64)
     size_t total;
 };
 // Byte offset, in an LN workspace, of the word the single kernels set when

@@ -49,10 +49,10 @@
 //          is not resident) are computed by the reader from x, with the same
 //          bits (so it never runs in place: y == x takes the split);
 //          variant 2 (a cooperative launch): the last workgroup to deliver
-//          a sample's partial merges it and announces the statistics with a
-//          flag (LN page, turn 6: last-block-done), done by the control
-//          wave of ln_single_ctl_kernel (ctl_wave_last_block) beside the
-//          same data waves.
+//          a sample's partial merges it and announces the statistics (LN
+//          page, turn 6: last-block-done; generation-tagged words serve as
+//          the flag), done by the control wave of ln_single_ctl_kernel
+//          (ctl_wave_last_block) beside the same data waves.
 //          Samples too large for the kernel's co-resident grid take the
 //          split under every variant.
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
@@ -76,7 +76,7 @@ struct alignas(32) Partial {
 };
 
 struct LnCtrl {
-    uint32_t gen;    // last-workgroup-merges kernel: launches so far (its flags carry the next value)
+    uint32_t gen;    // last-workgroup-merges kernel: launches so far (its statistics words carry the next value's tag)
     uint32_t done;   // completion counter of the current single-kernel launch (returns to 0)
     uint32_t error;  // set to 1 if a wait ran past its spin limit (last-workgroup-merges kernel)
     uint32_t recomputed;  // control-wave kernel: workgroup moments computed by a reader instead (diagnostic)
@@ -210,8 +210,6 @@ LnLayout ln_layout(int64_t outer, int64_t inner)
     off += sizeof(LnCtrl);
     L.off_counter = off;
     off += align256(4 * (size_t)kLnCounterWords);
-    L.off_flag = off;
-    off += align256(4 * (size_t)outer);
     L.off_split_counter = off;
     off += align256(4 * (size_t)kCounterStride * (size_t)outer);
     L.off_stats = off;
@@ -220,27 +218,13 @@ LnLayout ln_layout(int64_t outer, int64_t inner)
     off += align256(sizeof(Partial) * (size_t)outer * (size_t)L.P_cap);
     L.off_xchg = off;
     off += align256((NORMFWD_LN_XCHG_SLOT ? NORMFWD_LN_XCHG_SLOT : 2) * sizeof(double) * (size_t)outer * (size_t)L.P_cap);
+    L.off_lbd = off;
+    off += align256(2 * sizeof(double) * (size_t)outer);
     L.total = off;
     return L;
 }
 
 // ---------------------------------------------------------------- device pieces
-
-__device__ __forceinline__ void chan_merge(double& n, double& m, double& m2, double nb, double mb, double m2b)
-{
-    if (nb == 0.0) return;
-    if (n == 0.0) {
-        n = nb;
-        m = mb;
-        m2 = m2b;
-        return;
-    }
-    const double nn = n + nb;
-    const double d = mb - m;
-    m = m + d * (nb / nn);
-    m2 = m2 + m2b + d * d * (n * nb / nn);
-    n = nn;
-}
 
 // Sum of one double per thread over the workgroup, fixed order; valid in
 // every thread on return.  red: LDS of NT/64 + 1 doubles.
@@ -261,18 +245,21 @@ __device__ __forceinline__ double block_sum(double v, double* red)
 // acquire fences make them coherent by writing back / invalidating the
 // whole L2 (buffer_wbl2 / buffer_inv), which measured ~100 us over one
 // LayerNorm launch.  The protocol below avoids them: every location that
-// crosses workgroups (partial moments, statistics, counters, flags) is only
-// ever accessed with agent-scope atomic loads and stores, which the gfx950
-// code generator issues as device-coherent accesses (sc1) served at the
-// device's coherence point, and a writer waits for its data stores to
-// complete (s_waitcnt vmcnt(0)) before it stores the counter or flag that
-// announces them.  A reader issues its data loads only after it has seen
-// that counter or flag value, so it reads the announced data.
+// crosses workgroups (partial moments, statistics, counters, exchange
+// words) is only ever accessed with agent-scope atomic loads and stores,
+// which the gfx950 code generator issues as device-coherent accesses (sc1)
+// served at the device's coherence point.  A writer waits for its data
+// stores to complete (s_waitcnt vmcnt(0)) before it counts its arrival, so
+// the workgroup that sees the last arrival reads every partial; words that
+// announce themselves (generation-tagged, see ln_tag.hpp) need no flag: an
+// aligned 8-byte store is seen whole, and a reader takes a word only when
+// it carries the current tag.
 //
-// Arrival counters live in a ring of kRing slots (sample t uses slot t %
-// kRing), each on its own 128-byte line.  Reuse is safe: the merger of
-// sample t resets the slot before it announces flag[t], and no workgroup
-// arrives at sample t + 2 before it has seen flag[t].
+// Arrival counters of the single kernel live in a ring of kRing slots
+// (sample t uses slot t % kRing), each on its own 128-byte line.  Reuse is
+// safe: the merger of sample t resets the slot, drains, and only then
+// announces the statistics of sample t, and no workgroup arrives at sample
+// t + kRing before it has read them.
 
 // Wait until this thread's earlier vector-memory accesses have completed.
 __device__ __forceinline__ void vmem_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -342,47 +329,46 @@ __device__ __forceinline__ int64_t rows_owned_units(int64_t nu, int64_t p, int64
     return owns_last ? (c - 1) * kLnThreads + last_units : c * kLnThreads;
 }
 
-// Merge of a sample's P partials by one wave: lane l folds partials l,
-// l + 64, ... in order, then a fixed butterfly over the 64 lanes (shuffles,
-// no LDS or barriers); every lane ends with the merged (n, mean, M2).
-// COHERENT: the partials were written by other workgroups of the running
-// launch and are read with device-coherent loads.
-template <bool COHERENT, int kBatch = 4>
-__device__ __forceinline__ void wave_merge(const Partial* pb, int64_t P, double& n, double& m, double& m2)
+// A sample's P partials (n, mean, M2) merged by one wave in the k-way form
+// of the pairwise update, around partial 0's mean c: N = sum n_j, A = sum
+// n_j (mean_j - c), B = sum (M2_j + n_j (mean_j - c)^2) (lane l takes
+// partials l, l + 64, ..., the loads of a block of 256 in flight together;
+// wave_total: a fixed order), then mean = c + A / N and M2 = B - A^2 / N.
+// One division in all (a pairwise merge takes two per step, on the critical
+// path of the sample); uniform on return.  COHERENT: the partials were
+// written by other workgroups of the running launch and are read with
+// device-coherent loads.
+template <bool COHERENT>
+__device__ __forceinline__ void kway_merge(const Partial* pb, int64_t P, double& n, double& mean, double& m2)
 {
-    n = 0.0;
-    m = 0.0;
-    m2 = 0.0;
     const int lane = threadIdx.x & (kWave - 1);
-    // kBatch partials per lane are loaded before any is merged, so their
-    // loads are in flight together (the merge order is unchanged: lane l
-    // folds l, l + 64, l + 128, ...).  Out-of-range slots read slot l and
-    // count as empty.
-    for (int64_t j0 = lane; j0 < P; j0 += kBatch * kWave) {
-        double bn[kBatch], bm[kBatch], bm2[kBatch];
+    auto ld = [](const double* q) { return COHERENT ? dev_load(q) : *q; };
+    const double c = lane_f64(ld(&pb[0].mean), 0);
+    double N = 0.0, A = 0.0, B = 0.0;
+    for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
+        double nj[4], mj[4], qj[4];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t j = j0 + (int64_t)u * kWave;
-            const Partial* q = pb + (j < P ? j : j0);
-            if constexpr (COHERENT) {
-                bn[u] = dev_load(&q->n);
-                bm[u] = dev_load(&q->mean);
-                bm2[u] = dev_load(&q->m2);
-            } else {
-                bn[u] = q->n;
-                bm[u] = q->mean;
-                bm2[u] = q->m2;
-            }
-            if (j >= P) bn[u] = 0.0;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + lane + (int64_t)u * kWave;
+            const Partial* pj = pb + (j < P ? j : 0);
+            nj[u] = j < P ? ld(&pj->n) : 0.0;
+            mj[u] = ld(&pj->mean);
+            qj[u] = j < P ? ld(&pj->m2) : 0.0;
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) chan_merge(n, m, m2, bn[u], bm[u], bm2[u]);
+        for (int u = 0; u < 4; ++u) {
+            const double d = mj[u] - c;
+            N += nj[u];
+            A += nj[u] * d;
+            B += qj[u] + nj[u] * (d * d);
+        }
     }
-#pragma unroll
-    for (int mask = 1; mask < kWave; mask <<= 1) {
-        const double on = __shfl_xor(n, mask), om = __shfl_xor(m, mask), om2 = __shfl_xor(m2, mask);
-        chan_merge(n, m, m2, on, om, om2);
-    }
+    n = wave_total(N);
+    A = wave_total(A);
+    B = wave_total(B);
+    const double md = n > 0.0 ? A / n : 0.0;
+    mean = c + md;
+    m2 = fmax(B - A * md, 0.0);
 }
 
 __device__ __forceinline__ void store_stats(int64_t b, const f4& st, f4* stats, float* mean_out, float* rstd_out)
@@ -484,14 +470,14 @@ ln_partial_kernel(const float* x, int64_t inner, int64_t P, int64_t P_cap, Parti
     __syncthreads();
     if (!last || threadIdx.x >= kWave) return;
     double n, m, m2;
-    wave_merge<true>(pb, P, n, m, m2);
+    kway_merge<true>(pb, P, n, m, m2);
     if (threadIdx.x == 0) {
         store_stats(b, finish_stats(n, m, m2, eps), stats, mean_out, rstd_out);
         dev_store(counter, 0u);
     }
 }
 
-// One wave per sample merges its partials (wave_merge); lane 0 writes
+// One wave per sample merges its partials (kway_merge); lane 0 writes
 // (mean hi, mean lo, rstd).
 __global__ void __launch_bounds__(kWave)
 ln_merge_kernel(const Partial* parts, int64_t P, int64_t P_cap, float eps, f4* stats, float* mean_out,
@@ -499,7 +485,7 @@ ln_merge_kernel(const Partial* parts, int64_t P, int64_t P_cap, float eps, f4* s
 {
     const int64_t b = blockIdx.x;
     double n, m, m2;
-    wave_merge<false>(parts + b * P_cap, P, n, m, m2);
+    kway_merge<false>(parts + b * P_cap, P, n, m, m2);
     if (threadIdx.x == 0) store_stats(b, finish_stats(n, m, m2, eps), stats, mean_out, rstd_out);
 }
 
@@ -785,24 +771,6 @@ __device__ __forceinline__ void merge_wave_moments(const double* rd, const uint3
     m2 = fmax(B - A * md, 0.0);
 }
 
-// Wait for flag[t] == target and return sample t's statistics (thread 0
-// only).  A spin limit turns a wait that cannot end into an error flag
-// instead of a hang.
-__device__ __forceinline__ f4 await_stats(const uint32_t* flag, const f4* stats, int64_t t, uint32_t target,
-                                          LnCtrl* ctrl)
-{
-    uint32_t it = 0;
-    while (dev_load(&flag[t]) != target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++it > kSpinLimit) {
-            dev_store(&ctrl->error, 1u);
-            break;
-        }
-    }
-    const float* sp = reinterpret_cast<const float*>(stats + t);
-    return f4{dev_load(sp + 0), dev_load(sp + 1), dev_load(sp + 2), 0.0f};
-}
-
 // The (mean, M2) workgroup j of ln_single_ctl_kernel publishes for one
 // sample (xs: the sample's float4s), computed by one whole wave from x: for
 // each data wave w of j, lane l loads what thread w * 64 + l of j holds and
@@ -887,11 +855,12 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // moments the control wave gathers, so the gather rarely waits and the data
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
-// data waves, ctl_wave_last_block below, measured 166-167 us per call
-// against 99-100 us at [16, 4M]: its chain per sample, drain, arrival
-// atomic, the last arrival's merge, flag and the readers' poll, is longer
-// than one sample's streaming time; counting arrivals in two levels, or
-// tagged statistics words in place of the flag, did not shorten it.)
+// data waves, ctl_wave_last_block below, runs the chain drain, arrival
+// atomic, the last arrival's merge, its announcement and the readers' poll
+// once per sample: 140-141 us per call at [16, 4M], ~15 us of which the
+// cooperative launch costs, against 96-97 us.  With a pairwise merge, two
+// fp64 divisions per step on that chain, it took 160-161 us; with a flag
+// and then the statistics read after it, 163-164.)
 //
 // Control wave of ln_single_ctl_kernel with the last-workgroup-merges
 // exchange (LN page, turn 6: last-block-done), for ln_forward variant 2, a
@@ -899,29 +868,48 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // has a spin limit that sets the control block's error word instead of
 // hanging).  The data waves are those of the tagged exchange, unchanged, so
 // they never wait on another workgroup.  After barrier t:
+//   issue the loads of the statistics words of sample g = t - LAG + 1 (they
+//   were announced an iteration or more ago, and their round trip overlaps
+//   what follows);
 //   merge the data waves' moments of sample t into this workgroup's (n,
 //   mean, M2) (merge_wave_moments), publish it in its partial slot, drain
 //   the stores and count the arrival on the sample's counter (a ring of
 //   kRing); the last of the P arrivals merges the sample's partials in a
-//   fixed order (wave_merge, one wave), stores the statistics, puts the
-//   counter back to 0 and announces the sample with its flag (= the launch
-//   generation);
-//   then wait for the flag of sample t - LAG + 1 and leave its statistics in
-//   LDS before barrier t + 1 (they are normalized after barrier t + 2).
-// The last workgroup out advances the generation.
+//   fixed order (kway_merge, one wave), puts the counter back to 0, drains,
+//   and announces the sample's mean and rstd as two fp64 words tagged with
+//   the launch generation (ln_tag.hpp; a region only this kernel and the
+//   zeroing kernel write), so one poll both finds and reads them;
+//   then poll sample g's words until both carry this launch's tag and leave
+//   its statistics in LDS before barrier t + 1.
+// Every workgroup derives mean hi/lo and rstd from the same two words.  The
+// last workgroup out advances the generation.
 template <int DW, int LAG>
 __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t* cnt, const double* cnt_inv,
                                     f4* s_stats, int64_t outer, int64_t P, int64_t P_cap, int64_t p,
-                                    uint32_t n_mine, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag,
+                                    uint32_t n_mine, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd,
                                     Partial* parts, f4* stats, float* mean_out, float* rstd_out)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t target = dev_load(&ctrl->gen) + 1u;
+    const uint32_t tag = ln_tag_of(target);
     const double inv_mine = inv_count_f64(n_mine);
     const int64_t steps = outer + LAG;
+    // (mean hi, mean lo, rstd) from the tagged words
+    auto unpack = [](double tm, double tr) {
+        const double m = ln_untag(tm);
+        const float hi = (float)m;
+        return f4{hi, (float)(m - (double)hi), (float)ln_untag(tr), 0.0f};
+    };
     __syncthreads();  // prologue: w/b in LDS
     for (int64_t t = 0; t < steps; ++t) {
         __syncthreads();  // barrier t: the wave moments of sample t are in LDS
+        const int64_t g = t - (LAG - 1);
+        const bool gather = g >= 0 && g < outer;
+        double tm = 0.0, tr = 0.0;
+        if (gather && lane == 0) {
+            tm = dev_load(lbd + 2 * g);
+            tr = dev_load(lbd + 2 * g + 1);
+        }
         if (t < outer) {
             Partial q{};
             q.n = (double)n_mine;
@@ -931,23 +919,34 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
             if (lane == 0) last = deliver_partial(parts + t * P_cap + p, q, counter, P) ? 1u : 0u;
             if (__builtin_amdgcn_readfirstlane(last)) {
                 double n, m, m2;
-                wave_merge<true>(parts + t * P_cap, P, n, m, m2);
+                kway_merge<true>(parts + t * P_cap, P, n, m, m2);
                 if (lane == 0) {
-                    const f4 st = finish_stats(n, m, m2, eps);
-                    float* sp = reinterpret_cast<float*>(stats + t);
-                    dev_store(sp + 0, st.x);
-                    dev_store(sp + 1, st.y);
-                    dev_store(sp + 2, st.z);
-                    if (mean_out) mean_out[t] = st.x;
-                    if (rstd_out) rstd_out[t] = st.z;
+                    const double var = n > 0.0 ? m2 / n : 0.0;
+                    const double wm = ln_tag_word(m, tag), wr = ln_tag_word(1.0 / sqrt(var + (double)eps), tag);
                     dev_store(counter, 0u);
                     vmem_drain();
-                    dev_store(&flag[t], target);
+                    dev_store(lbd + 2 * t, wm);
+                    dev_store(lbd + 2 * t + 1, wr);
+                    const f4 st = unpack(wm, wr);
+                    stats[t] = st;
+                    if (mean_out) mean_out[t] = st.x;
+                    if (rstd_out) rstd_out[t] = st.z;
                 }
             }
         }
-        const int64_t g = t - (LAG - 1);
-        if (g >= 0 && g < outer && lane == 0) s_stats[g & 1] = await_stats(flag, stats, g, target, ctrl);
+        if (gather && lane == 0) {
+            uint32_t it = 0;
+            while (!(ln_has_tag(tm, tag) && ln_has_tag(tr, tag))) {
+                __builtin_amdgcn_s_sleep(1);
+                if (++it > kSpinLimit) {
+                    dev_store(&ctrl->error, 1u);
+                    break;
+                }
+                tm = dev_load(lbd + 2 * g);
+                tr = dev_load(lbd + 2 * g + 1);
+            }
+            s_stats[g & 1] = unpack(tm, tr);
+        }
     }
     // completion: the last workgroup out advances the generation
     if (lane == 0) {
@@ -990,7 +989,7 @@ __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, float* y_all, int64_t outer_all,
                      int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, double* xchg_all,
                      float* mean_all, float* rstd_all, int64_t groups, uint32_t spin_limit, uint32_t silent_mask,
-                     uint32_t* counters, uint32_t* flag, Partial* parts)
+                     uint32_t* counters, double* lbd, Partial* parts)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
@@ -1040,7 +1039,7 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
         }
         const uint32_t n_mine = ctl_wg_elems<F4PT, DW>((uint32_t)p, (uint32_t)P, nv);
         ctl_wave_last_block<DW, LAG>(red, cnt[0], cnt_inv[0], s_stats, outer, P, P_cap, p, n_mine, eps, ctrl,
-                                     counters, flag, parts, stats, mean_out, rstd_out);
+                                     counters, lbd, parts, stats, mean_out, rstd_out);
         return;
     }
     if (tid >= RW) {
@@ -1471,7 +1470,7 @@ static int coresident(const void* fn, size_t lds, int threads)
 // ordinary launch; PROTO 1, the last workgroup merging: a cooperative one.
 template <int F4PT, int DW, int LAG, int PROTO>
 static bool try_launch_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
-                              int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, uint32_t* flag, f4* stats,
+                              int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd, f4* stats,
                               Partial* parts, double* xchg, int64_t P_cap, float* mean_out, float* rstd_out,
                               hipStream_t st, hipError_t& err)
 {
@@ -1511,7 +1510,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
         err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, LAG, 0>, dim3((unsigned)(groups * P)),
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
-                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, flag, parts);
+                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, lbd, parts);
         return true;
     } else {
         // one group of P workgroups; the tagged exchange's arguments are unused
@@ -1520,7 +1519,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         void* args[] = {(void*)&x,        (void*)&w,        (void*)&b,        (void*)&y,      (void*)&outer,
                         (void*)&inner,    (void*)&pcap,     (void*)&eps,      (void*)&ctrl,   (void*)&stats,
                         (void*)&xchg,     (void*)&mean_out, (void*)&rstd_out, (void*)&groups, (void*)&spin,
-                        (void*)&force,    (void*)&counters, (void*)&flag,     (void*)&parts};
+                        (void*)&force,    (void*)&counters, (void*)&lbd,      (void*)&parts};
         // a cooperative launch cannot carry events: armed ones bracket it as markers
         const LaunchEvents ev = take_launch_events();
         if (ev.start) (void)hipEventRecord(ev.start, st);
@@ -1594,10 +1593,10 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     char* base = static_cast<char*>(ws);
     LnCtrl* ctrl = reinterpret_cast<LnCtrl*>(base + lay.off_ctrl);
     uint32_t* counters = reinterpret_cast<uint32_t*>(base + lay.off_counter);
-    uint32_t* flag = reinterpret_cast<uint32_t*>(base + lay.off_flag);
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
     Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
     double* xchg = reinterpret_cast<double*>(base + lay.off_xchg);
+    double* lbd = reinterpret_cast<double*>(base + lay.off_lbd);
 
     // The single-read kernel, when a co-resident grid can hold every
     // sample's rows (on MI355X: samples of up to 256 x 4224 float4, about
@@ -1607,7 +1606,7 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
 #define NORMFWD_TRY_SINGLE(F, DW, LG, PR)                                                                     \
-    try_launch_single<F, DW, LG, PR>(x, w, b, y, outer, inner, eps, ctrl, counters, flag, stats, parts, xchg,     \
+    try_launch_single<F, DW, LG, PR>(x, w, b, y, outer, inner, eps, ctrl, counters, lbd, stats, parts, xchg,      \
                                  lay.P_cap, mean_out, rstd_out, st, err)
         const bool wide = ln_wide_tile(outer, inner);
         const bool launched =
