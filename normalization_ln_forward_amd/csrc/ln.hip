@@ -984,7 +984,7 @@ __device__ __forceinline__ bool ctl_steps(int64_t t0, int64_t steps, F& f)
     }
 }
 
-template <int F4PT, int DW, int LAG, int PROTO>
+template <int F4PT, int DW, int LAG, int PROTO, bool ILV>
 __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, float* y_all, int64_t outer_all,
                      int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, double* xchg_all,
@@ -1200,15 +1200,22 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     const uint32_t last_unit = (uint32_t)(nv - 1);
     auto addr = [&](int k) -> uint32_t { return std::min(index(k), last_unit); };
     f4 T[NT][F4PT];  // register tiles; sample s lives in tile s % NT
-    auto load = [&](int r, int64_t s) __attribute__((always_inline)) {
-        // past the last sample every lane reads the last sample's first
-        // float4 (index masked to 0): same instruction count, no traffic.
-        // Streaming loads: x is read once here (measured ~1% faster).
+    // Sample s's row and the mask applied to every index: past the last
+    // sample every lane reads the last sample's first float4 (index masked to
+    // 0): same instruction count, no traffic.
+    struct Row {
+        const f4* xs;
+        uint32_t m;
+    };
+    auto row = [&](int64_t s) __attribute__((always_inline)) {
         const int64_t sb = s < outer ? s : outer - 1;
-        const uint32_t m = s < outer ? 0xFFFFFFFFu : 0u;
-        const f4* xs = reinterpret_cast<const f4*>(x + sb * sstride);
+        return Row{reinterpret_cast<const f4*>(x + sb * sstride), s < outer ? 0xFFFFFFFFu : 0u};
+    };
+    // Streaming loads: x is read once here (measured ~1% faster).
+    auto load = [&](int r, int64_t s) __attribute__((always_inline)) {
+        const Row q = row(s);
 #pragma unroll
-        for (int k = 0; k < F4PT; ++k) T[r][k] = ld_nt(xs + (addr(k) & m));
+        for (int k = 0; k < F4PT; ++k) T[r][k] = ld_nt(q.xs + (addr(k) & q.m));
     };
     for (int which = 0; which < 2; ++which) {
         // weight / bias rows -> LDS: all loads in flight first, then the LDS stores
@@ -1253,10 +1260,17 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
             }
         }
         __syncthreads();  // barrier t: sample t-LAG's statistics are in LDS
+        // tile r then receives sample t-LAG+NT (in the first LAG iterations it
+        // is still empty); the loads are unconditional so that every iteration
+        // issues the same memory operations
         if constexpr (norm) {
             const int64_t s = t - LAG;
             const f4 st = s_stats[s & 1];
             f4* y4 = reinterpret_cast<f4*>(y + s * sstride);
+            // ILV: each element's store is followed at once by its register's
+            // refill, so loads enter the queue while the stores drain; else
+            // all stores, then all loads
+            const Row q = row(t - LAG + NT);
 #pragma unroll
             for (int k = 0; k < F4PT; ++k) {
                 if (valid(k)) {
@@ -1265,12 +1279,12 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
                     const f4 bv = bias ? b_s[k * RW + tid] : f4(0.0f);
                     st_nt(tt * wv + bv, y4 + index(k));
                 }
+                if constexpr (ILV) T[r][k] = ld_nt(q.xs + (addr(k) & q.m));
             }
+            if constexpr (!ILV) load(r, t - LAG + NT);
+        } else {
+            load(r, t - LAG + NT);
         }
-        // tile r now receives sample t-LAG+NT (in the first LAG iterations it
-        // is still empty); the load is unconditional so that every iteration
-        // issues the same memory operations
-        load(r, t - LAG + NT);
     };
     // the first LAG iterations have nothing to normalize yet; from then on
     // every iteration does (t < steps = outer + LAG, and outer >= 1)
@@ -1464,11 +1478,11 @@ static int coresident(const void* fn, size_t lds, int threads)
     return cap;
 }
 
-// Launches ln_single_ctl_kernel<F4PT, DW, LAG, PROTO> when a co-resident grid
+// Launches ln_single_ctl_kernel<F4PT, DW, LAG, PROTO, ILV> when a co-resident grid
 // of one workgroup per F4PT rows of DW * 64 float4 holds every sample's rows
 // (false: it cannot, nothing launched).  PROTO 0, the tagged exchange: an
 // ordinary launch; PROTO 1, the last workgroup merging: a cooperative one.
-template <int F4PT, int DW, int LAG, int PROTO>
+template <int F4PT, int DW, int LAG, int PROTO, bool ILV>
 static bool try_launch_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                               int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd, f4* stats,
                               Partial* parts, double* xchg, int64_t P_cap, float* mean_out, float* rstd_out,
@@ -1486,7 +1500,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
     // every launch on a workspace writing the same slots).
     const size_t lds_max = (size_t)2 * F4PT * rw * sizeof(f4);
     if (lds_max + 8 * 1024 > (size_t)d.max_lds_per_block) return false;
-    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, LAG, PROTO>);
+    const void* fn = reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, LAG, PROTO, ILV>);
     const int threads = (DW + 1) * kWave;
     const int cap = coresident(fn, lds_max, threads);
     if (cap < P) return false;
@@ -1508,7 +1522,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         // as many groups of P workgroups (each taking every groups-th
         // sample) as stay co-resident, at most one per sample
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
-        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, LAG, 0>, dim3((unsigned)(groups * P)),
+        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, LAG, 0, ILV>, dim3((unsigned)(groups * P)),
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
                             mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, lbd, parts);
         return true;
@@ -1545,7 +1559,7 @@ static void single_grid(int64_t inner, int64_t& P, int& cap)
     DeviceInfo d;
     cap = 0;
     if (!device_info(d) || lds + 8 * 1024 > (size_t)d.max_lds_per_block) return;
-    cap = coresident(reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, LAG, 0>), lds,
+    cap = coresident(reinterpret_cast<const void*>(&ln_single_ctl_kernel<F4PT, DW, LAG, 0, true>), lds,
                      (DW + 1) * kWave);
 }
 
@@ -1559,6 +1573,24 @@ static bool ln_wide_tile(int64_t outer, int64_t inner)
     single_grid<kLnTileF4, kLnTileWaves, kLnTileLag>(inner, Pn, capn);
     if (capn < Pn) return true;
     return outer >= 8 && Pw <= capw && Pw * 10 >= (int64_t)capw * 9;
+}
+
+// Whether the 8 x 8 tile interleaves its stores with the next sample's loads
+// (the wide tile always does: it runs where a sample takes at least 90% of
+// the co-resident grid).  Measured per call on MI355X, interleaved against
+// all stores, then all loads, by workgroups per sample P out of 256
+// co-resident: P = 256 [4, 4M] 27.7 vs 30.7 us; 192 [16, 3M] 74.3 vs 76.2;
+// 128 [64, 2M] 176.9 vs 180.6, [32, 2M] 92.1 vs 93.9, [4, 2M] 16.5 vs 18.9;
+// 112 [16, 1.75M] 44.6 vs 45.0; 96 [16, 1.5M] 40.4 vs 39.8, [8, 1.5M] 23.2
+// vs 21.5; 80 [16, 1.25M] 34.2 vs 33.3; 64 [16, 1M] 27.8 vs 25.4, [32, 1M]
+// 50.0 vs 49.5; 16 [64, 256K] 29.1 vs 27.5; 4 [128, 64K] 16.1 vs 15.7; 1
+// [256, 16K] 12.2 vs 11.8.  So: where a sample spans at least half the grid.
+static bool ln_tile_interleave(int64_t inner)
+{
+    int64_t P = 0;
+    int cap = 0;
+    single_grid<kLnTileF4, kLnTileWaves, kLnTileLag>(inner, P, cap);
+    return 2 * P >= cap;
 }
 
 // Measured on MI355X (split against the single-read kernel with the tile
@@ -1605,15 +1637,18 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     // (in place the tagged exchange does not run and variant 1 takes the split)
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
-#define NORMFWD_TRY_SINGLE(F, DW, LG, PR)                                                                     \
-    try_launch_single<F, DW, LG, PR>(x, w, b, y, outer, inner, eps, ctrl, counters, lbd, stats, parts, xchg,      \
-                                 lay.P_cap, mean_out, rstd_out, st, err)
+#define NORMFWD_TRY_SINGLE(F, DW, LG, PR, IL)                                                                 \
+    try_launch_single<F, DW, LG, PR, IL>(x, w, b, y, outer, inner, eps, ctrl, counters, lbd, stats, parts, xchg,  \
+                                         lay.P_cap, mean_out, rstd_out, st, err)
         const bool wide = ln_wide_tile(outer, inner);
         const bool launched =
-            protocol == 1 ? (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, kLnWideLag, 0)
-                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 0))
-                          : (wide ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, kLnWideLag, 1)
-                                  : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 1));
+            wide ? (protocol == 1 ? NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, kLnWideLag, 0, true)
+                                  : NORMFWD_TRY_SINGLE(kLnWideF4, kLnWideWaves, kLnWideLag, 1, true))
+            : ln_tile_interleave(inner)
+                ? (protocol == 1 ? NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 0, true)
+                                 : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 1, true))
+                : (protocol == 1 ? NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 0, false)
+                                 : NORMFWD_TRY_SINGLE(kLnTileF4, kLnTileWaves, kLnTileLag, 1, false));
 #undef NORMFWD_TRY_SINGLE
         if (launched) return err;
     }

@@ -15,8 +15,8 @@ import normalization_ln_forward_amd as nf  # noqa: E402
 from normalization_ln_forward_amd import synth  # noqa: E402
 
 # (outer, inner, seed, workload): 3 workgroups per sample with a ragged last row, 32, 62 with a ragged last
-# row, and 256 (every lane of the gather busy) on the N(100, 0.01) stress input, with the 8 x 8 tile; 237
-# with a ragged last row with the wide 11 x 6 tile
+# row, and 256 (every lane of the gather busy, stores interleaved with the next sample's loads) on the
+# N(100, 0.01) stress input, with the 8 x 8 tile; 237 with a ragged last row with the wide 11 x 6 tile
 CASES = [(5, 40000, 11, "ln_16x64x256x256"), (4, 1 << 19, 12, "ln_16x64x256x256"),
          (9, 1000004, 14, "ln_16x64x256x256"), (3, 1 << 22, 13, "ln_stress_16x64x256x256"),
          (8, 4000000, 15, "ln_16x64x256x256")]
