@@ -1577,14 +1577,16 @@ static bool ln_wide_tile(int64_t outer, int64_t inner)
 
 // Whether the 8 x 8 tile interleaves its stores with the next sample's loads
 // (the wide tile always does: it runs where a sample takes at least 90% of
-// the co-resident grid).  Measured per call on MI355X, interleaved against
-// all stores, then all loads, by workgroups per sample P out of 256
-// co-resident: P = 256 [4, 4M] 27.7 vs 30.7 us; 192 [16, 3M] 74.3 vs 76.2;
-// 128 [64, 2M] 176.9 vs 180.6, [32, 2M] 92.1 vs 93.9, [4, 2M] 16.5 vs 18.9;
-// 112 [16, 1.75M] 44.6 vs 45.0; 96 [16, 1.5M] 40.4 vs 39.8, [8, 1.5M] 23.2
-// vs 21.5; 80 [16, 1.25M] 34.2 vs 33.3; 64 [16, 1M] 27.8 vs 25.4, [32, 1M]
-// 50.0 vs 49.5; 16 [64, 256K] 29.1 vs 27.5; 4 [128, 64K] 16.1 vs 15.7; 1
-// [256, 16K] 12.2 vs 11.8.  So: where a sample spans at least half the grid.
+// the co-resident grid).  Measured per call on MI355X (median of 40
+// launches, compared builds writing one shared output buffer), interleaved
+// against all stores, then all loads, by workgroups per sample P out of 256
+// co-resident: P = 256 [4, 4M] 27.7 vs 30.3 us; 192 [16, 3M] 74.4 vs 77.0;
+// 128 [64, 2M] 176.9 vs 180.7, [32, 2M] 92.1 vs 94.3, [4, 2M] 16.4 vs 18.7;
+// 112 [16, 1.75M] 44.8 vs 45.0; 96 [16, 1.5M] 40.3 vs 40.0, [8, 1.5M] 23.3
+// vs 21.5; 80 [16, 1.25M] 34.2 vs 33.7; 64 [16, 1M] 27.3 vs 26.8, [32, 1M]
+// 49.6 vs 49.6, [8, 1M] 16.4 vs 17.3; 16 [64, 256K] 29.3 vs 27.7; 4 [128,
+// 64K] 16.1 vs 16.4; 1 [256, 16K] 12.1 vs 11.9.  So: where a sample spans at
+// least half the grid.
 static bool ln_tile_interleave(int64_t inner)
 {
     int64_t P = 0;
