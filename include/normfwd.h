@@ -133,12 +133,16 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 forced silent and beside other kernels on other
  *                 streams).  Since readers need x intact until the end, in
  *                 place (y == x) this variant runs the split schedule;
- *             2 = single kernel in which the last workgroup to deliver a
- *                 sample's partial merges it and announces the statistics
- *                 (LN page, turn 6: last-block-done), the others waiting
- *                 for them (a control wave per workgroup does
- *                 the exchange beside the data waves of variant 1, which
- *                 read x once; in place is fine).  A cooperative launch, since its
+ *             2 = single kernel in which the last workgroup to arrive at
+ *                 a sample, by an atomic count, merges every workgroup's
+ *                 partial of it and announces the statistics (LN page,
+ *                 turn 6: last-block-done), the others waiting for them (a
+ *                 control wave per workgroup does the exchange beside the
+ *                 data waves of variant 1, which read x once; partials
+ *                 carry the launch's generation tag, so arrivals are
+ *                 counted an iteration ahead and the merger polls until
+ *                 every partial is current; in place is fine).  A
+ *                 cooperative launch, since its
  *                 waits need every workgroup resident.  The runtime grants
  *                 cooperative launches on a GPU to one process at a time:
  *                 after another, still running process has made one, this

@@ -73,6 +73,7 @@ struct LnLayout {
     size_t off_part;
     size_t off_xchg;  // control-wave kernel's exchange: per sample, P_cap tagged means then P_cap tagged M2s
     size_t off_lbd;   // control-wave kernel, last workgroup merging: per sample, tagged mean and rstd (fp64)
+    size_t off_lbdx;  // ... and its workgroups' moments: per sample, P_cap tagged means then P_cap tagged M2s
     size_t total;
 };
 // Byte offset, in an LN workspace, of the word the single kernels set when

@@ -220,6 +220,8 @@ LnLayout ln_layout(int64_t outer, int64_t inner)
     off += align256((NORMFWD_LN_XCHG_SLOT ? NORMFWD_LN_XCHG_SLOT : 2) * sizeof(double) * (size_t)outer * (size_t)L.P_cap);
     L.off_lbd = off;
     off += align256(2 * sizeof(double) * (size_t)outer);
+    L.off_lbdx = off;
+    off += align256(2 * sizeof(double) * (size_t)outer * (size_t)L.P_cap);
     L.total = off;
     return L;
 }
@@ -855,44 +857,67 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // moments the control wave gathers, so the gather rarely waits and the data
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
-// data waves, ctl_wave_last_block below, runs the chain drain, arrival
-// atomic, the last arrival's merge, its announcement and the readers' poll
-// once per sample: 140-141 us per call at [16, 4M], ~15 us of which the
-// cooperative launch costs, against 96-97 us.  With a pairwise merge, two
-// fp64 divisions per step on that chain, it took 160-161 us; with a flag
-// and then the statistics read after it, 163-164.)
+// data waves, ctl_wave_last_block below, puts the last arrival's merge and
+// announcement and the readers' poll on every sample's path: 125-126 us per
+// call at [16, 4M], ~15 us of which the cooperative launch costs, against
+// 93 us.)
 //
 // Control wave of ln_single_ctl_kernel with the last-workgroup-merges
 // exchange (LN page, turn 6: last-block-done), for ln_forward variant 2, a
 // cooperative launch (its waits need every workgroup resident; each wait
 // has a spin limit that sets the control block's error word instead of
 // hanging).  The data waves are those of the tagged exchange, unchanged, so
-// they never wait on another workgroup.  After barrier t:
+// they never wait on another workgroup.  Each workgroup counts its arrival
+// at a sample on that sample's counter (a ring of kRing) one iteration
+// early, and the arrival that finds P - 1 (mod P) before it merges the
+// sample.  After barrier t:
+//   take the count returned for sample t (issued an iteration ago) and
+//   issue this workgroup's arrival at sample t + 1;
 //   issue the loads of the statistics words of sample g = t - LAG + 1 (they
 //   were announced an iteration or more ago, and their round trip overlaps
 //   what follows);
-//   merge the data waves' moments of sample t into this workgroup's (n,
-//   mean, M2) (merge_wave_moments), publish it in its partial slot, drain
-//   the stores and count the arrival on the sample's counter (a ring of
-//   kRing); the last of the P arrivals merges the sample's partials in a
-//   fixed order (kway_merge, one wave), puts the counter back to 0, drains,
-//   and announces the sample's mean and rstd as two fp64 words tagged with
-//   the launch generation (ln_tag.hpp; a region only this kernel and the
-//   zeroing kernel write), so one poll both finds and reads them;
+//   merge the data waves' moments of sample t into this workgroup's (mean,
+//   M2) (merge_wave_moments) and store them as two words tagged with the
+//   launch generation in its slot of a region only this kernel and the
+//   zeroing kernel write;
+//   if elected for sample t, read every workgroup's words, polling any whose
+//   tag is not yet current (each owner stores them in its iteration t, so
+//   they land), merge them in a fixed order (the k-way pairwise update
+//   around workgroup 0's mean, one wave), take P back off the counter and
+//   announce the sample's mean and rstd as two tagged fp64 words
+//   (ln_tag.hpp), so one poll both finds and reads them;
 //   then poll sample g's words until both carry this launch's tag and leave
 //   its statistics in LDS before barrier t + 1.
+// The counter only elects the merger; the tags, not the order of arrival,
+// tell it which words are this launch's, so nothing on its path waits for
+// a store to complete or for an atomic's round trip.  Counters are never
+// reset: a sample's P arrivals see every residue mod P once, whatever count
+// the counter held before (even one a launch that gave up left behind).  A
+// workgroup issues its arrival at sample s + kRing in iteration s + kRing -
+// 1, after reading the statistics of sample s (kRing >= LAG + 1), which
+// exist only once all of sample s's arrivals were counted; the merger's
+// subtraction lands before its own arrival at sample s + kRing (same
+// address, same wave), so each count stays below 2P.  Measured per call at
+// [16, 4M]: 140-144 us with the partials stored, drained and then counted
+// and the counter reset, stored and drained before the announcement (the
+// last arrival then kept merging every sample, each of its iterations ~7.7
+// us against ~5.8 us for the data, and the whole grid ran at its pace);
+// 133.9 us with the tagged words and the count issued right after them;
+// 125-126 us with the count issued an iteration early.  Merging sample t
+// one iteration later, when every workgroup's words have surely landed,
+// measured 128.5 us; a lag of 4 samples (with a ring of 8) 125.6.
 // Every workgroup derives mean hi/lo and rstd from the same two words.  The
 // last workgroup out advances the generation.
 template <int DW, int LAG>
 __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t* cnt, const double* cnt_inv,
-                                    f4* s_stats, int64_t outer, int64_t P, int64_t P_cap, int64_t p,
-                                    uint32_t n_mine, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd,
-                                    Partial* parts, f4* stats, float* mean_out, float* rstd_out)
+                                    const float* wg_cnt, f4* s_stats, int64_t outer, int64_t inner, int64_t P,
+                                    int64_t P_cap, int64_t p, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd,
+                                    double* lbdx, f4* stats, float* mean_out, float* rstd_out)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t target = dev_load(&ctrl->gen) + 1u;
     const uint32_t tag = ln_tag_of(target);
-    const double inv_mine = inv_count_f64(n_mine);
+    const double inv_mine = inv_count_f64((uint32_t)wg_cnt[p]);
     const int64_t steps = outer + LAG;
     // (mean hi, mean lo, rstd) from the tagged words
     auto unpack = [](double tm, double tr) {
@@ -900,31 +925,87 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
         const float hi = (float)m;
         return f4{hi, (float)(m - (double)hi), (float)ln_untag(tr), 0.0f};
     };
+    static_assert(kRing >= LAG + 1, "an arrival is counted before the statistics kRing samples back are read");
+    auto arrive = [&](int64_t s) {
+        return __hip_atomic_fetch_add(counters + (s % kRing) * kCounterStride, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // count before this workgroup's arrival at the next sample (lane 0)
+    uint32_t before_next = lane == 0 ? arrive(0) : 0u;
     __syncthreads();  // prologue: w/b in LDS
     for (int64_t t = 0; t < steps; ++t) {
         __syncthreads();  // barrier t: the wave moments of sample t are in LDS
         const int64_t g = t - (LAG - 1);
         const bool gather = g >= 0 && g < outer;
+        // sample t's arrival was counted an iteration ago; count sample t + 1's now
+        const uint32_t before = before_next;
+        if (t + 1 < outer && lane == 0) before_next = arrive(t + 1);
         double tm = 0.0, tr = 0.0;
         if (gather && lane == 0) {
             tm = dev_load(lbd + 2 * g);
             tr = dev_load(lbd + 2 * g + 1);
         }
         if (t < outer) {
-            Partial q{};
-            q.n = (double)n_mine;
-            merge_wave_moments<DW>(red[t & 1], cnt, cnt_inv, inv_mine, q.mean, q.m2);
-            uint32_t* counter = counters + (t % kRing) * kCounterStride;
-            uint32_t last = 0;
-            if (lane == 0) last = deliver_partial(parts + t * P_cap + p, q, counter, P) ? 1u : 0u;
-            if (__builtin_amdgcn_readfirstlane(last)) {
-                double n, m, m2;
-                kway_merge<true>(parts + t * P_cap, P, n, m, m2);
+            // this workgroup's (mean, M2) of sample t, tagged, into its slot
+            double mean, m2;
+            merge_wave_moments<DW>(red[t & 1], cnt, cnt_inv, inv_mine, mean, m2);
+            double* xs = lbdx + t * 2 * P_cap;  // P_cap tagged means, then P_cap tagged M2s
+            if (lane == 0) {
+                dev_store(xs + p, ln_tag_word(mean, tag));
+                dev_store(xs + P_cap + p, ln_tag_word(m2, tag));
+            }
+            if (__builtin_amdgcn_readfirstlane(lane == 0 && (before + 1u) % (uint32_t)P == 0u ? 1u : 0u)) {
+                // the last arrival: k-way merge of the P tagged words around
+                // workgroup 0's mean (lane l: workgroups l, l + 64, ...)
+                double c = 0.0, A = 0.0, B = 0.0;
+                for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
+                    double a[4], b2[4];
+                    auto load_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int64_t j = j0 + lane + (int64_t)u * kWave;
+                            const int64_t jj = j < P ? j : p;
+                            a[u] = dev_load(xs + jj);
+                            b2[u] = dev_load(xs + P_cap + jj);
+                        }
+                    };
+                    auto block_ok = [&]() __attribute__((always_inline)) {
+                        bool ok = true;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) ok = ok && ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag);
+                        return __all(ok);
+                    };
+                    load_block();
+                    for (uint32_t it = 0; !block_ok(); ++it) {
+                        if (it == kSpinLimit) {
+                            if (lane == 0) dev_store(&ctrl->error, 1u);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                        load_block();
+                    }
+                    if (j0 == 0) c = ln_untag(lane_f64(a[0], 0));  // workgroup 0's mean
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int64_t j = j0 + lane + (int64_t)u * kWave;
+                        if (j < P) {
+                            const double nj = (double)wg_cnt[j];
+                            const double d = ln_untag(a[u]) - c;
+                            A += nj * d;
+                            B += ln_untag(b2[u]) + nj * (d * d);
+                        }
+                    }
+                }
+                A = wave_total(A);
+                B = wave_total(B);
                 if (lane == 0) {
-                    const double var = n > 0.0 ? m2 / n : 0.0;
+                    const double n = (double)inner;
+                    const double md = A / n;
+                    const double m = c + md, m2s = fmax(B - A * md, 0.0);
+                    const double var = m2s / n;
                     const double wm = ln_tag_word(m, tag), wr = ln_tag_word(1.0 / sqrt(var + (double)eps), tag);
-                    dev_store(counter, 0u);
-                    vmem_drain();
+                    __hip_atomic_fetch_sub(counters + (t % kRing) * kCounterStride, (uint32_t)P, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                     dev_store(lbd + 2 * t, wm);
                     dev_store(lbd + 2 * t + 1, wr);
                     const f4 st = unpack(wm, wr);
@@ -989,7 +1070,7 @@ __global__ void __launch_bounds__((DW + 1) * kWave)
 ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, float* y_all, int64_t outer_all,
                      int64_t inner, int64_t P_cap, float eps, LnCtrl* ctrl, f4* stats_all, double* xchg_all,
                      float* mean_all, float* rstd_all, int64_t groups, uint32_t spin_limit, uint32_t silent_mask,
-                     uint32_t* counters, double* lbd, Partial* parts)
+                     uint32_t* counters, double* lbd, double* lbdx)
 {
     constexpr int RW = DW * kWave;  // row width in float4 = data threads
     constexpr int NT = LAG + 2;     // register tiles per data thread
@@ -1037,9 +1118,9 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
             cnt[0][lane] = n;
             cnt_inv[0][lane] = inv_count_f64(n);
         }
-        const uint32_t n_mine = ctl_wg_elems<F4PT, DW>((uint32_t)p, (uint32_t)P, nv);
-        ctl_wave_last_block<DW, LAG>(red, cnt[0], cnt_inv[0], s_stats, outer, P, P_cap, p, n_mine, eps, ctrl,
-                                     counters, lbd, parts, stats, mean_out, rstd_out);
+        for (int64_t j = lane; j < P; j += kWave) wg_cnt[j] = (float)ctl_wg_elems<F4PT, DW>((uint32_t)j, (uint32_t)P, nv);
+        ctl_wave_last_block<DW, LAG>(red, cnt[0], cnt_inv[0], wg_cnt, s_stats, outer, inner, P, P_cap, p, eps, ctrl,
+                                     counters, lbd, lbdx, stats, mean_out, rstd_out);
         return;
     }
     if (tid >= RW) {
@@ -1485,7 +1566,7 @@ static int coresident(const void* fn, size_t lds, int threads)
 template <int F4PT, int DW, int LAG, int PROTO, bool ILV>
 static bool try_launch_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                               int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd, f4* stats,
-                              Partial* parts, double* xchg, int64_t P_cap, float* mean_out, float* rstd_out,
+                              double* lbdx, double* xchg, int64_t P_cap, float* mean_out, float* rstd_out,
                               hipStream_t st, hipError_t& err)
 {
     DeviceInfo d;
@@ -1524,7 +1605,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(outer, cap / P));
         err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, LAG, 0, ILV>, dim3((unsigned)(groups * P)),
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
-                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, lbd, parts);
+                            mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, lbd, lbdx);
         return true;
     } else {
         // one group of P workgroups; the tagged exchange's arguments are unused
@@ -1533,7 +1614,7 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         void* args[] = {(void*)&x,        (void*)&w,        (void*)&b,        (void*)&y,      (void*)&outer,
                         (void*)&inner,    (void*)&pcap,     (void*)&eps,      (void*)&ctrl,   (void*)&stats,
                         (void*)&xchg,     (void*)&mean_out, (void*)&rstd_out, (void*)&groups, (void*)&spin,
-                        (void*)&force,    (void*)&counters, (void*)&lbd,      (void*)&parts};
+                        (void*)&force,    (void*)&counters, (void*)&lbd,      (void*)&lbdx};
         // a cooperative launch cannot carry events: armed ones bracket it as markers
         const LaunchEvents ev = take_launch_events();
         if (ev.start) (void)hipEventRecord(ev.start, st);
@@ -1628,7 +1709,7 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     LnCtrl* ctrl = reinterpret_cast<LnCtrl*>(base + lay.off_ctrl);
     uint32_t* counters = reinterpret_cast<uint32_t*>(base + lay.off_counter);
     f4* stats = reinterpret_cast<f4*>(base + lay.off_stats);
-    Partial* parts = reinterpret_cast<Partial*>(base + lay.off_part);
+    double* lbdx = reinterpret_cast<double*>(base + lay.off_lbdx);
     double* xchg = reinterpret_cast<double*>(base + lay.off_xchg);
     double* lbd = reinterpret_cast<double*>(base + lay.off_lbd);
 
@@ -1640,7 +1721,7 @@ hipError_t launch_ln_single(const float* x, const float* w, const float* b, floa
     if (ln_single_supported(inner, x, w, b, y) && !(protocol == 1 && x == y)) {
         hipError_t err = hipSuccess;
 #define NORMFWD_TRY_SINGLE(F, DW, LG, PR, IL)                                                                 \
-    try_launch_single<F, DW, LG, PR, IL>(x, w, b, y, outer, inner, eps, ctrl, counters, lbd, stats, parts, xchg,  \
+    try_launch_single<F, DW, LG, PR, IL>(x, w, b, y, outer, inner, eps, ctrl, counters, lbd, stats, lbdx, xchg,   \
                                          lay.P_cap, mean_out, rstd_out, st, err)
         const bool wide = ln_wide_tile(outer, inner);
         const bool launched =
