@@ -250,18 +250,17 @@ __device__ __forceinline__ double block_sum(double v, double* red)
 // crosses workgroups (partial moments, statistics, counters, exchange
 // words) is only ever accessed with agent-scope atomic loads and stores,
 // which the gfx950 code generator issues as device-coherent accesses (sc1)
-// served at the device's coherence point.  A writer waits for its data
-// stores to complete (s_waitcnt vmcnt(0)) before it counts its arrival, so
-// the workgroup that sees the last arrival reads every partial; words that
-// announce themselves (generation-tagged, see ln_tag.hpp) need no flag: an
-// aligned 8-byte store is seen whole, and a reader takes a word only when
-// it carries the current tag.
+// served at the device's coherence point.  In the split schedule's fused
+// tail a writer waits for its partial's stores to complete (s_waitcnt
+// vmcnt(0)) before it counts its arrival, so the workgroup that sees the
+// last arrival reads every partial.  The single kernels exchange words that
+// announce themselves instead (generation-tagged, see ln_tag.hpp), which
+// need no flag and no such wait: an aligned 8-byte store is seen whole, and
+// a reader takes a word only when it carries the current tag.
 //
 // Arrival counters of the single kernel live in a ring of kRing slots
-// (sample t uses slot t % kRing), each on its own 128-byte line.  Reuse is
-// safe: the merger of sample t resets the slot, drains, and only then
-// announces the statistics of sample t, and no workgroup arrives at sample
-// t + kRing before it has read them.
+// (sample t uses slot t % kRing), each on its own 128-byte line, and are
+// never reset (see ctl_wave_last_block for why reuse is safe).
 
 // Wait until this thread's earlier vector-memory accesses have completed.
 __device__ __forceinline__ void vmem_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -11,7 +11,7 @@
         it reads for the plain device copy of N MiB the same command ran
         (torch's copy kernel: N MiB read, N MiB written), so the result is in
         bytes whatever unit the counter uses.  With --json, the entries are
-        written to that file together with the hash of the kernel sources, so
+        written to that file together with the hash of the kernels' code (comments removed), so
         bench.py reports them only while the kernels are unchanged.
 
     python -m normalization_ln_forward_amd.profiling counters <counter_collection.csv>...
@@ -47,11 +47,27 @@ KERNEL_SOURCES = {
 }
 
 
-def source_sha(files):
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_text(text):
+    """The text the compiler acts on: comments and blank lines removed, trailing blanks trimmed (so a
+    change to comments alone keeps a measurement valid)."""
+    text = _COMMENTS.sub("", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def source_sha(files, read=None):
+    """Hash of the code (see code_text) of the named csrc files; `read(name) -> str` overrides reading
+    them from the package's csrc/."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(code_text(text).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -44,3 +44,27 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cpu, key
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
+
+
+def test_traffic_is_reported_only_for_unchanged_kernel_code():
+    """roofline.traffic comes from the committed counter summary only while the profiled kernels' code is
+    the code that was measured: the hash covers the sources with comments and blank lines removed, so a
+    change to code changes it and a change to comments alone does not."""
+    from normalization_ln_forward_amd import profiling
+
+    def sha(text):
+        return profiling.source_sha(["k.hip"], read=lambda name: text)
+
+    base = "__global__ void k(float* y) {\n    y[0] = 1.0f;  // one\n}\n"
+    assert sha(base) == sha("// a kernel\n__global__ void k(float* y) {\n    y[0] = 1.0f;\n}\n\n")
+    assert sha(base) == sha("/* a\n   kernel */\n__global__ void k(float* y) {   \n    y[0] = 1.0f; /* x */\n}\n")
+    assert sha(base) != sha("__global__ void k(float* y) {\n    y[0] = 2.0f;\n}\n")
+    assert sha(base) != sha("__global__ void k(float* y) {\n    y[1] = 1.0f;\n}\n")
+    # the committed summary matches the current sources kernel by kernel
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
+                           "hbm_traffic_bench_workloads.json")) as f:
+        entries = json.load(f)
+    for k, e in entries.items():
+        assert e["source_sha"] == profiling.source_sha(profiling.KERNEL_SOURCES[k]), k
