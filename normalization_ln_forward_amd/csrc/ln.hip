@@ -171,6 +171,10 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 // 352.7 / 352.1 / 364.0, [32, 4M] 183.5 / 182.9 / 185.4, [16, 4M] 96.9 /
 // 96.2 / 96.3, [8, 4M] 53.6 / 50.1 / 49.4 (last-workgroup merges at [16,
 // 4M]: 167-168 / 164-165 us per call).  The 8 x 8 tile spills with 3.
+// (Those figures predate the store/refill interleave.  With it, at [16, 4M]:
+// 11 x 6 with lags 2 / 3 / 4 95.1 / 93.2 / 93.3 us, 10 x 7 with lags 2 / 3
+// 95.7 / 94.3, 13 x 5 with a lag of 3 93.5, 8 x 8 with a lag of 2 94.8;
+// 12 x 6, 8 x 8 with a lag of 3 and 13 x 5 with 4 spill.)
 constexpr int kLnTileWaves = 8;
 constexpr int kLnTileF4 = 8;
 constexpr int kLnTileLag = 2;
