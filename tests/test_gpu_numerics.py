@@ -262,3 +262,23 @@ def test_ln_last_block_election_survives_leftover_counts(shape):
         nf.ln_forward_workspace_check(ws)
     ref = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]))
     _close(_np(clean), ref, what=f"variant 2 {shape}")
+
+
+def test_ln_last_block_past_the_tag_cycle():
+    """300 consecutive variant-2 calls on one workspace, past the 255-launch cycle of the generation tags
+    that its partials and statistics words carry: every output equals the first bit for bit, no wait
+    gives up, and the completion counter is back at zero."""
+    _say("ln last-block 300 calls")
+    shape = (6, 1 << 19)
+    d = synth.make("ln_stress_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=31)
+    _, ws = nf.alloc_workspace(nf.ln_forward_workspace_size(*shape), "cuda")
+    nf.ln_forward_workspace_init(ws)
+    first = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=2, workspace=ws)
+    for i in range(1, 300):
+        y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=2, workspace=ws)
+        if not torch.equal(y, first):
+            pytest.fail(f"call {i} differs from the first")
+    torch.cuda.synchronize()
+    gen, done, err, recomputed, gen_ctl = _ctrl(ws)
+    assert done == 0 and err == 0 and gen == 300, (gen, done, err)
+    _close(_np(first), oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"])), what="variant 2, 300 calls")
