@@ -48,11 +48,13 @@
 //          moments that do not arrive within a bounded wait (their workgroup
 //          is not resident) are computed by the reader from x, with the same
 //          bits (so it never runs in place: y == x takes the split);
-//          variant 2 (a cooperative launch): the last workgroup to deliver
-//          a sample's partial merges it and announces the statistics (LN
-//          page, turn 6: last-block-done; generation-tagged words serve as
-//          the flag), done by the control wave of ln_single_ctl_kernel
-//          (ctl_wave_last_block) beside the same data waves.
+//          variant 2 (a cooperative launch): the last workgroup to arrive at
+//          a sample (an atomic count, issued an iteration ahead) merges
+//          every workgroup's generation-tagged partial of it and announces
+//          the statistics as tagged words (LN page, turn 6: last-block-done;
+//          the tags serve as the flags), done by the control wave of
+//          ln_single_ctl_kernel (ctl_wave_last_block) beside the same data
+//          waves.
 //          Samples too large for the kernel's co-resident grid take the
 //          split under every variant.
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
