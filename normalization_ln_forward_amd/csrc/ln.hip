@@ -162,8 +162,14 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 // 53.7 vs 54.6, [4, 4M] 30.4 vs 30.4, [2, 4M] 22.0 vs 20.4, [1, 4M] 15.2 vs
 // 14.2, [16, 3M] 77.3 vs 76.3, [32, 3M] 147.0 vs 146.5, [16, 2M] 52.8 vs
 // 50.0, [32, 1M] 52.6 vs 49.4, [8, 1M] 21.4 vs 17.1, [256, 16K] 12.1 vs
-// 11.6.  So the wide tile runs where a sample fills at least 90% of the
-// co-resident grid (one group) and there are at least 8 samples, and where
+// 11.6.  With the store/refill interleave (both tiles; kernel us, median of
+// 40 launches, one shared output buffer): [1, 4M] 14.8 vs 14.4, [2, 4M] 19.2
+// vs 18.2, [3, 4M] 22.1 vs 22.0, [4, 4M] 26.8 vs 27.5, [5, 4M] 31.0 vs 34.3,
+// [6, 4M] 37.3 vs 39.5, [7, 4M] 42.9 vs 45.9, [4, 4000000] 25.4 vs 28.7,
+// [6, 3900000] 35.3 vs 39.7, [16, 3.5M] 83.2 vs 83.6, [16, 3M] 74.1 vs 74.9,
+// [8, 3M] 38.7 vs 39.6, [32, 3M] 144.3 vs 142.7, [16, 2.5M] 68.4 vs 67.2.
+// So the wide tile runs where a sample fills at least 90% of the
+// co-resident grid (one group) and there are at least 4 samples, and where
 // the 8 x 8 tile cannot hold a sample.  The choice depends on the shape and
 // the device only, as the tagged exchange needs (a workspace of one shape
 // always sees the same tile).
@@ -1658,7 +1664,7 @@ static bool ln_wide_tile(int64_t outer, int64_t inner)
     single_grid<kLnWideF4, kLnWideWaves, kLnWideLag>(inner, Pw, capw);
     single_grid<kLnTileF4, kLnTileWaves, kLnTileLag>(inner, Pn, capn);
     if (capn < Pn) return true;
-    return outer >= 8 && Pw <= capw && Pw * 10 >= (int64_t)capw * 9;
+    return outer >= 4 && Pw <= capw && Pw * 10 >= (int64_t)capw * 9;
 }
 
 // Whether the 8 x 8 tile interleaves its stores with the next sample's loads

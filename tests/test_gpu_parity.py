@@ -168,6 +168,10 @@ LN_CASES = [
     (8, 4000000, True, 2),
     (2, 4325376, True, 1),
     (2, 4325376, True, 2),
+    # the wide tile from 4 samples on: 5 samples of 975,000 float4 (222 workgroups, ragged last row),
+    # no affine
+    (5, 3900000, False, 1),
+    (5, 3900000, False, 2),
     # the 8 x 8 tile with its stores interleaved with the next sample's loads (a sample spans at least half
     # the grid): 153 workgroups per sample, the last with 5 rows, the last row with 360 of 512 float4
     (3, 2500000, True, 1),
