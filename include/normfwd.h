@@ -76,8 +76,8 @@ const char* normfwd_last_error(void);
  * kernel's duration with no marker packets between kernels.  For an entry
  * point that launches several kernels, the first one is timed (ln_forward
  * variant 0: the moments kernel; use ln_forward_apply to time the normalize
- * kernel).  The cooperative launch of ln_forward variant 2 cannot carry
- * events; there they are recorded as markers just before and after it.  The
+ * kernel).  The cooperative launch of ln_forward variant 2 in place cannot
+ * carry events; there they are recorded as markers just before and after it.  The
  * events stay armed until a launch takes them or this is called again
  * (NULL, NULL disarms).  Always NORMFWD_OK. */
 normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
@@ -141,13 +141,19 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 data waves of variant 1, which read x once; partials
  *                 carry the launch's generation tag, so arrivals are
  *                 counted an iteration ahead and the merger polls until
- *                 every partial is current; in place is fine).  A
- *                 cooperative launch, since its
- *                 waits need every workgroup resident.  The runtime grants
- *                 cooperative launches on a GPU to one process at a time:
- *                 after another, still running process has made one, this
- *                 variant returns NORMFWD_ERR_UNSUPPORTED and launches
- *                 nothing.
+ *                 every partial is current).  Not in place it is an
+ *                 ordinary launch: if a workgroup is not resident (so it
+ *                 never arrives and no merger is elected), a workgroup that
+ *                 has waited for a sample's statistics for the same bounded
+ *                 number of polls as in variant 1 merges the sample itself,
+ *                 computing the missing moments from x, with the same bits
+ *                 whoever merges.  In place (y == x) it is a cooperative
+ *                 launch, every workgroup resident, since x may be
+ *                 overwritten by then.  The runtime grants cooperative
+ *                 launches on a GPU to one process at a time: after
+ *                 another, still running process has made one, an in-place
+ *                 call of this variant returns NORMFWD_ERR_UNSUPPORTED and
+ *                 launches nothing.
  *             3 = automatic: variant 1 wherever it can run (it measured
  *                 faster than the split, or within 1 us of it on calls of
  *                 ~10 us, at every shape tried), otherwise variant 0 (also
@@ -176,10 +182,10 @@ normfwd_status ln_forward_workspace_init(void* workspace, size_t workspace_bytes
 /* Health check of the last-workgroup-merges kernel (ln_forward variant 2).
  * Its workgroups wait for one another; each wait gives up after a bounded
  * number of polls (a fraction of a second), which can only happen if the
- * workgroups of the cooperative launch were not all resident, and then
- * records the failure in the workspace instead of hanging.  (Variant 1
- * never records one: a workgroup whose moments do not arrive has them
- * computed by the others.)  This call waits
+ * workgroups of its cooperative launch (in place) were not all resident,
+ * and then records the failure in the workspace instead of hanging.
+ * (Variant 1, and variant 2 not in place, never record one: moments that
+ * do not arrive are computed by the waiting workgroups.)  This call waits
  * for the work queued on `stream` (it synchronizes, unlike every other entry
  * point, so it cannot be captured in a graph), reads that record and clears
  * it.  Returns NORMFWD_OK if no launch that used `workspace` since the last

@@ -131,7 +131,7 @@ normfwd_status ln_dispatch(const float* x, const float* weight, const float* bia
             return fail(NORMFWD_ERR_UNSUPPORTED,
                         "ln_forward: the cooperative launch of the last-workgroup-merges kernel was refused "
                         "(hipErrorIllegalState): another process that is still running has made a cooperative "
-                        "launch on this GPU; variants 0, 1 and 3 do not use one");
+                        "launch on this GPU; only variant 2 in place uses one");
         return hip_status(e, "ln_forward (single kernel) launch");
     }
     hipError_t e = normfwd::launch_ln_stats(x, outer, inner, eps, workspace, lay, mean_out, rstd_out, st);

@@ -48,13 +48,15 @@
 //          moments that do not arrive within a bounded wait (their workgroup
 //          is not resident) are computed by the reader from x, with the same
 //          bits (so it never runs in place: y == x takes the split);
-//          variant 2 (a cooperative launch): the last workgroup to arrive at
-//          a sample (an atomic count, issued an iteration ahead) merges
-//          every workgroup's generation-tagged partial of it and announces
-//          the statistics as tagged words (LN page, turn 6: last-block-done;
-//          the tags serve as the flags), done by the control wave of
-//          ln_single_ctl_kernel (ctl_wave_last_block) beside the same data
-//          waves.
+//          variant 2: the last workgroup to arrive at a sample (an atomic
+//          count, issued an iteration ahead) merges every workgroup's
+//          generation-tagged partial of it and announces the statistics as
+//          tagged words (LN page, turn 6: last-block-done; the tags serve as
+//          the flags), done by the control wave of ln_single_ctl_kernel
+//          (ctl_wave_last_block) beside the same data waves; an ordinary
+//          launch in which a sample nobody announces (a workgroup that is
+//          not resident never arrives) is merged by whoever waited for it,
+//          from x where moments are missing; in place a cooperative launch.
 //          Samples too large for the kernel's co-resident grid take the
 //          split under every variant.
 //   automatic (variant 3): ln_auto_variant picks variant 1 or the split by
@@ -869,15 +871,19 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
 // data waves, ctl_wave_last_block below, puts the last arrival's merge and
-// announcement and the readers' poll on every sample's path: 125-126 us per
-// call at [16, 4M], ~15 us of which the cooperative launch costs, against
-// 93 us.)
+// announcement and the readers' poll on every sample's path: 108-109 us per
+// call at [16, 4M] against 93 us.)
 //
 // Control wave of ln_single_ctl_kernel with the last-workgroup-merges
-// exchange (LN page, turn 6: last-block-done), for ln_forward variant 2, a
-// cooperative launch (its waits need every workgroup resident; each wait
-// has a spin limit that sets the control block's error word instead of
-// hanging).  The data waves are those of the tagged exchange, unchanged, so
+// exchange (LN page, turn 6: last-block-done), for ln_forward variant 2.
+// Not in place it is an ordinary launch (may_recompute): a wait that runs
+// out (a workgroup that is not resident neither arrives nor publishes, so
+// no merger is elected) is followed by the waiter merging the sample
+// itself, computing missing moments from x with the same bits, so the
+// result is the same bits whoever merges.  In place it is a cooperative
+// launch (x may be overwritten by then; every workgroup is resident) and a
+// wait that runs past its spin limit sets the control block's error word
+// instead.  The data waves are those of the tagged exchange, unchanged, so
 // they never wait on another workgroup.  Each workgroup counts its arrival
 // at a sample on that sample's counter (a ring of kRing) one iteration
 // early, and the arrival that finds P - 1 (mod P) before it merges the
@@ -908,28 +914,42 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // 1, after reading the statistics of sample s (kRing >= LAG + 1), which
 // exist only once all of sample s's arrivals were counted; the merger's
 // subtraction lands before its own arrival at sample s + kRing (same
-// address, same wave), so each count stays below 2P.  Measured per call at
+// address, same wave), so each count stays below 2P.  (When a workgroup
+// is not resident, a sample's statistics can come from a waiter before all
+// its arrivals; elections may then fall on other arrivals, including a
+// late one, but every merge, elected or not, announces the same bits, no
+// subtraction comes before a count of P, and a sample nobody merges is
+// merged by its waiters.)  Measured per call at
 // [16, 4M]: 140-144 us with the partials stored, drained and then counted
 // and the counter reset, stored and drained before the announcement (the
 // last arrival then kept merging every sample, each of its iterations ~7.7
 // us against ~5.8 us for the data, and the whole grid ran at its pace);
 // 133.9 us with the tagged words and the count issued right after them;
-// 125-126 us with the count issued an iteration early.  Merging sample t
-// one iteration later, when every workgroup's words have surely landed,
-// measured 128.5 us; a lag of 4 samples (with a ring of 8) 125.6.
+// 125-126 us with the count issued an iteration early; 108-109 us as an
+// ordinary launch (the cooperative one cost ~17 us per call).  Merging
+// sample t one iteration later, when every workgroup's words have surely
+// landed, measured 128.5 us; a lag of 4 samples (with a ring of 8) 125.6
+// (both with the cooperative launch).
 // Every workgroup derives mean hi/lo and rstd from the same two words.  The
 // last workgroup out advances the generation.
-template <int DW, int LAG>
+template <int F4PT, int DW, int LAG>
 __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t* cnt, const double* cnt_inv,
-                                    const float* wg_cnt, f4* s_stats, int64_t outer, int64_t inner, int64_t P,
-                                    int64_t P_cap, int64_t p, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd,
-                                    double* lbdx, f4* stats, float* mean_out, float* rstd_out)
+                                    const float* wg_cnt, f4* s_stats, const float* x, int64_t outer, int64_t inner,
+                                    int64_t P, int64_t P_cap, int64_t p, float eps, LnCtrl* ctrl, uint32_t* counters,
+                                    double* lbd, double* lbdx, f4* stats, float* mean_out, float* rstd_out,
+                                    bool may_recompute, uint32_t limit, bool silent, double* rc, uint32_t* rc_cnt,
+                                    double* rc_inv)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t target = dev_load(&ctrl->gen) + 1u;
     const uint32_t tag = ln_tag_of(target);
     const double inv_mine = inv_count_f64((uint32_t)wg_cnt[p]);
     const int64_t steps = outer + LAG;
+    const int64_t nv = inner / 4;
+    // polls before a wait gives up: with recompute allowed, then compute
+    // what is missing; without (a cooperative launch, every workgroup
+    // resident), set the error word and go on
+    const uint32_t wait = may_recompute ? limit : kSpinLimit;
     // (mean hi, mean lo, rstd) from the tagged words
     auto unpack = [](double tm, double tr) {
         const double m = ln_untag(tm);
@@ -941,8 +961,108 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
         return __hip_atomic_fetch_add(counters + (s % kRing) * kCounterStride, 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
     };
-    // count before this workgroup's arrival at the next sample (lane 0)
-    uint32_t before_next = lane == 0 ? arrive(0) : 0u;
+    // Merge sample s from every workgroup's tagged words (lane l: workgroups
+    // l, l + 64, ...; the k-way pairwise update around workgroup 0's mean)
+    // and announce its mean and rstd; returns the two announced words
+    // (uniform).  A word still missing after `wait` polls belongs to a
+    // workgroup that is not resident: with recompute allowed it is computed
+    // here from x with the same bits and stored in the owner's slot (the
+    // owner, once it runs, stores the same bits there); x of sample s is
+    // intact, since this path never runs in place.
+    auto merge_sample = [&](int64_t s, double& wm, double& wr) {
+        const double* xs = lbdx + s * 2 * P_cap;  // P_cap tagged means, then P_cap tagged M2s
+        double c = 0.0, A = 0.0, B = 0.0;
+        for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
+            double a[4], b2[4];
+            auto load_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t j = j0 + lane + (int64_t)u * kWave;
+                    const int64_t jj = j < P ? j : 0;
+                    a[u] = dev_load(xs + jj);
+                    b2[u] = dev_load(xs + P_cap + jj);
+                }
+            };
+            auto present = [&](int u) __attribute__((always_inline)) {
+                return j0 + lane + (int64_t)u * kWave >= P || (ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag));
+            };
+            auto block_ok = [&]() __attribute__((always_inline)) {
+                bool ok = true;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) ok = ok && present(u);
+                return __all(ok);
+            };
+            load_block();
+            bool late = false;
+            for (uint32_t it = 0; !block_ok(); ++it) {
+                if (it == wait) {
+                    late = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                load_block();
+            }
+            if (late && !may_recompute) {
+                if (lane == 0) dev_store(&ctrl->error, 1u);
+            } else if (late) {
+                const f4* xg = reinterpret_cast<const f4*>(x + s * inner);
+                uint32_t n_done = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint64_t todo = __ballot(!present(u));
+                    while (todo) {
+                        const int l = __builtin_ctzll(todo);
+                        todo &= todo - 1;
+                        const uint32_t jj = (uint32_t)(j0 + l + u * kWave);
+                        double mean, m2;
+                        ctl_recompute<F4PT, DW>(xg, jj, (uint32_t)P, nv, rc, rc_cnt, rc_inv, mean, m2);
+                        const double tm = ln_tag_word(mean, tag), tv = ln_tag_word(m2, tag);
+                        if (lane == l) {
+                            a[u] = tm;
+                            b2[u] = tv;
+                        }
+                        if (lane == 0) {
+                            dev_store(lbdx + s * 2 * P_cap + jj, tm);
+                            dev_store(lbdx + s * 2 * P_cap + P_cap + jj, tv);
+                        }
+                        ++n_done;
+                    }
+                }
+                if (lane == 0)
+                    __hip_atomic_fetch_add(&ctrl->recomputed, n_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (j0 == 0) c = ln_untag(lane_f64(a[0], 0));  // workgroup 0's mean
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t j = j0 + lane + (int64_t)u * kWave;
+                if (j < P) {
+                    const double nj = (double)wg_cnt[j];
+                    const double d = ln_untag(a[u]) - c;
+                    A += nj * d;
+                    B += ln_untag(b2[u]) + nj * (d * d);
+                }
+            }
+        }
+        A = wave_total(A);
+        B = wave_total(B);
+        const double n = (double)inner;
+        const double md = A / n;
+        const double m = c + md, m2s = fmax(B - A * md, 0.0);
+        const double var = m2s / n;
+        wm = ln_tag_word(m, tag);
+        wr = ln_tag_word(1.0 / sqrt(var + (double)eps), tag);
+        if (lane == 0) {
+            dev_store(lbd + 2 * s, wm);
+            dev_store(lbd + 2 * s + 1, wr);
+            const f4 st = unpack(wm, wr);
+            stats[s] = st;
+            if (mean_out) mean_out[s] = st.x;
+            if (rstd_out) rstd_out[s] = st.z;
+        }
+    };
+    // count before this workgroup's arrival at the next sample (lane 0); a
+    // silent workgroup (test knob) neither arrives nor stores its words
+    uint32_t before_next = lane == 0 && !silent ? arrive(0) : 0u;
     __syncthreads();  // prologue: w/b in LDS
     for (int64_t t = 0; t < steps; ++t) {
         __syncthreads();  // barrier t: the wave moments of sample t are in LDS
@@ -950,7 +1070,7 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
         const bool gather = g >= 0 && g < outer;
         // sample t's arrival was counted an iteration ago; count sample t + 1's now
         const uint32_t before = before_next;
-        if (t + 1 < outer && lane == 0) before_next = arrive(t + 1);
+        if (t + 1 < outer && lane == 0 && !silent) before_next = arrive(t + 1);
         double tm = 0.0, tr = 0.0;
         if (gather && lane == 0) {
             tm = dev_load(lbd + 2 * g);
@@ -960,84 +1080,42 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
             // this workgroup's (mean, M2) of sample t, tagged, into its slot
             double mean, m2;
             merge_wave_moments<DW>(red[t & 1], cnt, cnt_inv, inv_mine, mean, m2);
-            double* xs = lbdx + t * 2 * P_cap;  // P_cap tagged means, then P_cap tagged M2s
-            if (lane == 0) {
+            double* xs = lbdx + t * 2 * P_cap;
+            if (lane == 0 && !silent) {
                 dev_store(xs + p, ln_tag_word(mean, tag));
                 dev_store(xs + P_cap + p, ln_tag_word(m2, tag));
             }
-            if (__builtin_amdgcn_readfirstlane(lane == 0 && (before + 1u) % (uint32_t)P == 0u ? 1u : 0u)) {
-                // the last arrival: k-way merge of the P tagged words around
-                // workgroup 0's mean (lane l: workgroups l, l + 64, ...)
-                double c = 0.0, A = 0.0, B = 0.0;
-                for (int64_t j0 = 0; j0 < P; j0 += 4 * kWave) {
-                    double a[4], b2[4];
-                    auto load_block = [&]() __attribute__((always_inline)) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int64_t j = j0 + lane + (int64_t)u * kWave;
-                            const int64_t jj = j < P ? j : p;
-                            a[u] = dev_load(xs + jj);
-                            b2[u] = dev_load(xs + P_cap + jj);
-                        }
-                    };
-                    auto block_ok = [&]() __attribute__((always_inline)) {
-                        bool ok = true;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) ok = ok && ln_has_tag(a[u], tag) && ln_has_tag(b2[u], tag);
-                        return __all(ok);
-                    };
-                    load_block();
-                    for (uint32_t it = 0; !block_ok(); ++it) {
-                        if (it == kSpinLimit) {
-                            if (lane == 0) dev_store(&ctrl->error, 1u);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                        load_block();
-                    }
-                    if (j0 == 0) c = ln_untag(lane_f64(a[0], 0));  // workgroup 0's mean
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int64_t j = j0 + lane + (int64_t)u * kWave;
-                        if (j < P) {
-                            const double nj = (double)wg_cnt[j];
-                            const double d = ln_untag(a[u]) - c;
-                            A += nj * d;
-                            B += ln_untag(b2[u]) + nj * (d * d);
-                        }
-                    }
-                }
-                A = wave_total(A);
-                B = wave_total(B);
-                if (lane == 0) {
-                    const double n = (double)inner;
-                    const double md = A / n;
-                    const double m = c + md, m2s = fmax(B - A * md, 0.0);
-                    const double var = m2s / n;
-                    const double wm = ln_tag_word(m, tag), wr = ln_tag_word(1.0 / sqrt(var + (double)eps), tag);
+            if (__builtin_amdgcn_readfirstlane(lane == 0 && !silent && (before + 1u) % (uint32_t)P == 0u ? 1u : 0u)) {
+                // the last arrival merges the sample and takes P back off the counter
+                double wm, wr;
+                merge_sample(t, wm, wr);
+                if (lane == 0)
                     __hip_atomic_fetch_sub(counters + (t % kRing) * kCounterStride, (uint32_t)P, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-                    dev_store(lbd + 2 * t, wm);
-                    dev_store(lbd + 2 * t + 1, wr);
-                    const f4 st = unpack(wm, wr);
-                    stats[t] = st;
-                    if (mean_out) mean_out[t] = st.x;
-                    if (rstd_out) rstd_out[t] = st.z;
-                }
             }
         }
-        if (gather && lane == 0) {
-            uint32_t it = 0;
-            while (!(ln_has_tag(tm, tag) && ln_has_tag(tr, tag))) {
+        if (gather) {
+            // sample g's statistics; if they do not come (no workgroup was
+            // elected: one is not resident), merge the sample here
+            bool ok = false;
+            for (uint32_t it = 0;; ++it) {
+                ok = __builtin_amdgcn_readfirstlane(lane == 0 && ln_has_tag(tm, tag) && ln_has_tag(tr, tag) ? 1u : 0u);
+                if (ok || it == wait) break;
                 __builtin_amdgcn_s_sleep(1);
-                if (++it > kSpinLimit) {
-                    dev_store(&ctrl->error, 1u);
-                    break;
+                if (lane == 0) {
+                    tm = dev_load(lbd + 2 * g);
+                    tr = dev_load(lbd + 2 * g + 1);
                 }
-                tm = dev_load(lbd + 2 * g);
-                tr = dev_load(lbd + 2 * g + 1);
             }
-            s_stats[g & 1] = unpack(tm, tr);
+            if (!ok && may_recompute) {
+                double wm, wr;
+                merge_sample(g, wm, wr);
+                tm = wm;
+                tr = wr;
+            } else if (!ok && lane == 0) {
+                dev_store(&ctrl->error, 1u);
+            }
+            if (lane == 0) s_stats[g & 1] = unpack(tm, tr);
         }
     }
     // completion: the last workgroup out advances the generation
@@ -1130,8 +1208,14 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
             cnt_inv[0][lane] = inv_count_f64(n);
         }
         for (int64_t j = lane; j < P; j += kWave) wg_cnt[j] = (float)ctl_wg_elems<F4PT, DW>((uint32_t)j, (uint32_t)P, nv);
-        ctl_wave_last_block<DW, LAG>(red, cnt[0], cnt_inv[0], wg_cnt, s_stats, outer, inner, P, P_cap, p, eps, ctrl,
-                                     counters, lbd, lbdx, stats, mean_out, rstd_out);
+        // Not in place, the launch is an ordinary one and a workgroup that
+        // is not resident has its moments computed by the others (x stays
+        // intact); in place it is cooperative, every workgroup resident.
+        const bool may_recompute = x_all != y_all;
+        const bool silent = may_recompute && ((uint32_t)p & silent_mask) == silent_mask;
+        ctl_wave_last_block<F4PT, DW, LAG>(red, cnt[0], cnt_inv[0], wg_cnt, s_stats, x_all, outer, inner, P, P_cap, p,
+                                           eps, ctrl, counters, lbd, lbdx, stats, mean_out, rstd_out, may_recompute,
+                                           spin_limit, silent, rc, cnt[1], cnt_inv[1]);
         return;
     }
     if (tid >= RW) {
@@ -1573,7 +1657,8 @@ static int coresident(const void* fn, size_t lds, int threads)
 // Launches ln_single_ctl_kernel<F4PT, DW, LAG, PROTO, ILV> when a co-resident grid
 // of one workgroup per F4PT rows of DW * 64 float4 holds every sample's rows
 // (false: it cannot, nothing launched).  PROTO 0, the tagged exchange: an
-// ordinary launch; PROTO 1, the last workgroup merging: a cooperative one.
+// ordinary launch; PROTO 1, the last workgroup merging: an ordinary one,
+// and a cooperative one in place.
 template <int F4PT, int DW, int LAG, int PROTO, bool ILV>
 static bool try_launch_single(const float* x, const float* w, const float* b, float* y, int64_t outer,
                               int64_t inner, float eps, LnCtrl* ctrl, uint32_t* counters, double* lbd, f4* stats,
@@ -1618,8 +1703,21 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
                             dim3(threads), (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg,
                             mean_out, rstd_out, groups, k ? 8u : kCtlSpinLimit, force, counters, lbd, lbdx);
         return true;
+    } else if (x != y) {
+        // One group of P workgroups, an ordinary launch (the cooperative one
+        // measured ~17 us more per call): a sample whose statistics do not
+        // come (a workgroup that is not resident never arrives, so no merger
+        // is elected) is merged by whoever waited for it, computing missing
+        // moments from x with the same bits.  Test knob as for PROTO 0.
+        const uint32_t k = ln_force_recompute();
+        const uint32_t force = k ? k - 1u : 0xFFFFFFFFu;
+        err = launch_kernel(ln_single_ctl_kernel<F4PT, DW, LAG, 1, ILV>, dim3((unsigned)P), dim3(threads),
+                            (uint32_t)lds, st, x, w, b, y, outer, inner, pcap, eps, ctrl, stats, xchg, mean_out,
+                            rstd_out, (int64_t)1, k ? 8u : kCtlSpinLimit, force, counters, lbd, lbdx);
+        return true;
     } else {
-        // one group of P workgroups; the tagged exchange's arguments are unused
+        // In place: one group of P workgroups, a cooperative launch (a merge
+        // from x could read rows their owner has already overwritten)
         int64_t groups = 1;
         uint32_t spin = kSpinLimit, force = 0xFFFFFFFFu;
         void* args[] = {(void*)&x,        (void*)&w,        (void*)&b,        (void*)&y,      (void*)&outer,
@@ -1630,7 +1728,12 @@ static bool try_launch_single(const float* x, const float* w, const float* b, fl
         const LaunchEvents ev = take_launch_events();
         if (ev.start) (void)hipEventRecord(ev.start, st);
         err = hipLaunchCooperativeKernel(fn, dim3((unsigned)P), dim3(threads), args, lds, st);
-        if (err == hipSuccess) err = hipGetLastError();
+        // a refused launch is reported through err; taking it off the runtime's
+        // pending error keeps it from surfacing in the caller's next HIP call
+        if (err == hipSuccess)
+            err = hipGetLastError();
+        else
+            (void)hipGetLastError();
         if (err == hipSuccess && ev.stop) err = hipEventRecord(ev.stop, st);
         return true;
     }

@@ -1,7 +1,9 @@
-"""The control-wave LayerNorm kernel (ln_forward variant 1) runs as an ordinary launch: when a workgroup's
-published sums do not arrive (it is not resident), the others compute them from x with the same bits.  A
-child process forces that path for every k-th workgroup (NORMFWD_LN_FORCE_RECOMPUTE=k, read once by the
-library) and the results must equal this process's normal results bit for bit, and the oracle."""
+"""The control-wave LayerNorm kernel runs as an ordinary launch (ln_forward variant 1, and variant 2 when not
+in place): when a workgroup's published sums do not arrive (it is not resident), the others compute them
+from x with the same bits (variant 2: a sample no merger announces, since that workgroup never arrives, is
+merged by whoever waited for it).  A child process forces that path for every k-th workgroup
+(NORMFWD_LN_FORCE_RECOMPUTE=k, read once by the library: those workgroups publish and count nothing) and
+the results must equal this process's normal results bit for bit, and the oracle."""
 import os
 import subprocess
 import sys
@@ -34,10 +36,11 @@ def test_forced_recompute_is_bitwise_equal(k, tmp_path):
     normal = recompute_child.run_cases()  # this process: no knob, nothing recomputed
     # k = 4 forces workgroups 3, 7, ...: none in the 3-workgroup case
     n_cases = len(recompute_child.CASES)
-    assert sum(int(forced[f"recomputed_{o}x{i}"]) > 0 for o, i, _, _ in recompute_child.CASES) >= (
-        n_cases if k == 1 else n_cases - 1)
-    for outer, inner, seed, name in recompute_child.CASES:
-        tag = f"{outer}x{inner}"
+    for v in recompute_child.VARIANTS:
+        assert sum(int(forced[f"recomputed_v{v}_{o}x{i}"]) > 0 for o, i, _, _ in recompute_child.CASES) >= (
+            n_cases if k == 1 else n_cases - 1), v
+    for (outer, inner, seed, name), v in [(c, v) for c in recompute_child.CASES for v in recompute_child.VARIANTS]:
+        tag = f"v{v}_{outer}x{inner}"
         assert int(normal[f"recomputed_{tag}"]) == 0, f"{tag}: a healthy launch recomputed sums"
         for key in ("y", "mean", "rstd"):
             a, b = forced[f"{key}_{tag}"], normal[f"{key}_{tag}"]
