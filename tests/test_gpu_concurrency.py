@@ -1,6 +1,7 @@
-"""The single-read LayerNorm kernel (an ordinary launch whose workgroups exchange moments) next to other
-work on a second stream: every result equals its solo result bit for bit, and a short kernel alongside
-does not stall it (its waits are bounded; a missing workgroup's moments are computed by the readers).
+"""The single-read LayerNorm kernel (an ordinary launch whose workgroups exchange moments: variant 1, every
+workgroup merging every sample, and variant 2, the last to arrive merging it) next to other work on a
+second stream: every result equals its solo result bit for bit, and a short kernel alongside does not
+stall it (its waits are bounded; a missing workgroup's moments are computed by the readers).
 Durations are medians of several repetitions, each taken with events on the LayerNorm's own stream."""
 import sys
 
@@ -14,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPE = (16, 1 << 22)
 REPS = 8
+VARIANTS = (1, 2)
 
 
 def _say(msg):
@@ -33,9 +35,9 @@ def setup():
         _, w = nf.alloc_workspace(nf.ln_forward_workspace_size(*SHAPE), dev)
         nf.ln_forward_workspace_init(w)
         ws.append(w)
-    ref = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1)
+    refs = {v: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=v) for v in VARIANTS}
     torch.cuda.synchronize()
-    yield dev, d, ws, ref
+    yield dev, d, ws, refs
     torch.cuda.synchronize()
 
 
@@ -80,15 +82,17 @@ def _concurrent(other, ln, s_other, s_ln, check):
     return _median(tl), _median(to)
 
 
-def test_ln_beside_a_short_kernel(setup):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_ln_beside_a_short_kernel(setup, variant):
     """GroupNorm [1024, 8192] (~12 us) on one stream, the LayerNorm [16, 4M] right after on another: both
     results bitwise equal to their solo results; the LayerNorm takes under 2x its solo time."""
-    dev, d, ws, ref = setup
+    dev, d, ws, refs = setup
+    ref = refs[variant]
     g = synth.make("gn_lrelu_x2_1024x8192", device=dev)
     g_ref = nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512)
     gy, y = torch.empty_like(g_ref), torch.empty_like(ref)
     s_ln, s_other = torch.cuda.Stream(), torch.cuda.Stream()
-    ln = lambda: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, out=y, workspace=ws[0])  # noqa: E731
+    ln = lambda: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, out=y, workspace=ws[0])  # noqa: E731
     other = lambda: nf.gn_lrelu_x2_forward(g["x"], g["gamma"], g["beta"], 512, out=gy)  # noqa: E731
     solo = _solo_ms(ln, s_ln)
 
@@ -98,19 +102,22 @@ def test_ln_beside_a_short_kernel(setup):
         y.fill_(float("nan"))
 
     t_ln, t_other = _concurrent(other, ln, s_other, s_ln, check)
-    _say(f"solo LN {solo * 1e3:.1f} us; beside GN: LN {t_ln * 1e3:.1f} us, GN {t_other * 1e3:.1f} us")
+    _say(f"v{variant}: solo LN {solo * 1e3:.1f} us; beside GN: LN {t_ln * 1e3:.1f} us, "
+         f"GN {t_other * 1e3:.1f} us")
     assert t_ln < 2.0 * solo, (t_ln, solo)
 
 
-def test_ln_beside_a_streaming_kernel(setup):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_ln_beside_a_streaming_kernel(setup, variant):
     """RMSNorm [4, 64, 512, 512] (~100 us, HBM-bound like the LayerNorm) alongside: both bitwise equal to
     their solo results; the two share HBM, so the LayerNorm takes at most about the time of both."""
-    dev, d, ws, ref = setup
+    dev, d, ws, refs = setup
+    ref = refs[variant]
     r = synth.make("rms_ch_112x64x512x512", device=dev, shape=(4, 64, 512, 512))
     r_ref = nf.rmsnorm_ch_forward(r["x"])
     ry, y = torch.empty_like(r_ref), torch.empty_like(ref)
     s_ln, s_other = torch.cuda.Stream(), torch.cuda.Stream()
-    ln = lambda: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, out=y, workspace=ws[0])  # noqa: E731
+    ln = lambda: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, out=y, workspace=ws[0])  # noqa: E731
     other = lambda: nf.rmsnorm_ch_forward(r["x"], out=ry)  # noqa: E731
     solo_ln, solo_other = _solo_ms(ln, s_ln), _solo_ms(other, s_other)
 
@@ -120,20 +127,22 @@ def test_ln_beside_a_streaming_kernel(setup):
         y.fill_(float("nan"))
 
     t_ln, t_other = _concurrent(other, ln, s_other, s_ln, check)
-    _say(f"solo LN {solo_ln * 1e3:.1f} us, RMS {solo_other * 1e3:.1f} us; together: LN {t_ln * 1e3:.1f} us, "
-         f"RMS {t_other * 1e3:.1f} us")
+    _say(f"v{variant}: solo LN {solo_ln * 1e3:.1f} us, RMS {solo_other * 1e3:.1f} us; "
+         f"together: LN {t_ln * 1e3:.1f} us, RMS {t_other * 1e3:.1f} us")
     assert t_ln < 1.5 * (solo_ln + solo_other), (t_ln, solo_ln, solo_other)
 
 
-def test_two_ln_calls_on_two_streams(setup):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_two_ln_calls_on_two_streams(setup, variant):
     """Two single-read LayerNorm calls on two streams (separate workspaces) at once: both equal the solo
     result bit for bit and finish within twice the time of the two run one after the other."""
-    dev, d, ws, ref = setup
+    dev, d, ws, refs = setup
+    ref = refs[variant]
     x2 = d["x"].clone()
     y1, y2 = torch.empty_like(ref), torch.empty_like(ref)
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    a = lambda: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=1, out=y1, workspace=ws[0])  # noqa: E731
-    b = lambda: nf.ln_forward(x2, d["weight"], d["bias"], variant=1, out=y2, workspace=ws[1])  # noqa: E731
+    a = lambda: nf.ln_forward(d["x"], d["weight"], d["bias"], variant=variant, out=y1, workspace=ws[0])  # noqa: E731
+    b = lambda: nf.ln_forward(x2, d["weight"], d["bias"], variant=variant, out=y2, workspace=ws[1])  # noqa: E731
     solo = _solo_ms(a, s1)
 
     def check():
@@ -142,5 +151,5 @@ def test_two_ln_calls_on_two_streams(setup):
         y2.fill_(float("nan"))
 
     t1, t2 = _concurrent(b, a, s2, s1, check)
-    _say(f"solo LN {solo * 1e3:.1f} us; two at once: {t1 * 1e3:.1f} / {t2 * 1e3:.1f} us")
+    _say(f"v{variant}: solo LN {solo * 1e3:.1f} us; two at once: {t1 * 1e3:.1f} / {t2 * 1e3:.1f} us")
     assert max(t1, t2) < 4.0 * solo, (t1, t2, solo)
