@@ -3,8 +3,9 @@
 Every translation unit under csrc/ is compiled with
   -O3 --offload-arch=gfx950 -std=c++17 -fPIC
   -Xclang -target-feature -Xclang -packed-fp32-ops   (no packed fp32 VALU ops)
-and linked into normalization_ln_forward_amd/libnormfwd.so.  No fast-math:
-sqrt and division stay correctly rounded.
+plus the per-file flags in EXTRA_FLAGS, and linked into
+normalization_ln_forward_amd/libnormfwd.so.  No fast-math: sqrt and division
+stay correctly rounded.
 """
 import concurrent.futures as cf
 import os
@@ -21,6 +22,16 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "ln.hip", "gn.hip", "rms.hip", "fc.hip", "ref.hip"]
+
+# ln.hip: LLVM's AMDGPU atomic optimizer off.  Every atomic in ln.hip is
+# issued by a single lane; the optimizer rewrites each one into a wave-wide
+# form that broadcasts the returned value right after the atomic, so the wave
+# waits out the atomic's round trip where it issues it.  The last-workgroup-
+# merges control wave counts its arrival at a sample an iteration ahead so
+# that this round trip overlaps the iteration (with the optimizer, each
+# control wave waited for it before publishing its moments: 108-114 us per
+# call at [16, 4M], 105-107 us without).
+EXTRA_FLAGS = {"ln.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
@@ -43,7 +54,7 @@ def build(out=LIB, defines=(), build_dir=BUILD_DIR, verbose=False, jobs=8) -> st
 
     def one(src):
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *compile_flags(defines), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(defines), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -871,7 +871,7 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
 // data waves, ctl_wave_last_block below, puts the last arrival's merge and
-// announcement and the readers' poll on every sample's path: 108-109 us per
+// announcement and the readers' poll on every sample's path: 105-107 us per
 // call at [16, 4M] against 93 us.)
 //
 // Control wave of ln_single_ctl_kernel with the last-workgroup-merges
@@ -926,10 +926,14 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // us against ~5.8 us for the data, and the whole grid ran at its pace);
 // 133.9 us with the tagged words and the count issued right after them;
 // 125-126 us with the count issued an iteration early; 108-109 us as an
-// ordinary launch (the cooperative one cost ~17 us per call).  Merging
-// sample t one iteration later, when every workgroup's words have surely
-// landed, measured 128.5 us; a lag of 4 samples (with a ring of 8) 125.6
-// (both with the cooperative launch).
+// ordinary launch (the cooperative one cost ~17 us per call); 105-107 us
+// with LLVM's AMDGPU atomic optimizer off for this file (build.py), which
+// otherwise turns the single-lane arrival into a wave-wide atomic whose
+// result is broadcast, and so waited for, right where it is issued.
+// Merging sample t one iteration later, when every workgroup's words have
+// surely landed, measured 128.5 us; a lag of 4 samples (with a ring of 8)
+// 125.6 (both with the cooperative launch), and 113 us against 107 as an
+// ordinary launch; issuing the merger's loads of the words first, 110 us.
 // Every workgroup derives mean hi/lo and rstd from the same two words.  The
 // last workgroup out advances the generation.
 template <int F4PT, int DW, int LAG>
@@ -957,6 +961,9 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
         return f4{hi, (float)(m - (double)hi), (float)ln_untag(tr), 0.0f};
     };
     static_assert(kRing >= LAG + 1, "an arrival is counted before the statistics kRing samples back are read");
+    // (returns this arrival's count in lane 0; its round trip is waited for
+    // only where the count is used, an iteration later, as long as the
+    // compiler's atomic optimizer is off for this file)
     auto arrive = [&](int64_t s) {
         return __hip_atomic_fetch_add(counters + (s % kRing) * kCounterStride, 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);

@@ -58,8 +58,9 @@ def code_text(text):
 
 
 def source_sha(files, read=None):
-    """Hash of the code (see code_text) of the named csrc files; `read(name) -> str` overrides reading
-    them from the package's csrc/."""
+    """Hash of the code (see code_text) of the named csrc files and of the extra compiler flags each is
+    built with; `read(name) -> str` overrides reading them from the package's csrc/."""
+    from . import build
     h = hashlib.sha256()
     for f in files:
         if read is None:
@@ -68,6 +69,7 @@ def source_sha(files, read=None):
         else:
             text = read(f)
         h.update(code_text(text).encode("utf-8"))
+        h.update(" ".join(build.EXTRA_FLAGS.get(f, [])).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

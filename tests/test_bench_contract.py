@@ -46,11 +46,12 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
 
 
-def test_traffic_is_reported_only_for_unchanged_kernel_code():
+def test_traffic_is_reported_only_for_unchanged_kernel_code(monkeypatch):
     """roofline.traffic comes from the committed counter summary only while the profiled kernels' code is
-    the code that was measured: the hash covers the sources with comments and blank lines removed, so a
-    change to code changes it and a change to comments alone does not."""
-    from normalization_ln_forward_amd import profiling
+    the code that was measured: the hash covers the sources with comments and blank lines removed and the
+    extra compiler flags of each, so a change to code or flags changes it and a change to comments alone
+    does not."""
+    from normalization_ln_forward_amd import build, profiling
 
     def sha(text):
         return profiling.source_sha(["k.hip"], read=lambda name: text)
@@ -60,3 +61,6 @@ def test_traffic_is_reported_only_for_unchanged_kernel_code():
     assert sha(base) == sha("/* a\n   kernel */\n__global__ void k(float* y) {   \n    y[0] = 1.0f; /* x */\n}\n")
     assert sha(base) != sha("__global__ void k(float* y) {\n    y[0] = 2.0f;\n}\n")
     assert sha(base) != sha("__global__ void k(float* y) {\n    y[1] = 1.0f;\n}\n")
+    plain = sha(base)
+    monkeypatch.setitem(build.EXTRA_FLAGS, "k.hip", ["-mllvm", "-some-option"])
+    assert sha(base) != plain
