@@ -871,8 +871,8 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
 // data waves, ctl_wave_last_block below, puts the last arrival's merge and
-// announcement and the readers' poll on every sample's path: 105-107 us per
-// call at [16, 4M] against 93 us.)
+// announcement and the readers' poll on every sample's path: 98-100 us per
+// call at [16, 4M] against 92-93 us.)
 //
 // Control wave of ln_single_ctl_kernel with the last-workgroup-merges
 // exchange (LN page, turn 6: last-block-done), for ln_forward variant 2.
@@ -929,7 +929,8 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // ordinary launch (the cooperative one cost ~17 us per call); 105-107 us
 // with LLVM's AMDGPU atomic optimizer off for this file (build.py), which
 // otherwise turns the single-lane arrival into a wave-wide atomic whose
-// result is broadcast, and so waited for, right where it is issued.
+// result is broadcast, and so waited for, right where it is issued; 98-100
+// us with the control wave at raised priority.
 // Merging sample t one iteration later, when every workgroup's words have
 // surely landed, measured 128.5 us; a lag of 4 samples (with a ring of 8)
 // 125.6 (both with the cooperative launch), and 113 us against 107 as an
@@ -1209,6 +1210,8 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
 
     if (tid >= RW && PROTO == 1) {
         // ---- control wave, last workgroup merges (groups == 1)
+        // (issued ahead of the data waves of its SIMD: see the control wave below)
+        __builtin_amdgcn_s_setprio(2);
         if (lane < DW) {
             const uint32_t n = ctl_wave_elems<F4PT, DW>((uint32_t)p, lane, (uint32_t)P, nv);
             cnt[0][lane] = n;
@@ -1227,6 +1230,18 @@ ln_single_ctl_kernel(const float* x_all, const float* w, const float* bias, floa
     }
     if (tid >= RW) {
         // ---- control wave
+        // Raised wave priority: the SIMD's arbiter issues this wave's
+        // instructions ahead of the two data waves beside it, so the exchange
+        // (its LDS reads, merges and publication) is not queued behind their
+        // streaming.  Measured per call on MI355X, priority 2 against the
+        // default: [16, 4M] 92.1-92.5 against 93.9-94.7 us, [8, 4M] 47.5-48.1
+        // against 48.8-49.6, [4, 4M] 25.8-25.9 against 26.8-27.1 (priority
+        // 3), [64, 4M] 353.0-353.1 against 350.8-351.6, [16, 3M] 75.4-75.5
+        // against 74.3-75.2, the rest within 0.5 us; the last-workgroup-
+        // merges kernel [16, 4M] 99.1-99.4 against 109.6-110.9 us, [64, 256K]
+        // 345-350 against 386 (priorities 1, 2 and 3 within each other's
+        // spread).  Outputs bitwise equal.
+        __builtin_amdgcn_s_setprio(2);
         const uint32_t gen_target = ln_next_generation(dev_load(&ctrl->gen_ctl));
         const uint32_t tag = ln_tag_of(gen_target);
         uint32_t limit = spin_limit;
