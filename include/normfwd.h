@@ -140,7 +140,7 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *                 control wave per workgroup does the exchange beside the
  *                 data waves of variant 1, which read x once; partials
  *                 carry the launch's generation tag, so arrivals are
- *                 counted an iteration ahead and the merger polls until
+ *                 counted iterations ahead and the merger polls until
  *                 every partial is current).  Not in place it is an
  *                 ordinary launch: if a workgroup is not resident (so it
  *                 never arrives and no merger is elected), a workgroup that

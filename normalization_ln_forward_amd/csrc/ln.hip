@@ -49,7 +49,7 @@
 //          is not resident) are computed by the reader from x, with the same
 //          bits (so it never runs in place: y == x takes the split);
 //          variant 2: the last workgroup to arrive at a sample (an atomic
-//          count, issued an iteration ahead) merges every workgroup's
+//          count, issued LAG - 1 iterations ahead) merges every workgroup's
 //          generation-tagged partial of it and announces the statistics as
 //          tagged words (LN page, turn 6: last-block-done; the tags serve as
 //          the flags), done by the control wave of ln_single_ctl_kernel
@@ -96,7 +96,7 @@ constexpr int kLnThreads = 256;
 // The single kernel's arrival counters: a ring of kRing, each on its own
 // 128-byte line (atomics that meet on one line serialize).
 constexpr int kCounterStride = 32;  // uint32 words
-constexpr int kRing = 4;
+constexpr int kRing = 8;
 // Polls before a wait gives up (sets the control block's error word and
 // goes on): ~0.3-0.5 s, thousands of times the longest wait of a healthy
 // launch, so a launch whose workgroups are not all resident ends instead of
@@ -208,9 +208,9 @@ constexpr int kLnWideLag = 3;
 #endif
 
 
-// uint32 words of the single kernel's arrival-counter ring (4 slots x 128
-// bytes).
-constexpr size_t kLnCounterWords = 4 * 32;
+// uint32 words of the single kernel's arrival-counter ring (kRing slots x
+// 128 bytes).
+constexpr size_t kLnCounterWords = (size_t)kRing * 32;
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -871,7 +871,7 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // waves do not wait for the slowest workgroup each iteration.  No atomics,
 // counters or flags.  (The last-workgroup-merges exchange beside the same
 // data waves, ctl_wave_last_block below, puts the last arrival's merge and
-// announcement and the readers' poll on every sample's path: 98-100 us per
+// announcement and the readers' poll on every sample's path: 98-99 us per
 // call at [16, 4M] against 92-93 us.)
 //
 // Control wave of ln_single_ctl_kernel with the last-workgroup-merges
@@ -885,11 +885,11 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // wait that runs past its spin limit sets the control block's error word
 // instead.  The data waves are those of the tagged exchange, unchanged, so
 // they never wait on another workgroup.  Each workgroup counts its arrival
-// at a sample on that sample's counter (a ring of kRing) one iteration
-// early, and the arrival that finds P - 1 (mod P) before it merges the
-// sample.  After barrier t:
-//   take the count returned for sample t (issued an iteration ago) and
-//   issue this workgroup's arrival at sample t + 1;
+// at a sample on that sample's counter (a ring of kRing) AHEAD = LAG - 1
+// iterations early, and the arrival that finds P - 1 (mod P) before it
+// merges the sample.  After barrier t:
+//   take the count returned for sample t (issued AHEAD iterations ago) and
+//   issue this workgroup's arrival at sample t + AHEAD;
 //   issue the loads of the statistics words of sample g = t - LAG + 1 (they
 //   were announced an iteration or more ago, and their round trip overlaps
 //   what follows);
@@ -911,8 +911,8 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // reset: a sample's P arrivals see every residue mod P once, whatever count
 // the counter held before (even one a launch that gave up left behind).  A
 // workgroup issues its arrival at sample s + kRing in iteration s + kRing -
-// 1, after reading the statistics of sample s (kRing >= LAG + 1), which
-// exist only once all of sample s's arrivals were counted; the merger's
+// AHEAD, after reading the statistics of sample s (kRing >= LAG + AHEAD),
+// which exist only once all of sample s's arrivals were counted; the merger's
 // subtraction lands before its own arrival at sample s + kRing (same
 // address, same wave), so each count stays below 2P.  (When a workgroup
 // is not resident, a sample's statistics can come from a waiter before all
@@ -930,7 +930,8 @@ __device__ void ctl_recompute(const f4* xs, uint32_t j, uint32_t P, int64_t nv, 
 // with LLVM's AMDGPU atomic optimizer off for this file (build.py), which
 // otherwise turns the single-lane arrival into a wave-wide atomic whose
 // result is broadcast, and so waited for, right where it is issued; 98-100
-// us with the control wave at raised priority.
+// us with the control wave at raised priority; 98-99 us with arrivals
+// counted LAG - 1 (two) iterations ahead.
 // Merging sample t one iteration later, when every workgroup's words have
 // surely landed, measured 128.5 us; a lag of 4 samples (with a ring of 8)
 // 125.6 (both with the cooperative launch), and 113 us against 107 as an
@@ -961,7 +962,18 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
         const float hi = (float)m;
         return f4{hi, (float)(m - (double)hi), (float)ln_untag(tr), 0.0f};
     };
-    static_assert(kRing >= LAG + 1, "an arrival is counted before the statistics kRing samples back are read");
+    // Arrivals are counted AHEAD iterations early.  A merge lengthens the
+    // merger's iteration, and the arrival it issues next (at sample t +
+    // AHEAD) then comes late, so its workgroup is elected again AHEAD + 1
+    // samples on: the merges rotate over AHEAD + 1 workgroups.  With a lag
+    // of 3 (the wide tile) two ahead measured faster per call at [16, 4M]
+    // (98.1-98.7 against 99.9-100.3 us), [32, 4M] and [4, 4M]; with a lag of
+    // 2 (the 8 x 8 tile) it measured slower ([64, 256K] 373 against 348-353
+    // us: the workgroup elected two iterations back has often caught up and
+    // waits for the laggard's words), so one ahead there.
+    constexpr int AHEAD = LAG - 1;
+    static_assert(AHEAD >= 1, "arrivals are counted at least an iteration ahead");
+    static_assert(kRing >= LAG + AHEAD, "an arrival is counted before the statistics kRing samples back are read");
     // (returns this arrival's count in lane 0; its round trip is waited for
     // only where the count is used, an iteration later, as long as the
     // compiler's atomic optimizer is off for this file)
@@ -1068,17 +1080,22 @@ __device__ void ctl_wave_last_block(const double (*red)[3 * DW], const uint32_t*
             if (rstd_out) rstd_out[s] = st.z;
         }
     };
-    // count before this workgroup's arrival at the next sample (lane 0); a
-    // silent workgroup (test knob) neither arrives nor stores its words
-    uint32_t before_next = lane == 0 && !silent ? arrive(0) : 0u;
+    // counts before this workgroup's arrivals at the next AHEAD samples
+    // (lane 0; q[i]: sample t + i); a silent workgroup (test knob) neither
+    // arrives nor stores its words
+    uint32_t q[AHEAD];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) q[i] = lane == 0 && !silent && i < outer ? arrive(i) : 0u;
     __syncthreads();  // prologue: w/b in LDS
     for (int64_t t = 0; t < steps; ++t) {
         __syncthreads();  // barrier t: the wave moments of sample t are in LDS
         const int64_t g = t - (LAG - 1);
         const bool gather = g >= 0 && g < outer;
-        // sample t's arrival was counted an iteration ago; count sample t + 1's now
-        const uint32_t before = before_next;
-        if (t + 1 < outer && lane == 0 && !silent) before_next = arrive(t + 1);
+        // sample t's arrival was counted AHEAD iterations ago; count sample t + AHEAD's now
+        const uint32_t before = q[0];
+#pragma unroll
+        for (int i = 0; i + 1 < AHEAD; ++i) q[i] = q[i + 1];
+        if (t + AHEAD < outer && lane == 0 && !silent) q[AHEAD - 1] = arrive(t + AHEAD);
         double tm = 0.0, tr = 0.0;
         if (gather && lane == 0) {
             tm = dev_load(lbd + 2 * g);

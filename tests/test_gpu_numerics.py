@@ -233,31 +233,32 @@ def test_ln_variants_alternating_on_one_workspace_past_the_tag_cycle():
 
 
 # the last-workgroup-merges kernel's arrival counters: int32 index of the first (right after the 256-byte
-# control block) and words between them (one per 128-byte line, four of them)
+# control block) and words between them (one per 128-byte line, eight of them)
 COUNTER_RING_WORD = 64
 COUNTER_STRIDE_WORDS = 32
+COUNTER_RING = 8
 
 
-@pytest.mark.parametrize("shape", [(6, 1 << 19), (8, 4000000)])
+@pytest.mark.parametrize("shape", [(12, 1 << 19), (16, 4000000)])
 def test_ln_last_block_election_survives_leftover_counts(shape):
     """Variant 2 elects as a sample's merger the arrival that finds P - 1 modulo P before it, and the merger
     takes P back off the counter, so counts left in the ring (a launch that gave up on a wait stops counting
     halfway) move no election: with counts planted from the host the output stays bitwise equal to a clean
-    run's and no wait gives up.  Shapes: 32 workgroups per sample with the 8 x 8 tile, and 237 with the
-    wide tile, whose eight samples take each counter twice."""
+    run's and no wait gives up.  Shapes: 32 workgroups per sample with the 8 x 8 tile (arrivals counted one
+    sample ahead), and 237 with the wide tile (two ahead), whose 16 samples take each counter twice."""
     _say(f"ln last-block election with planted counts shape={shape}")
     d = synth.make("ln_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=29)
     _, ws = nf.alloc_workspace(nf.ln_forward_workspace_size(*shape), "cuda")
     nf.ln_forward_workspace_init(ws)
     clean = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=2, workspace=ws)
     words = ws.view(torch.int32)
-    for planted in ([1, 31, 5, 100], [(1 << 20) + 3, 7, 0, 236], [9, 9, 9, 9]):
+    for planted in ([1, 31, 5, 100, 2, 63, 17, 4], [(1 << 20) + 3, 7, 0, 236, 1, 235, 64, 3], [9] * COUNTER_RING):
         for k, v in enumerate(planted):
             words[COUNTER_RING_WORD + k * COUNTER_STRIDE_WORDS] = v
         y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=2, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y, clean), planted
-        left = [int(words[COUNTER_RING_WORD + k * COUNTER_STRIDE_WORDS]) for k in range(4)]
+        left = [int(words[COUNTER_RING_WORD + k * COUNTER_STRIDE_WORDS]) for k in range(COUNTER_RING)]
         assert left == planted, (planted, left)  # every sample's arrivals and its merger's subtraction cancel
         nf.ln_forward_workspace_check(ws)
     ref = oracle.ln(_np(d["x"]), _np(d["weight"]), _np(d["bias"]))
