@@ -147,10 +147,14 @@ constexpr uint32_t kSpinLimitAfterMiss = 1u << 5;
 // Split schedule: below NORMFWD_LN_FUSE_BELOW moments workgroups in all,
 // the last workgroup of a sample to finish merges its partials (no separate
 // merge launch); from there on ln_merge_kernel does (0 = always the kernel).
-// Measured on MI355X: fusing saves 0.6-1.2 us at 64-512 workgroups
-// ([16, 65536], [8, 2^20]), is even at 1024 and costs 0.6-1.5 us at 1024-4096
-// ([4, 2^22], [16, 2^22]), where the atomics of thousands of workgroups
-// outweigh the saved launch.
+// Measured on MI355X, step per call, fused against the merge kernel: 64-512
+// workgroups ([16, 65536], [8, 2^20]) 0.6-1.2 us faster; [16, 2^22] (4096)
+// 135.3-136.3 against 137.0-137.8 us, [32, 2^22] (8192) 270.0-270.4 against
+// 274.4-277.0, [128, 2^20] (8192) 267.2-268.0 against 265.3-269.3, [8, 2^22],
+// [4, 2^22], [16, 2^20], [64, 2^18] within 0.3 us; [64, 2^22] (16384)
+// 593.2-595.0 against 575.5-577.3.  (With the compiler's atomic optimizer
+// on, which waited for each counter atomic where it was issued, fusing had
+// cost 0.6-1.5 us at 1024-4096 workgroups.)
 // Single-read kernel tiles: DW data waves (plus the control wave) of F4PT
 // float4 per thread, i.e. a workgroup holds F4PT rows of 64 DW float4 of
 // every sample.  Measured on MI355X at [16, 4M] (kernel duration, one call,
@@ -204,7 +208,7 @@ constexpr int kLnWideLag = 3;
 #endif
 
 #ifndef NORMFWD_LN_FUSE_BELOW
-#define NORMFWD_LN_FUSE_BELOW 1024
+#define NORMFWD_LN_FUSE_BELOW 16384
 #endif
 
 

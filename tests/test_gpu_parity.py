@@ -240,6 +240,26 @@ def test_ln_full_size(name, variant):
     assert torch.equal(y, y2), "not bitwise deterministic"
 
 
+def test_ln_split_with_the_merge_kernel():
+    """The split schedule with at least 16384 moments workgroups in all, where ln_merge_kernel merges the
+    partials (below that the last workgroup of each sample does): [16384, 8196], one ragged workgroup per
+    sample; y, means and rstds of sampled rows against the oracle, bitwise deterministic."""
+    shape = (16384, 8196)
+    _say(f"ln split, merge kernel {shape}")
+    d = synth.make("ln_16x64x256x256", device="cuda", shape=shape, normalized_ndim=1, seed=77)
+    mean = torch.empty(shape[0], device="cuda")
+    rstd = torch.empty(shape[0], device="cuda")
+    y = nf.ln_forward(d["x"], d["weight"], d["bias"], variant=0, mean_out=mean, rstd_out=rstd)
+    rows = [0, 1, 255, 4096, 8191, 8192, 12345, 16382, 16383]
+    ref, om, ov = oracle.ln(_np(d["x"][rows]), _np(d["weight"]), _np(d["bias"]), eps=1e-5, return_stats=True)
+    _assert_close(_np(y[rows]), ref, what="ln split merge kernel")
+    np.testing.assert_allclose(_np(mean[rows]), om, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(_np(rstd[rows]), 1.0 / np.sqrt(ov + np.float32(1e-5)), rtol=1e-5)
+    assert torch.equal(y, nf.ln_forward(d["x"], d["weight"], d["bias"], variant=0)), "not bitwise deterministic"
+    del d, y
+    torch.cuda.empty_cache()
+
+
 def test_ln_auto_variant_picks_the_measured_fastest():
     """variant 3 runs the single-read kernel wherever it can run (float4 rows, 16-byte aligned tensors,
     a co-resident grid) and the split schedule elsewhere: its output is bitwise that of the variant it
