@@ -108,7 +108,7 @@ normfwd_status normfwd_time_next_kernel(void* start_event, void* stop_event);
  *             that may run concurrently.
  *   variant   0 = split: a partial-moments kernel, a per-sample merge of
  *                 the partials, then a normalize kernel.  With fewer than
- *                 1024 moments workgroups the merge is done by the last
+ *                 16384 moments workgroups the merge is done by the last
  *                 workgroup of each sample to finish (LN page, turn 6;
  *                 nothing waits, so any grid size works), otherwise by a
  *                 merge kernel;
