@@ -168,6 +168,9 @@ LN_CASES = [
     (8, 4000000, True, 2),
     (2, 4325376, True, 1),
     (2, 4325376, True, 2),
+    # variant 2 on the wide tile counts arrivals two samples ahead: one sample (no second arrival) and three
+    (1, 4325376, True, 2),
+    (3, 4325376, False, 2),
     # the wide tile from 4 samples on: 5 samples of 975,000 float4 (222 workgroups, ragged last row),
     # no affine
     (5, 3900000, False, 1),
