@@ -113,7 +113,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path", file=sys.stderr, flush=True)
+              "the library has no multi-GPU path", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch

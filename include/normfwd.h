@@ -58,7 +58,7 @@ extern "C" {
 typedef int normfwd_status;
 #define NORMFWD_OK 0
 #define NORMFWD_ERR_INVALID 1     /* bad shape, null required pointer, bad enum value   */
-#define NORMFWD_ERR_UNSUPPORTED 2 /* valid arguments this build does not handle         */
+#define NORMFWD_ERR_UNSUPPORTED 2 /* valid arguments the library does not handle       */
 #define NORMFWD_ERR_WORKSPACE 3   /* workspace null or smaller than the size query says */
 #define NORMFWD_ERR_HIP 4         /* a HIP runtime call or kernel launch failed         */
 #define NORMFWD_ERR_INCOMPLETE 5  /* a single-kernel LayerNorm gave up waiting (below)  */
